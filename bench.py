@@ -1,0 +1,200 @@
+#!/usr/bin/env python3
+"""Throughput of the M²RNN hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input already resident
+in HBM: gate precompute (m2rnn_gates) -> forward with state checkpoints every C
+steps (m2rnn_fwd) -> reverse-time backward (m2rnn_bwd) with a synthetic
+upstream gradient dy.  Default workload: B=4, T=16384, n_heads=16, K=V=64,
+bf16 k/v/q, fp32 state, exp-softplus gate, C=64.
+
+Prints ONE JSON line.  Per-call durations come from HIP events recorded on the
+stream the library launches on (torch's current stream); the roofline block
+prices the dominant call against the fp32 MFMA peak with the algorithmic flop
+count (forward 2 K V^2, backward 4 K V^2 per token and head; the backward's
+recompute is not counted).  ``cpu_baseline`` times the float64 CPU oracle on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="long_t16k_k64")
+    ap.add_argument("--C", type=int, default=64, help="checkpoint interval")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target duration of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def oracle_baseline(wl, target_s):
+    """float64 oracle (forward + backward) on the first Ts steps of every unit."""
+    import numpy as np
+
+    import oracle
+    from m2rnn_inputs import make_inputs
+
+    def run(T):
+        w = wl.replace(T=T)
+        inp = make_inputs(w, with_dy=True)
+        t0 = time.perf_counter()
+        f = oracle.gates(w.gate, inp.logit, inp.alpha, inp.beta)
+        oracle.forward(inp.k, inp.v, inp.q, f, inp.W, inp.w_r)
+        oracle.backward(inp.k, inp.v, inp.q, f, inp.W, inp.w_r, inp.dy, gate_kind=w.gate,
+                        logit=inp.logit, alpha=inp.alpha, beta=inp.beta)
+        return time.perf_counter() - t0
+
+    probe_T = 32
+    per_step = run(probe_T) / probe_T
+    Ts = int(max(probe_T, min(wl.T, target_s / max(per_step, 1e-9))))
+    el = run(Ts)
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 0) for p in threadpool_info()), default=None)
+    except Exception:  # noqa: BLE001
+        pass
+    cores = threads or len(os.sched_getaffinity(0))
+    return {"value": wl.B * Ts * wl.N / el, "unit": "tokens*heads/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle, gates+forward+backward (forward rerun inside the "
+                      f"backward), all {wl.B * wl.N} (b,n) units, first {Ts} of {wl.T} steps, "
+                      f"{el:.1f} s; {len(os.sched_getaffinity(0))} host cpus visible, "
+                      f"{np.__version__=}"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from m2rnn_inputs import WORKLOADS, make_inputs, to_device
+    from matrix_state_nonlinear_amd import m2rnn_bwd, m2rnn_fwd, m2rnn_gates
+    from matrix_state_nonlinear_amd.ops import m2rnn_workspace_bytes
+
+    wl = WORKLOADS[args.workload]
+    C = args.C
+    B, T, N, K, V = wl.B, wl.T, wl.N, wl.K, wl.V
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(wl, with_dy=True)
+    d = to_device(inp, "float32", dev)
+    f = torch.empty((B, T, N), dtype=torch.float32, device=dev)
+    y = torch.empty((B, T, N, V), dtype=torch.float32, device=dev)
+    HT = torch.empty((B, N, K, V), dtype=torch.float32, device=dev)
+    ckpt = torch.empty((B, N, (T + C - 1) // C, K, V), dtype=torch.float32, device=dev)
+    wsf = torch.empty(max(1, m2rnn_workspace_bytes(False, B, T, N, K, V, C)), dtype=torch.uint8,
+                      device=dev)
+    wsb = torch.empty(max(1, m2rnn_workspace_bytes(True, B, T, N, K, V, C)), dtype=torch.uint8,
+                      device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    names = ("gates", "fwd", "bwd")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        m2rnn_gates(d["logit"], wl.gate, d["alpha"], d["beta"], out=f)
+        if ev is not None:
+            ev[1].record(stream)
+        m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"], None, C, out=(y, HT, ckpt),
+                  workspace=wsf)
+        if ev is not None:
+            ev[2].record(stream)
+        g = m2rnn_bwd(d["k"], d["v"], d["q"], wl.gate, d["logit"], d["alpha"], d["beta"], f,
+                      d["W"], d["w_r"], None, ckpt, C, d["dy"], workspace=wsb)
+        if ev is not None:
+            ev[3].record(stream)
+        return g
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = {n: [] for n in names}
+    for ev in events:
+        for j, n in enumerate(names):
+            per_call[n].append(ev[j].elapsed_time(ev[j + 1]))
+    avg_ms = {n: float(np.mean(v)) for n, v in per_call.items()}
+    ms_step = wall * 1e3 / args.steps
+    th = B * T * N
+    flops = {"fwd": 2.0 * th * K * V * V, "bwd": 4.0 * th * K * V * V}
+    in_b = 2 if wl.bf16 else 4
+    kernels = {}
+    for n in names:
+        ms = avg_ms[n]
+        entry = {"avg_ms": ms}
+        if n in flops:
+            tf = flops[n] / (ms * 1e-3) / 1e12
+            entry.update({"bound": "mfma", "achieved_tflops": tf,
+                          "frac": tf / MFMA_F32_PEAK_TFLOPS, "tokens_heads_per_s": th / (ms * 1e-3)})
+        else:
+            gbs = th * 8 / (ms * 1e-3) / 1e9   # read logit, write f (fp32)
+            entry.update({"bound": "hbm", "achieved_gbs": gbs, "frac": gbs / HBM_PEAK_GBS})
+        kernels[n] = entry
+    # streamed bytes of the forward call: k, q, v, f in; y out
+    fwd_bytes = th * ((2 * K + V) * in_b + 4 + 4 * V)
+    kernels["fwd"]["stream_gbs"] = fwd_bytes / (avg_ms["fwd"] * 1e-3) / 1e9
+    dom = max(("fwd", "bwd"), key=lambda n: avg_ms[n])
+    dom_tf = kernels[dom]["achieved_tflops"]
+    out = {
+        "metric": "M2RNN fwd+bwd tokens*heads/s at T=16K, K=V=64 (gates + forward with "
+                  "checkpoints + backward)",
+        "value": th / (ms_step * 1e-3),
+        "unit": "tokens*heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "T": T, "n_heads": N, "K": K, "V": V,
+                   "C": C, "kvq_dtype": "bf16" if wl.bf16 else "f32", "state_dtype": "f32",
+                   "gate": "exp_softplus" if wl.gate == 1 else "sigmoid",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": f"m2rnn_{dom}", "achieved": dom_tf,
+                     "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": dom_tf / MFMA_F32_PEAK_TFLOPS, "traffic": None},
+        "fwd_only": {"tokens_heads_per_s": kernels["fwd"]["tokens_heads_per_s"],
+                     "ms": avg_ms["fwd"], "mfma_frac": kernels["fwd"]["frac"],
+                     "achieved_tflops": kernels["fwd"]["achieved_tflops"]},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = oracle_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,153 @@
+/*
+ * m2rnn.h -- C ABI of the MI355X (gfx950) M²RNN recurrence library (libm2rnn.so).
+ *
+ * The operation is the matrix-state non-linear recurrence of the review of
+ * "M²RNN: Non-Linear RNNs with Matrix-Valued States for Scalable Language
+ * Modeling" (arXiv:2603.14360v2), section 2.1, Eq. (10)-(12), with the forget
+ * gate of the pararnn-torch "ParaM2RNN" page ("Recurrence (library core)":
+ * f = sigmoid(logit)) or of the review's section 2.2, Eq. (13)/(17)
+ * (f = exp(-alpha * softplus(a + beta))).  Per batch row b and head n, from the
+ * initial state H_0 (K x V):
+ *
+ *     Z_t = tanh(H_{t-1} W_n + k_t v_t^T)          (W_n is V x V, right-multiplied)
+ *     H_t = f_t H_{t-1} + (1 - f_t) Z_t
+ *     y_t = H_t^T q_t + w_r[n] (.) v_t
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is DEVICE memory owned by the caller, C-contiguous,
+ *   in the layout stated next to it.  The library allocates nothing and keeps
+ *   no state between calls; calls are asynchronous on `stream` (a hipStream_t,
+ *   NULL = the default stream) and never synchronise the device.
+ * - Outputs are overwritten, never accumulated, and must not alias inputs.
+ * - `state_dtype` (M2RNN_F32 or M2RNN_F64) is the type of the recurrent state,
+ *   of every accumulation, and of every floating-point tensor except k, v, q:
+ *   f, logit, alpha, beta, W, w_r, H0, y, HT, ckpt, dy, dHT and every gradient.
+ *   F32 is the production path; F64 runs the same kernels in double precision.
+ * - `in_dtype` is the type of k, v, q: M2RNN_F32 or M2RNN_BF16 with an F32
+ *   state; M2RNN_F64 or M2RNN_BF16 with an F64 state.  bf16 values are widened
+ *   exactly.
+ * - Arguments are checked on the host before anything is launched; a failed
+ *   check returns its status and launches nothing.  Values on the device are
+ *   not checked (f in [0, 1], alpha >= 0, finite inputs are preconditions).
+ * - Launch failures are reported as M2RNN_ERR_HIP (hipGetLastError).
+ * - Supported sizes: B, T, n_heads >= 1; 1 <= K <= 256; 1 <= V <= 128;
+ *   B * n_heads * ceil(K / 16) <= 2^31 - 1.  Larger K or V return
+ *   M2RNN_ERR_UNSUPPORTED.
+ * - Results are bit-reproducible for the same inputs, sizes, device and build
+ *   (every reduction runs in a fixed order, without atomics).
+ */
+#ifndef M2RNN_H_
+#define M2RNN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  M2RNN_OK = 0,
+  M2RNN_ERR_INVALID_ARG = 1, /* bad size, NULL pointer, bad enum, missing/extra gate parameters */
+  M2RNN_ERR_UNSUPPORTED = 2, /* K > 256, V > 128, or an unsupported dtype pairing */
+  M2RNN_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than the *_workspace_bytes query */
+  M2RNN_ERR_HIP = 4          /* a kernel launch failed */
+} m2rnn_status;
+
+typedef enum { M2RNN_F32 = 0, M2RNN_BF16 = 1, M2RNN_F64 = 2 } m2rnn_dtype;
+
+typedef enum { M2RNN_GATE_SIGMOID = 0, M2RNN_GATE_EXP_SOFTPLUS = 1 } m2rnn_gate;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* m2rnn_status_string(int status);
+
+/*
+ * m2rnn_gates -- forget gate for every (b, t, n) at once.  The gate does not
+ * read the state (review section 2.2, last paragraph), so the whole sequence
+ * is computed in one elementwise pass.
+ *   gate_kind M2RNN_GATE_SIGMOID:      f = 1 / (1 + exp(-logit))       (ParaM2RNN "Recurrence")
+ *   gate_kind M2RNN_GATE_EXP_SOFTPLUS: f = exp(-alpha[n] * softplus(logit + beta[n]))
+ *                                        = (1 + e^{logit + beta[n]})^{-alpha[n]}   (review Eq. 13/17)
+ *   logit  [B, T, n_heads]      in, `dtype` (F32 or F64)
+ *   alpha  [n_heads]            in, EXP_SOFTPLUS only, else must be NULL
+ *   beta   [n_heads]            in, EXP_SOFTPLUS only, else must be NULL
+ *   f      [B, T, n_heads]      out
+ */
+int m2rnn_gates(int64_t B, int64_t T, int64_t n_heads, int gate_kind, int dtype,
+                const void* logit, const void* alpha, const void* beta, void* f,
+                void* stream);
+
+/*
+ * Workspace (device bytes) that m2rnn_fwd (is_bwd = 0) or m2rnn_bwd
+ * (is_bwd = 1) needs for these sizes and checkpoint interval C (C is only
+ * used for the backward); 0 means none (workspace may be NULL).  Returns 0 as
+ * well for sizes the library rejects.
+ */
+size_t m2rnn_workspace_bytes(int is_bwd, int64_t B, int64_t T, int64_t n_heads, int64_t K,
+                             int64_t V, int64_t C, int state_dtype);
+
+/*
+ * m2rnn_fwd -- the recurrence and readout of review section 2.1, Eq. (10)-(12),
+ * for all B * n_heads units, from H0 (or zero), over T steps.
+ *   k, q   [B, T, n_heads, K]   in, in_dtype
+ *   v      [B, T, n_heads, V]   in, in_dtype
+ *   f      [B, T, n_heads]      in, forget gate (from m2rnn_gates)
+ *   W      [n_heads, V, V]      in, (H W)[i][j] = sum_l H[i][l] * W[n][l][j]
+ *   w_r    [n_heads, V]         in
+ *   H0     [B, n_heads, K, V]   in, or NULL for H_0 = 0
+ *   y      [B, T, n_heads, V]   out
+ *   HT     [B, n_heads, K, V]   out, final state H_T, or NULL
+ *   ckpt   [B, n_heads, ceil(T / C), K, V]  out, ckpt[b][n][c] = H_{cC} (c = 0 is H_0),
+ *          or NULL (then C is ignored).  These are the states m2rnn_bwd restarts
+ *          from (the review's section 2.6 reruns the recurrence at the start of
+ *          the backward; storing every C-th state bounds that rerun to C steps).
+ *   C      checkpoint interval, >= 1 when ckpt != NULL
+ *   workspace / workspace_bytes: at least m2rnn_workspace_bytes(0, ...)
+ */
+int m2rnn_fwd(int64_t B, int64_t T, int64_t n_heads, int64_t K, int64_t V, int in_dtype,
+              int state_dtype, const void* k, const void* v, const void* q, const void* f,
+              const void* W, const void* w_r, const void* H0, void* y, void* HT, void* ckpt,
+              int64_t C, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * m2rnn_bwd -- reverse-time backward of m2rnn_fwd for a loss L with
+ * dL/dy = dy and dL/dH_T = dHT, following the corrected chain rule of review
+ * section 2.7 (value-residual branch restored).  With u_t = dy_t and C_t the
+ * state gradient from later steps (C_T = dHT):
+ *     R_t = C_t + q_t u_t^T,   D_t = ((1 - f_t) R_t) (.) (1 - Z_t (.) Z_t),
+ *     C_{t-1} = f_t R_t + D_t W^T,
+ *     df_t = <R_t, H_{t-1} - Z_t>_F,   dW = sum_{b,t} H_{t-1}^T D_t,
+ *     dk_t = D_t v_t,   dv_t = D_t^T k_t + w_r (.) u_t,   dq_t = H_t u_t,
+ *     dw_r = sum_{b,t} u_t (.) v_t,   dH0 = C_0,
+ * then the gate chain rule: sigmoid: dlogit = df f (1 - f); exp-softplus with
+ * x = logit + beta: dlogit = -df alpha sigmoid(x) f, dalpha = sum_{b,t} -df softplus(x) f,
+ * dbeta = sum_{b,t} dlogit.  The states are recomputed chunk by chunk from
+ * the checkpoints m2rnn_fwd wrote with the same C (review section 2.6).
+ *   k, v, q, f, W, w_r, H0     as for m2rnn_fwd (H0 NULL = zero)
+ *   gate_kind, logit, alpha, beta   as for m2rnn_gates (alpha/beta NULL for sigmoid)
+ *   ckpt   [B, n_heads, ceil(T / C), K, V]  in, from m2rnn_fwd with the same C, H0, inputs
+ *   dy     [B, T, n_heads, V]   in
+ *   dHT    [B, n_heads, K, V]   in, or NULL for zero
+ *   dk, dq [B, T, n_heads, K]   out, state_dtype
+ *   dv     [B, T, n_heads, V]   out
+ *   dlogit [B, T, n_heads]      out, dL/dlogit (sigmoid: g; exp-softplus: a)
+ *   dW     [n_heads, V, V]      out, summed over batch and time
+ *   dw_r   [n_heads, V]         out, summed over batch and time
+ *   dalpha, dbeta [n_heads]     out, EXP_SOFTPLUS only (else must be NULL)
+ *   dH0    [B, n_heads, K, V]   out, or NULL to skip
+ *   workspace / workspace_bytes: at least m2rnn_workspace_bytes(1, ...)
+ */
+int m2rnn_bwd(int64_t B, int64_t T, int64_t n_heads, int64_t K, int64_t V, int in_dtype,
+              int state_dtype, const void* k, const void* v, const void* q, int gate_kind,
+              const void* logit, const void* alpha, const void* beta, const void* f,
+              const void* W, const void* w_r, const void* H0, const void* ckpt, int64_t C,
+              const void* dy, const void* dHT, void* dk, void* dv, void* dq, void* dlogit,
+              void* dW, void* dw_r, void* dalpha, void* dbeta, void* dH0, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* M2RNN_H_ */

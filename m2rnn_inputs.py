@@ -179,3 +179,28 @@ def make_inputs(wl: Workload, seed: int | None = None, with_dy: bool | None = No
     return Inputs(wl=wl, k=k, v=v, q=q, logit=logit, alpha=alpha, beta=beta,
                   W=W.astype(f32), w_r=w_r, H0=H0, dy=dy, dHT=dHT,
                   k_bits=kb, v_bits=vb, q_bits=qb)
+
+
+def to_device(inp: Inputs, state_dtype="float32", device="cuda:0") -> dict:
+    """torch tensors of one workload on `device` (no arithmetic: dtype casts only).
+
+    k, v, q are bf16 (from the stored bit patterns) for bf16 workloads, else in
+    the state dtype; every other array is in the state dtype.
+    """
+    import torch
+
+    sd = {"float32": torch.float32, "float64": torch.float64}[state_dtype]
+    nd = {"float32": np.float32, "float64": np.float64}[state_dtype]
+
+    def t(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=nd)).to(device)
+
+    if inp.wl.bf16:
+        kv = {n: torch.from_numpy(getattr(inp, n + "_bits").view(np.int16)).view(torch.bfloat16)
+              .to(device) for n in ("k", "v", "q")}
+    else:
+        kv = {n: t(getattr(inp, n)) for n in ("k", "v", "q")}
+    out = dict(kv)
+    for name in ("logit", "alpha", "beta", "W", "w_r", "H0", "dy", "dHT"):
+        out[name] = t(getattr(inp, name))
+    return out

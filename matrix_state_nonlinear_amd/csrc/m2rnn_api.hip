@@ -1,0 +1,151 @@
+// C ABI of libm2rnn.so: argument checks, workspace sizing, kernel dispatch.
+// Declarations and the contract of every entry point are in include/m2rnn.h.
+
+#include <limits.h>
+
+#include "../../include/m2rnn.h"
+#include "m2rnn_internal.h"
+
+using namespace m2rnn;
+
+namespace {
+
+bool sizes_ok(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V) {
+  if (B < 1 || T < 1 || N < 1 || K < 1 || V < 1) return false;
+  // every element count the kernels index must stay far from int64 overflow
+  const double elems = (double)B * (double)T * (double)N * (double)(K > V ? K : V);
+  return elems < 4.0e18;
+}
+
+bool sizes_supported(int64_t B, int64_t N, int64_t K, int64_t V) {
+  if (K > 256 || V > 128) return false;
+  return (double)B * (double)N * (double)num_slabs(K) <= (double)INT_MAX;
+}
+
+size_t real_size(int state_dtype) { return state_dtype == M2RNN_F64 ? 8 : 4; }
+
+bool dtypes_ok(int in_dtype, int state_dtype) {
+  if (state_dtype == M2RNN_F32) return in_dtype == M2RNN_F32 || in_dtype == M2RNN_BF16;
+  if (state_dtype == M2RNN_F64) return in_dtype == M2RNN_F64 || in_dtype == M2RNN_BF16;
+  return false;
+}
+
+bool state_dtype_known(int state_dtype) {
+  return state_dtype == M2RNN_F32 || state_dtype == M2RNN_F64;
+}
+
+bool in_dtype_known(int in_dtype) {
+  return in_dtype == M2RNN_F32 || in_dtype == M2RNN_BF16 || in_dtype == M2RNN_F64;
+}
+
+size_t fwd_ws_bytes(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V, int state_dtype) {
+  const int64_t ns = num_slabs(K);
+  if (ns <= 1) return 0;
+  return align_up((size_t)ns * (size_t)B * (size_t)T * (size_t)N * (size_t)V *
+                      real_size(state_dtype),
+                  256);
+}
+
+size_t bwd_ws_bytes(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V, int64_t C,
+                    int state_dtype) {
+  const BwdWorkspace L = bwd_workspace_layout(B, T, N, K, V, C);
+  return align_up(L.total_elems * real_size(state_dtype), 256);
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? M2RNN_OK : M2RNN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* m2rnn_status_string(int status) {
+  switch (status) {
+    case M2RNN_OK: return "M2RNN_OK";
+    case M2RNN_ERR_INVALID_ARG: return "M2RNN_ERR_INVALID_ARG: invalid size, pointer or enum";
+    case M2RNN_ERR_UNSUPPORTED: return "M2RNN_ERR_UNSUPPORTED: K > 256, V > 128 or dtype pairing";
+    case M2RNN_ERR_WORKSPACE: return "M2RNN_ERR_WORKSPACE: workspace missing or too small";
+    case M2RNN_ERR_HIP: return "M2RNN_ERR_HIP: kernel launch failed";
+    default: return "M2RNN: unknown status";
+  }
+}
+
+size_t m2rnn_workspace_bytes(int is_bwd, int64_t B, int64_t T, int64_t n_heads, int64_t K,
+                             int64_t V, int64_t C, int state_dtype) {
+  if (!sizes_ok(B, T, n_heads, K, V) || !sizes_supported(B, n_heads, K, V) ||
+      !state_dtype_known(state_dtype) || (is_bwd && C < 1))
+    return 0;
+  return is_bwd ? bwd_ws_bytes(B, T, n_heads, K, V, C, state_dtype)
+                : fwd_ws_bytes(B, T, n_heads, K, V, state_dtype);
+}
+
+int m2rnn_gates(int64_t B, int64_t T, int64_t n_heads, int gate_kind, int dtype,
+                const void* logit, const void* alpha, const void* beta, void* f, void* stream) {
+  if (B < 1 || T < 1 || n_heads < 1) return M2RNN_ERR_INVALID_ARG;
+  if (dtype != M2RNN_F32 && dtype != M2RNN_F64) return M2RNN_ERR_INVALID_ARG;
+  if (!logit || !f) return M2RNN_ERR_INVALID_ARG;
+  if (gate_kind == M2RNN_GATE_SIGMOID) {
+    if (alpha || beta) return M2RNN_ERR_INVALID_ARG;
+  } else if (gate_kind == M2RNN_GATE_EXP_SOFTPLUS) {
+    if (!alpha || !beta) return M2RNN_ERR_INVALID_ARG;
+  } else {
+    return M2RNN_ERR_INVALID_ARG;
+  }
+  return status_of(launch_gates(B, T, n_heads, gate_kind, dtype, logit, alpha, beta, f,
+                                (hipStream_t)stream));
+}
+
+int m2rnn_fwd(int64_t B, int64_t T, int64_t n_heads, int64_t K, int64_t V, int in_dtype,
+              int state_dtype, const void* k, const void* v, const void* q, const void* f,
+              const void* W, const void* w_r, const void* H0, void* y, void* HT, void* ckpt,
+              int64_t C, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!sizes_ok(B, T, n_heads, K, V)) return M2RNN_ERR_INVALID_ARG;
+  if (!in_dtype_known(in_dtype) || !state_dtype_known(state_dtype)) return M2RNN_ERR_INVALID_ARG;
+  if (!k || !v || !q || !f || !W || !w_r || !y) return M2RNN_ERR_INVALID_ARG;
+  if (ckpt && C < 1) return M2RNN_ERR_INVALID_ARG;
+  if (!sizes_supported(B, n_heads, K, V) || !dtypes_ok(in_dtype, state_dtype))
+    return M2RNN_ERR_UNSUPPORTED;
+  const size_t need = fwd_ws_bytes(B, T, n_heads, K, V, state_dtype);
+  if (need && (!workspace || workspace_bytes < need)) return M2RNN_ERR_WORKSPACE;
+  FwdArgs a{};
+  a.k = k; a.v = v; a.q = q; a.f = f; a.W = W; a.w_r = w_r; a.H0 = H0;
+  a.y = y; a.ypart = workspace; a.HT = HT; a.ckpt = ckpt;
+  a.B = B; a.T = T; a.N = n_heads; a.K = K; a.V = V; a.C = ckpt ? C : 1;
+  a.nslab = (int)num_slabs(K);
+  return status_of(launch_fwd(a, in_dtype, state_dtype, (hipStream_t)stream));
+}
+
+int m2rnn_bwd(int64_t B, int64_t T, int64_t n_heads, int64_t K, int64_t V, int in_dtype,
+              int state_dtype, const void* k, const void* v, const void* q, int gate_kind,
+              const void* logit, const void* alpha, const void* beta, const void* f,
+              const void* W, const void* w_r, const void* H0, const void* ckpt, int64_t C,
+              const void* dy, const void* dHT, void* dk, void* dv, void* dq, void* dlogit,
+              void* dW, void* dw_r, void* dalpha, void* dbeta, void* dH0, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  if (!sizes_ok(B, T, n_heads, K, V)) return M2RNN_ERR_INVALID_ARG;
+  if (!in_dtype_known(in_dtype) || !state_dtype_known(state_dtype)) return M2RNN_ERR_INVALID_ARG;
+  if (!k || !v || !q || !logit || !f || !W || !w_r || !ckpt || !dy) return M2RNN_ERR_INVALID_ARG;
+  if (!dk || !dv || !dq || !dlogit || !dW || !dw_r) return M2RNN_ERR_INVALID_ARG;
+  if (C < 1) return M2RNN_ERR_INVALID_ARG;
+  if (gate_kind == M2RNN_GATE_SIGMOID) {
+    if (alpha || beta || dalpha || dbeta) return M2RNN_ERR_INVALID_ARG;
+  } else if (gate_kind == M2RNN_GATE_EXP_SOFTPLUS) {
+    if (!alpha || !beta || !dalpha || !dbeta) return M2RNN_ERR_INVALID_ARG;
+  } else {
+    return M2RNN_ERR_INVALID_ARG;
+  }
+  if (!sizes_supported(B, n_heads, K, V) || !dtypes_ok(in_dtype, state_dtype))
+    return M2RNN_ERR_UNSUPPORTED;
+  const size_t need = bwd_ws_bytes(B, T, n_heads, K, V, C, state_dtype);
+  if (need && (!workspace || workspace_bytes < need)) return M2RNN_ERR_WORKSPACE;
+  BwdArgs a{};
+  a.k = k; a.v = v; a.q = q; a.logit = logit; a.alpha = alpha; a.beta = beta; a.f = f;
+  a.W = W; a.w_r = w_r; a.H0 = H0; a.ckpt = ckpt; a.dy = dy; a.dHT = dHT;
+  a.dk = dk; a.dv = dv; a.dq = dq; a.dlogit = dlogit; a.dW = dW; a.dw_r = dw_r;
+  a.dalpha = dalpha; a.dbeta = dbeta; a.dH0 = dH0; a.ws = workspace;
+  a.B = B; a.T = T; a.N = n_heads; a.K = K; a.V = V; a.C = C;
+  a.nslab = (int)num_slabs(K);
+  a.gate_kind = gate_kind;
+  return status_of(launch_bwd(a, in_dtype, state_dtype, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// Device-side building blocks shared by the gfx950 M²RNN kernels.
+//
+// Everything here is written for CDNA4 (gfx950): 64-lane wavefronts, the
+// 16x16x4 fp32 / fp64 MFMA instructions, DPP row operations over 16-lane rows,
+// and 8 XCDs that each own an L2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace m2rnn {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+template <typename Real>
+struct Vec4;
+template <>
+struct Vec4<float> {
+  using type = f32x4;
+};
+template <>
+struct Vec4<double> {
+  using type = f64x4;
+};
+
+// D = A * B + C for one 16x16 tile with a contraction of 4.  Lane l supplies
+// A[l % 16][l / 16] and B[l / 16][l % 16]; it receives D[4 * (l / 16) + r][l % 16]
+// in element r of the result.
+__device__ __forceinline__ f32x4 mfma_16x16x4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f64x4 mfma_16x16x4(double a, double b, f64x4 c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+// tanh(x) = sign(x) (1 - e) / (1 + e) with e = exp(-2|x|) = 2^(-2 log2(e) |x|).
+// e lies in (0, 1], so neither term overflows; 1 - e is exact for e near 1
+// (Sterbenz), which keeps the absolute error near 1e-7 over the whole line.
+// Uses the hardware base-2 exponential and reciprocal (about 1 ulp each).
+__device__ __forceinline__ float tanh_fast(float x) {
+  const float two_log2e = 2.885390081777926814f;  // 2 / ln 2
+  const float e = __builtin_amdgcn_exp2f(-two_log2e * __builtin_fabsf(x));
+  const float t = (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e);
+  return __builtin_copysignf(t, x);
+}
+__device__ __forceinline__ double tanh_fast(double x) { return ::tanh(x); }
+
+// DPP: read the value of another lane of the same 16-lane row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_move(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
+}
+
+// Sum over the 16 lanes of each DPP row (row_ror by 8, 4, 2, 1).  Every lane of
+// the row ends with a sum; lane (row * 16) is the one callers read, so the
+// association order is fixed and results are reproducible.
+constexpr int kDppRowRor1 = 0x121;
+constexpr int kDppRowRor2 = 0x122;
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+template <typename Real>
+__device__ __forceinline__ Real row16_sum(Real x) {
+  x += dpp_move<kDppRowRor8>(x);
+  x += dpp_move<kDppRowRor4>(x);
+  x += dpp_move<kDppRowRor2>(x);
+  x += dpp_move<kDppRowRor1>(x);
+  return x;
+}
+
+// Sum over the four 16-lane rows (lanes l, l^16, l^32, l^48), via ds_swizzle-free
+// cross-row permutes.  Result valid in every lane.
+template <typename Real>
+__device__ __forceinline__ Real cross_row_sum(Real x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+// Workgroup id -> logical work id.  The dispatcher sends workgroup i to XCD
+// i % 8; this gives each XCD one contiguous range of logical ids, so units
+// with neighbouring ids (the K-row slabs of one head) share an L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  constexpr int kXcd = 8;
+  if (nblocks % kXcd != 0) return bid;
+  return (bid % kXcd) * (nblocks / kXcd) + bid / kXcd;
+}
+
+// Widening loads of the k / v / q element types.
+__device__ __forceinline__ float load_in(const float* p) { return *p; }
+__device__ __forceinline__ float load_in(const uint16_t* p) {
+  return __builtin_bit_cast(float, (uint32_t)(*p) << 16);
+}
+__device__ __forceinline__ double load_in(const double* p) { return *p; }
+
+template <typename Real, typename InT>
+__device__ __forceinline__ Real load_as(const InT* p) {
+  return (Real)load_in(p);
+}
+
+}  // namespace m2rnn

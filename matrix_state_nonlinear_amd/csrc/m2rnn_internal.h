@@ -1,0 +1,97 @@
+// Host-side interface between the C ABI (m2rnn_api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace m2rnn {
+
+enum : int { kF32 = 0, kBF16 = 1, kF64 = 2 };
+enum : int { kGateSigmoid = 0, kGateExpSoftplus = 1 };
+
+// Rows of the K x V state handled by one workgroup.  The K rows of a head are
+// independent recurrences that share W (W only mixes value columns), so a
+// head splits into ceil(K / 16) slabs that run on different compute units.
+constexpr int kSlabRows = 16;
+
+inline int64_t num_slabs(int64_t K) { return (K + kSlabRows - 1) / kSlabRows; }
+
+// Value columns padded to the kernels' tile count (multiples of 16, with the
+// tile counts 5 and 7 rounded up to 6 and 8 so waves split them evenly).
+inline int value_tiles(int64_t V) {
+  int vt = (int)((V + 15) / 16);
+  if (vt == 5) vt = 6;
+  if (vt == 7) vt = 8;
+  return vt;
+}
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct FwdArgs {
+  const void* k;
+  const void* v;
+  const void* q;
+  const void* f;
+  const void* W;
+  const void* w_r;
+  const void* H0;    // may be null
+  void* y;
+  void* ypart;       // [nslab, B, T, N, V] partial readouts when nslab > 1
+  void* HT;          // may be null
+  void* ckpt;        // may be null
+  int64_t B, T, N, K, V, C;
+  int nslab;
+};
+
+struct BwdArgs {
+  const void* k;
+  const void* v;
+  const void* q;
+  const void* logit;
+  const void* alpha;
+  const void* beta;
+  const void* f;
+  const void* W;
+  const void* w_r;
+  const void* H0;    // may be null
+  const void* ckpt;
+  const void* dy;
+  const void* dHT;   // may be null
+  void* dk;
+  void* dv;
+  void* dq;
+  void* dlogit;
+  void* dW;
+  void* dw_r;
+  void* dalpha;      // may be null
+  void* dbeta;       // may be null
+  void* dH0;         // may be null
+  void* ws;          // workspace base
+  int64_t B, T, N, K, V, C;
+  int nslab;
+  int gate_kind;
+};
+
+// Workspace layout of the backward: offsets in elements of the state type,
+// each region aligned to 64 elements.
+struct BwdWorkspace {
+  size_t states;      // per unit: (2 C + 1) slots of one slab's state tiles
+  size_t slot_elems;  // elements of one slot (VT * 64 lanes * 4)
+  size_t dv_part;     // [nslab, B, T, N, V]  (nslab > 1 only)
+  size_t df_part;     // [nslab, B, T, N]
+  size_t dW_part;     // [B * nslab, N, V, V]
+  size_t col_part;    // [row_blocks, N, V + 2] column-sum partials (dw_r, dalpha, dbeta)
+  int64_t row_blocks;
+  size_t total_elems;
+};
+BwdWorkspace bwd_workspace_layout(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V,
+                                  int64_t C);
+
+hipError_t launch_gates(int64_t B, int64_t T, int64_t N, int gate_kind, int dtype,
+                        const void* logit, const void* alpha, const void* beta, void* f,
+                        hipStream_t stream);
+hipError_t launch_fwd(const FwdArgs& a, int in_dtype, int state_dtype, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int in_dtype, int state_dtype, hipStream_t stream);
+
+}  // namespace m2rnn

@@ -1,0 +1,160 @@
+"""Python entry points with the C ABI's names: argument marshalling only.
+
+Each function checks that the torch tensors it is given are on one GPU,
+contiguous and of the shapes/dtypes the C ABI documents, allocates outputs and
+workspace with torch (device memory is the only thing torch provides here),
+and calls the library on torch's current stream.  All arithmetic happens in
+the HIP kernels.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+from ._lib import check
+
+_DT = {torch.float32: _lib.M2RNN_F32, torch.bfloat16: _lib.M2RNN_BF16,
+       torch.float64: _lib.M2RNN_F64}
+
+
+def _ptr(t):
+    return None if t is None else ctypes_ptr(t)
+
+
+def ctypes_ptr(t: torch.Tensor):
+    if not t.is_cuda:
+        raise ValueError("tensors passed to libm2rnn must live in GPU memory")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libm2rnn must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t, shape, dtype, name):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _opt(t, shape, dtype, name):
+    if t is not None:
+        _need(t, shape, dtype, name)
+
+
+def m2rnn_status_string(status: int) -> str:
+    return _lib.status_string(status)
+
+
+def m2rnn_workspace_bytes(is_bwd: bool, B: int, T: int, n_heads: int, K: int, V: int, C: int,
+                          state_dtype=torch.float32) -> int:
+    return int(_lib.lib().m2rnn_workspace_bytes(int(bool(is_bwd)), B, T, n_heads, K, V, C,
+                                                _DT[state_dtype]))
+
+
+def _workspace(nbytes: int, device, given=None):
+    if nbytes == 0:
+        return None, 0
+    if given is not None:
+        if given.numel() * given.element_size() < nbytes:
+            raise ValueError(f"workspace holds {given.numel() * given.element_size()} bytes, "
+                             f"{nbytes} needed")
+        return given, given.numel() * given.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def m2rnn_gates(logit: torch.Tensor, gate_kind: int, alpha=None, beta=None, out=None):
+    """f[B, T, N] from the gate logits (sigmoid or exp-softplus form)."""
+    if logit.dim() != 3:
+        raise ValueError("logit must be [B, T, n_heads]")
+    B, T, N = logit.shape
+    dt = logit.dtype
+    if dt not in (torch.float32, torch.float64):
+        raise ValueError("logit must be float32 or float64")
+    _opt(alpha, (N,), dt, "alpha")
+    _opt(beta, (N,), dt, "beta")
+    f = torch.empty_like(logit) if out is None else out
+    _need(f, (B, T, N), dt, "out")
+    st = _lib.lib().m2rnn_gates(B, T, N, int(gate_kind), _DT[dt], _ptr(logit), _ptr(alpha),
+                                _ptr(beta), _ptr(f), _stream(logit.device))
+    check(st, "m2rnn_gates")
+    return f
+
+
+def m2rnn_fwd(k, v, q, f, W, w_r, H0=None, C: int = 0, want_ht: bool = True,
+              out=None, workspace=None):
+    """Forward recurrence.  Returns (y, HT or None, ckpt or None).
+
+    k, q [B, T, N, K] and v [B, T, N, V] in float32 / bfloat16 (float32 state)
+    or float64 / bfloat16 (float64 state); f [B, T, N], W [N, V, V], w_r [N, V],
+    H0 [B, N, K, V] in the state dtype (taken from f).  C > 0 also writes the
+    checkpoints ckpt[B, N, ceil(T / C), K, V] with ckpt[:, :, c] = H_{cC}.
+    ``out`` may hold preallocated (y, HT, ckpt).
+    """
+    B, T, N, K = k.shape
+    V = v.shape[-1]
+    sd = f.dtype
+    _need(v, (B, T, N, V), k.dtype, "v")
+    _need(q, (B, T, N, K), k.dtype, "q")
+    _need(f, (B, T, N), sd, "f")
+    _need(W, (N, V, V), sd, "W")
+    _need(w_r, (N, V), sd, "w_r")
+    _opt(H0, (B, N, K, V), sd, "H0")
+    dev = k.device
+    if out is not None:
+        y, HT, ckpt = out
+    else:
+        y = torch.empty((B, T, N, V), dtype=sd, device=dev)
+        HT = torch.empty((B, N, K, V), dtype=sd, device=dev) if want_ht else None
+        ckpt = (torch.empty((B, N, math.ceil(T / C), K, V), dtype=sd, device=dev)
+                if C and C > 0 else None)
+    ws, wsb = _workspace(m2rnn_workspace_bytes(False, B, T, N, K, V, max(C, 1), sd), dev,
+                         workspace)
+    st = _lib.lib().m2rnn_fwd(B, T, N, K, V, _DT[k.dtype], _DT[sd], _ptr(k), _ptr(v), _ptr(q),
+                              _ptr(f), _ptr(W), _ptr(w_r), _ptr(H0), _ptr(y), _ptr(HT),
+                              _ptr(ckpt), int(C) if ckpt is not None else 0, _ptr(ws), wsb,
+                              _stream(dev))
+    check(st, "m2rnn_fwd")
+    return y, HT, ckpt
+
+
+def m2rnn_bwd(k, v, q, gate_kind: int, logit, alpha, beta, f, W, w_r, H0, ckpt, C: int, dy,
+              dHT=None, want_dh0: bool = True, workspace=None):
+    """Backward of m2rnn_fwd.  Returns a dict with dk, dv, dq, dlogit, dW, dw_r,
+    dalpha and dbeta (exp-softplus gate only, else None) and dH0 (or None)."""
+    B, T, N, K = k.shape
+    V = v.shape[-1]
+    sd = f.dtype
+    _need(v, (B, T, N, V), k.dtype, "v")
+    _need(q, (B, T, N, K), k.dtype, "q")
+    _need(logit, (B, T, N), sd, "logit")
+    _need(f, (B, T, N), sd, "f")
+    _need(W, (N, V, V), sd, "W")
+    _need(w_r, (N, V), sd, "w_r")
+    _opt(H0, (B, N, K, V), sd, "H0")
+    _need(ckpt, (B, N, math.ceil(T / C), K, V), sd, "ckpt")
+    _need(dy, (B, T, N, V), sd, "dy")
+    _opt(dHT, (B, N, K, V), sd, "dHT")
+    dev = k.device
+    e = lambda *s: torch.empty(s, dtype=sd, device=dev)  # noqa: E731
+    out = {"dk": e(B, T, N, K), "dv": e(B, T, N, V), "dq": e(B, T, N, K),
+           "dlogit": e(B, T, N), "dW": e(N, V, V), "dw_r": e(N, V),
+           "dalpha": e(N) if gate_kind == _lib.M2RNN_GATE_EXP_SOFTPLUS else None,
+           "dbeta": e(N) if gate_kind == _lib.M2RNN_GATE_EXP_SOFTPLUS else None,
+           "dH0": e(B, N, K, V) if want_dh0 else None}
+    ws, wsb = _workspace(m2rnn_workspace_bytes(True, B, T, N, K, V, C, sd), dev, workspace)
+    st = _lib.lib().m2rnn_bwd(
+        B, T, N, K, V, _DT[k.dtype], _DT[sd], _ptr(k), _ptr(v), _ptr(q), int(gate_kind),
+        _ptr(logit), _ptr(alpha), _ptr(beta), _ptr(f), _ptr(W), _ptr(w_r), _ptr(H0), _ptr(ckpt),
+        int(C), _ptr(dy), _ptr(dHT), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dq"]),
+        _ptr(out["dlogit"]), _ptr(out["dW"]), _ptr(out["dw_r"]), _ptr(out["dalpha"]),
+        _ptr(out["dbeta"]), _ptr(out["dH0"]), _ptr(ws), wsb, _stream(dev))
+    check(st, "m2rnn_bwd")
+    return out

@@ -1,0 +1,121 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+The library loads, exports every function include/m2rnn.h declares, sizes its
+workspace as documented, and rejects bad arguments with the documented status
+before any launch (every case below fails a host-side check).
+"""
+import os
+import re
+
+import pytest
+
+from matrix_state_nonlinear_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x1000  # never dereferenced: every call below is rejected on the host
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "m2rnn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(m2rnn_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        from matrix_state_nonlinear_amd import build
+        build.build()
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = header_functions()
+    assert names == sorted(_lib.SIGNATURES), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert _lib.status_string(s).startswith("M2RNN")
+    assert "unknown" in _lib.status_string(99)
+
+
+def test_workspace_sizes(L):
+    ws = L.m2rnn_workspace_bytes
+    # one slab per head: no forward workspace
+    assert ws(0, 2, 64, 1, 8, 8, 1, _lib.M2RNN_F32) == 0
+    # K = 64 -> 4 slabs of partial readouts
+    b = ws(0, 4, 100, 3, 64, 40, 1, _lib.M2RNN_F32)
+    assert b == ((4 * 4 * 100 * 3 * 40 * 4 + 255) // 256) * 256
+    assert ws(0, 4, 100, 3, 64, 40, 1, _lib.M2RNN_F64) == ((4 * 4 * 100 * 3 * 40 * 8 + 255) // 256) * 256
+    # unsupported sizes report 0
+    assert ws(0, 1, 10, 1, 300, 16, 1, _lib.M2RNN_F32) == 0
+    assert ws(1, 1, 10, 1, 16, 16, 0, _lib.M2RNN_F32) == 0
+    # backward grows with the checkpoint interval
+    assert ws(1, 2, 64, 2, 32, 64, 16, _lib.M2RNN_F32) < ws(1, 2, 64, 2, 32, 64, 32, _lib.M2RNN_F32)
+
+
+def fwd(L, **kw):
+    a = dict(B=2, T=8, N=1, K=16, V=16, ind=_lib.M2RNN_F32, sd=_lib.M2RNN_F32, k=FAKE, v=FAKE,
+             q=FAKE, f=FAKE, W=FAKE, w_r=FAKE, H0=None, y=FAKE, HT=None, ckpt=None, C=0,
+             ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return L.m2rnn_fwd(a["B"], a["T"], a["N"], a["K"], a["V"], a["ind"], a["sd"], a["k"], a["v"],
+                       a["q"], a["f"], a["W"], a["w_r"], a["H0"], a["y"], a["HT"], a["ckpt"],
+                       a["C"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_fwd_rejects_bad_arguments(L):
+    E = _lib
+    assert fwd(L, B=0) == E.M2RNN_ERR_INVALID_ARG
+    assert fwd(L, T=-1) == E.M2RNN_ERR_INVALID_ARG
+    assert fwd(L, k=None) == E.M2RNN_ERR_INVALID_ARG
+    assert fwd(L, y=None) == E.M2RNN_ERR_INVALID_ARG
+    assert fwd(L, ckpt=FAKE, C=0) == E.M2RNN_ERR_INVALID_ARG
+    assert fwd(L, ind=7) == E.M2RNN_ERR_INVALID_ARG
+    assert fwd(L, K=257) == E.M2RNN_ERR_UNSUPPORTED
+    assert fwd(L, V=129) == E.M2RNN_ERR_UNSUPPORTED
+    assert fwd(L, ind=E.M2RNN_F64) == E.M2RNN_ERR_UNSUPPORTED          # f64 inputs, f32 state
+    assert fwd(L, sd=E.M2RNN_F64, ind=E.M2RNN_F32) == E.M2RNN_ERR_UNSUPPORTED
+    assert fwd(L, K=64) == E.M2RNN_ERR_WORKSPACE                       # needs partials
+    assert fwd(L, K=64, ws=FAKE, wsb=16) == E.M2RNN_ERR_WORKSPACE
+
+
+def test_gates_rejects_bad_arguments(L):
+    E = _lib
+    g = L.m2rnn_gates
+    assert g(0, 4, 2, E.M2RNN_GATE_SIGMOID, E.M2RNN_F32, FAKE, None, None, FAKE, None) == E.M2RNN_ERR_INVALID_ARG
+    assert g(1, 4, 2, E.M2RNN_GATE_SIGMOID, E.M2RNN_F32, FAKE, FAKE, None, FAKE, None) == E.M2RNN_ERR_INVALID_ARG
+    assert g(1, 4, 2, E.M2RNN_GATE_EXP_SOFTPLUS, E.M2RNN_F32, FAKE, None, FAKE, FAKE, None) == E.M2RNN_ERR_INVALID_ARG
+    assert g(1, 4, 2, 5, E.M2RNN_F32, FAKE, None, None, FAKE, None) == E.M2RNN_ERR_INVALID_ARG
+    assert g(1, 4, 2, E.M2RNN_GATE_SIGMOID, E.M2RNN_BF16, FAKE, None, None, FAKE, None) == E.M2RNN_ERR_INVALID_ARG
+    assert g(1, 4, 2, E.M2RNN_GATE_SIGMOID, E.M2RNN_F32, None, None, None, FAKE, None) == E.M2RNN_ERR_INVALID_ARG
+
+
+def bwd(L, **kw):
+    a = dict(B=2, T=8, N=1, K=16, V=16, ind=_lib.M2RNN_F32, sd=_lib.M2RNN_F32, k=FAKE, v=FAKE,
+             q=FAKE, gate=_lib.M2RNN_GATE_SIGMOID, logit=FAKE, alpha=None, beta=None, f=FAKE,
+             W=FAKE, w_r=FAKE, H0=None, ckpt=FAKE, C=4, dy=FAKE, dHT=None, dk=FAKE, dv=FAKE,
+             dq=FAKE, dlogit=FAKE, dW=FAKE, dw_r=FAKE, dalpha=None, dbeta=None, dH0=None,
+             ws=None, wsb=0, stream=None)
+    a.update(kw)
+    keys = ["B", "T", "N", "K", "V", "ind", "sd", "k", "v", "q", "gate", "logit", "alpha", "beta",
+            "f", "W", "w_r", "H0", "ckpt", "C", "dy", "dHT", "dk", "dv", "dq", "dlogit", "dW",
+            "dw_r", "dalpha", "dbeta", "dH0", "ws", "wsb", "stream"]
+    return L.m2rnn_bwd(*[a[k] for k in keys])
+
+
+def test_bwd_rejects_bad_arguments(L):
+    E = _lib
+    assert bwd(L, C=0) == E.M2RNN_ERR_INVALID_ARG
+    assert bwd(L, ckpt=None) == E.M2RNN_ERR_INVALID_ARG
+    assert bwd(L, dy=None) == E.M2RNN_ERR_INVALID_ARG
+    assert bwd(L, dW=None) == E.M2RNN_ERR_INVALID_ARG
+    assert bwd(L, alpha=FAKE) == E.M2RNN_ERR_INVALID_ARG               # sigmoid takes no alpha
+    assert bwd(L, gate=E.M2RNN_GATE_EXP_SOFTPLUS) == E.M2RNN_ERR_INVALID_ARG
+    assert bwd(L, gate=E.M2RNN_GATE_EXP_SOFTPLUS, alpha=FAKE, beta=FAKE) == E.M2RNN_ERR_INVALID_ARG
+    assert bwd(L, V=200) == E.M2RNN_ERR_UNSUPPORTED
+    assert bwd(L) == E.M2RNN_ERR_WORKSPACE                             # always needs workspace
+    assert bwd(L, ws=FAKE, wsb=64) == E.M2RNN_ERR_WORKSPACE

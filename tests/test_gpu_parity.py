@@ -1,0 +1,227 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Small sizes (the oracle finishes in seconds) that still span several 16-row
+slabs, several 16-column tiles, ragged staging chunks and ragged checkpoint
+intervals, on the recipes of all five workloads, in both state precisions.
+
+Tolerances.  Over these short horizons the recurrence does not amplify
+rounding noticeably, so the fp32 path is held to 2e-5 max-abs on y, H_T and
+checkpoints (tighter than the stated 1e-4 / 2e-2: the per-step fp32 error is
+~1e-7 and grows by far less than 100x within ~100 steps), and the fp64 path to
+1e-11.  Gradients are compared per tensor as max|g - g_ref| <= tau *
+max(1, max|g_ref|), tau = 1e-4 (fp32) / 1e-10 (fp64).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from m2rnn_inputs import WORKLOADS, WORKLOAD_ORDER, Workload, make_inputs, to_device
+from matrix_state_nonlinear_amd import m2rnn_bwd, m2rnn_fwd, m2rnn_gates
+
+pytestmark = pytest.mark.gpu
+
+TOL_Y = {"float32": 2e-5, "float64": 1e-11}
+TAU_G = {"float32": 1e-4, "float64": 1e-10}
+
+
+def np_(t):
+    return None if t is None else t.detach().cpu().numpy().astype(np.float64)
+
+
+def gpu_forward(inp, sd, C=0):
+    d = to_device(inp, sd)
+    f = m2rnn_gates(d["logit"], inp.wl.gate, d["alpha"], d["beta"])
+    y, HT, ckpt = m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"], d["H0"], C)
+    torch.cuda.synchronize()
+    return d, f, y, HT, ckpt
+
+
+def oracle_forward(inp, C=0, keep=False):
+    f = oracle.gates(inp.wl.gate, inp.logit, inp.alpha, inp.beta)
+    return f, oracle.forward(inp.k, inp.v, inp.q, f, inp.W, inp.w_r, inp.H0, C=C,
+                             keep_states=keep)
+
+
+def small(name, **kw):
+    wl = WORKLOADS[name]
+    base = dict(B=min(wl.B, 2), T=77, N=min(wl.N, 2))
+    base.update(kw)
+    return wl.replace(**base)
+
+
+def maxerr(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
+
+
+# ---------------------------------------------------------------- gates
+
+@pytest.mark.parametrize("sd", ["float32", "float64"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "long_t16k_k64"])
+def test_gates(name, sd):
+    wl = small(name, T=300)
+    inp = make_inputs(wl)
+    inp.logit[0, :6, 0] = [-200.0, -30.0, -1e-3, 0.0, 30.0, 200.0]
+    d = to_device(inp, sd)
+    f = np_(m2rnn_gates(d["logit"], wl.gate, d["alpha"], d["beta"]))
+    ref = oracle.gates(wl.gate, inp.logit.astype(np.float64 if sd == "float64" else np.float32),
+                       inp.alpha, inp.beta)
+    tol = 2e-7 if sd == "float32" else 1e-15
+    assert maxerr(f, ref) <= tol
+    assert np.all((f >= 0) & (f <= 1))
+
+
+# ---------------------------------------------------------------- forward
+
+@pytest.mark.parametrize("sd", ["float32", "float64"])
+@pytest.mark.parametrize("name", WORKLOAD_ORDER)
+def test_forward_workload_recipes(name, sd):
+    wl = small(name)
+    inp = make_inputs(wl)
+    C = 16
+    _, f, y, HT, ckpt = gpu_forward(inp, sd, C=C)
+    fo, o = oracle_forward(inp, C=C)
+    tol = TOL_Y[sd]
+    ey, eh, ec = maxerr(np_(y), o["y"]), maxerr(np_(HT), o["HT"]), maxerr(np_(ckpt), o["ckpt"])
+    print(f"{name} {sd}: y {ey:.2e} HT {eh:.2e} ckpt {ec:.2e}")
+    assert ey <= tol and eh <= tol and ec <= tol
+
+
+SHAPES = [  # (K, V): slab and tile edge cases
+    (1, 1), (15, 5), (16, 16), (17, 17), (40, 40), (33, 72), (24, 100), (256, 16), (48, 128),
+]
+
+
+@pytest.mark.parametrize("sd", ["float32", "float64"])
+@pytest.mark.parametrize("K,V", SHAPES)
+def test_forward_shapes_with_h0_and_ragged_checkpoints(K, V, sd):
+    wl = WORKLOADS["fp32_k64"].replace(B=2, T=45, N=3, K=K, V=V, kq_scale=1 / math.sqrt(K),
+                                       v_scale=1 / math.sqrt(V), w_scale=1 / math.sqrt(V))
+    inp = make_inputs(wl, with_h0=True)
+    C = 7
+    _, f, y, HT, ckpt = gpu_forward(inp, sd, C=C)
+    fo, o = oracle_forward(inp, C=C)
+    tol = TOL_Y[sd]
+    assert maxerr(np_(y), o["y"]) <= tol
+    assert maxerr(np_(HT), o["HT"]) <= tol
+    assert maxerr(np_(ckpt), o["ckpt"]) <= tol
+
+
+@pytest.mark.parametrize("T", [1, 2, 31, 32, 33, 200])
+def test_forward_sequence_lengths(T):
+    wl = small("long_t16k_k64", T=T, B=1)
+    inp = make_inputs(wl)
+    _, f, y, HT, ckpt = gpu_forward(inp, "float32", C=32)
+    fo, o = oracle_forward(inp, C=32)
+    assert maxerr(np_(y), o["y"]) <= TOL_Y["float32"]
+    assert maxerr(np_(HT), o["HT"]) <= TOL_Y["float32"]
+
+
+def test_forward_gate_one_keeps_state_exactly():
+    wl = small("fp32_k64", T=40)
+    inp = make_inputs(wl, with_h0=True)
+    d = to_device(inp, "float32")
+    f = torch.ones_like(d["logit"])
+    y, HT, _ = m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"], d["H0"])
+    assert torch.equal(HT, d["H0"])
+    o = oracle.forward(inp.k, inp.v, inp.q, np.ones_like(inp.logit), inp.W, inp.w_r, inp.H0)
+    assert maxerr(np_(y), o["y"]) <= 1e-6
+
+
+def test_forward_gate_zero_w_zero_is_tanh_outer():
+    wl = small("fp32_k64", T=5)
+    inp = make_inputs(wl)
+    d = to_device(inp, "float32")
+    f = torch.zeros_like(d["logit"])
+    W = torch.zeros_like(d["W"])
+    _, HT, _ = m2rnn_fwd(d["k"], d["v"], d["q"], f, W, d["w_r"])
+    want = np.tanh(inp.k[:, -1, :, :, None].astype(np.float64) * inp.v[:, -1, :, None, :])
+    assert maxerr(np_(HT), want) <= 3e-7
+
+
+def test_forward_chunked_equals_full_bitwise_and_deterministic():
+    wl = small("long_t16k_k64", T=150, B=2)
+    inp = make_inputs(wl)
+    d = to_device(inp, "float32")
+    f = m2rnn_gates(d["logit"], wl.gate, d["alpha"], d["beta"])
+    y, HT, _ = m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"])
+    y2, HT2, _ = m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"])
+    assert torch.equal(y, y2) and torch.equal(HT, HT2)
+    T1 = 61
+    sl = lambda t, a, b: t[:, a:b].contiguous()  # noqa: E731
+    ya, Ha, _ = m2rnn_fwd(sl(d["k"], 0, T1), sl(d["v"], 0, T1), sl(d["q"], 0, T1),
+                          sl(f, 0, T1), d["W"], d["w_r"])
+    yb, Hb, _ = m2rnn_fwd(sl(d["k"], T1, 150), sl(d["v"], T1, 150), sl(d["q"], T1, 150),
+                          sl(f, T1, 150), d["W"], d["w_r"], Ha)
+    assert torch.equal(torch.cat([ya, yb], 1), y)
+    assert torch.equal(Hb, HT)
+
+
+def test_forward_state_stays_in_unit_box():
+    wl = small("long_t16k_k64", T=500, B=2, N=4)
+    inp = make_inputs(wl)
+    _, f, y, HT, ckpt = gpu_forward(inp, "float32", C=1)
+    assert float(ckpt.abs().max()) <= 1.0
+
+
+# ---------------------------------------------------------------- backward
+
+def gpu_backward(inp, sd, C):
+    d, f, y, HT, ckpt = gpu_forward(inp, sd, C=C)
+    g = m2rnn_bwd(d["k"], d["v"], d["q"], inp.wl.gate, d["logit"], d["alpha"], d["beta"], f,
+                  d["W"], d["w_r"], d["H0"], ckpt, C, d["dy"], d["dHT"])
+    torch.cuda.synchronize()
+    return {k_: np_(v_) for k_, v_ in g.items()}
+
+
+def oracle_backward(inp):
+    f = oracle.gates(inp.wl.gate, inp.logit, inp.alpha, inp.beta)
+    return oracle.backward(inp.k, inp.v, inp.q, f, inp.W, inp.w_r, inp.dy, inp.H0, inp.dHT,
+                           gate_kind=inp.wl.gate, logit=inp.logit, alpha=inp.alpha,
+                           beta=inp.beta)
+
+
+def check_grads(g, ref, tau, label=""):
+    worst = {}
+    for name, r in ref.items():
+        if name == "df" or r is None:
+            continue
+        scale = max(1.0, float(np.max(np.abs(r))))
+        err = maxerr(g[name], r) / scale
+        worst[name] = err
+    print(label, {k_: f"{v_:.1e}" for k_, v_ in worst.items()})
+    bad = {k_: v_ for k_, v_ in worst.items() if not v_ <= tau}
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("sd", ["float32", "float64"])
+@pytest.mark.parametrize("name", WORKLOAD_ORDER)
+def test_backward_workload_recipes(name, sd):
+    wl = small(name, T=70)
+    inp = make_inputs(wl, with_dy=True, with_h0=True, with_dht=True)
+    g = gpu_backward(inp, sd, C=16)
+    check_grads(g, oracle_backward(inp), TAU_G[sd], f"{name} {sd}")
+
+
+@pytest.mark.parametrize("K,V,C", [(1, 1, 1), (17, 40, 7), (40, 72, 64), (33, 100, 5),
+                                   (16, 128, 3)])
+def test_backward_shapes(K, V, C):
+    wl = WORKLOADS["fwd_bwd_k32_v128"].replace(B=2, T=29, N=2, K=K, V=V,
+                                               kq_scale=1 / math.sqrt(K),
+                                               v_scale=1 / math.sqrt(V), w_scale=1 / math.sqrt(V))
+    inp = make_inputs(wl, with_dy=True, with_h0=True, with_dht=True)
+    for sd in ("float32", "float64"):
+        g = gpu_backward(inp, sd, C=C)
+        check_grads(g, oracle_backward(inp), TAU_G[sd], f"K{K} V{V} C{C} {sd}")
+
+
+def test_backward_deterministic():
+    wl = small("fwd_bwd_k32_v128", T=50)
+    inp = make_inputs(wl, with_dy=True)
+    g1 = gpu_backward(inp, "float32", C=16)
+    g2 = gpu_backward(inp, "float32", C=16)
+    for k_ in g1:
+        if g1[k_] is not None:
+            assert np.array_equal(g1[k_], g2[k_]), k_
