@@ -18,7 +18,7 @@
 // sums across slabs, done by fixed-order reduction kernels afterwards.
 //
 // MFMA layouts.  C W-product: (D W^T)^T = W D^T, A = W (registers), B = D^T,
-// with the same contraction enumeration pi(s, g) = 16 (s / 4) + 4 g + s % 4 as
+// with the same contraction enumeration pi(s, g) = 16 (s / 4) + m(g, s % 4) as
 // the forward, so D's own tiles feed the B operand straight from registers and
 // the other waves' tiles come through LDS.  dW: output tile (l, j), A[l][i] =
 // H_{t-1}[i][l], B[i][j] = D[i][j], contraction over the 16 slab rows in four
@@ -112,7 +112,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
 #pragma unroll
     for (int s0 = 0; s0 < NS; ++s0) {
       const int s = (s0 + 4 * TPW * w) % NS;
-      const int l = 16 * (s >> 2) + 4 * g + (s & 3);
+      const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
       const bool ok = col < V && l < V;
       wf[p][s0] = ok ? Wp[((int64_t)n * V + l) * V + col] : Real(0);
       wb[p][s0] = ok ? Wp[((int64_t)n * V + col) * V + l] : Real(0);
@@ -122,7 +122,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
   auto slot_at = [&](int64_t s, int p) -> R4& {
     return slots[((size_t)s * VT + (w * TPW + p)) * 64 + lane];
   };
-  auto col_of = [&](int p, int r) { return (w * TPW + p) * 16 + 4 * g + r; };
+  auto col_of = [&](int p, int r) { return (w * TPW + p) * 16 + acc_m<Real>(g, r); };
   const int64_t state_base = (((int64_t)b * N + n) * K + row) * V;
 
   // state gradient C_T = dHT
@@ -310,8 +310,10 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
       // dW += H_{t-1}^T D over the slab's rows
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const int idx = 16 * (li >> 2) + 4 * kk + g;
-        const int rr = li & 3;
+        // element (row 4 kk + g, column 16 c + li) of a tile in the exchange
+        // buffer sits in lane 16 acc_g(li) + row, element acc_r(li)
+        const int idx = 16 * acc_g<Real>(li) + 4 * kk + g;
+        const int rr = acc_r<Real>(li);
         Real aop[TPW];
 #pragma unroll
         for (int p = 0; p < TPW; ++p)
@@ -336,7 +338,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
       }
     }
   }
-  // this slab's share of dW: lane holds dW[16 c + 4 g + r][16 jt + li]
+  // this slab's share of dW: lane holds dW[16 c + m(g, r)][16 jt + li]
   Real* dWp = ws + L.dW_part + (((size_t)b * nslab + slab) * N + n) * V * V;
 #pragma unroll
   for (int p = 0; p < TPW; ++p) {
@@ -344,7 +346,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
     for (int jt = 0; jt < VT; ++jt) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int l = (w * TPW + p) * 16 + 4 * g + r;
+        const int l = (w * TPW + p) * 16 + acc_m<Real>(g, r);
         const int j = jt * 16 + li;
         if (l < V && j < V) dWp[(int64_t)l * V + j] = dWacc[p][jt][r];
       }

@@ -25,13 +25,29 @@ struct Vec4<double> {
 };
 
 // D = A * B + C for one 16x16 tile with a contraction of 4.  Lane l supplies
-// A[l % 16][l / 16] and B[l / 16][l % 16]; it receives D[4 * (l / 16) + r][l % 16]
-// in element r of the result.
+// A[l % 16][l / 16] and B[l / 16][l % 16] (both precisions); element r of its
+// result holds D[acc_m<Real>(l / 16, r)][l % 16], where the row index differs
+// between the two instructions: 4 g + r for fp32, 4 r + g for fp64 (rows are
+// interleaved across the four 16-lane groups in the fp64 instruction).
 __device__ __forceinline__ f32x4 mfma_16x16x4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f64x4 mfma_16x16x4(double a, double b, f64x4 c) {
   return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+template <typename Real>
+__device__ __forceinline__ constexpr int acc_m(int g, int r) {
+  return sizeof(Real) == 4 ? 4 * g + r : 4 * r + g;
+}
+// Inverse of acc_m: the lane group and element holding accumulator row m.
+template <typename Real>
+__device__ __forceinline__ constexpr int acc_g(int m) {
+  return sizeof(Real) == 4 ? (m >> 2) : (m & 3);
+}
+template <typename Real>
+__device__ __forceinline__ constexpr int acc_r(int m) {
+  return sizeof(Real) == 4 ? (m & 3) : (m >> 2);
 }
 
 // tanh(x) = sign(x) (1 - e) / (1 + e) with e = exp(-2|x|) = 2^(-2 log2(e) |x|).

@@ -14,10 +14,11 @@
 // Inside a workgroup each wave owns TPW 16-column tiles of the slab.  The step
 // is computed transposed, (H W)^T = W^T H^T, on the 16x16x4 MFMA: W^T is the
 // A operand (held in registers for the whole sequence), H^T the B operand.
-// The MFMA result layout (lane l holds row l % 16, columns 4 (l / 16) + r) is
-// then exactly the B-operand layout of the next step, provided the
-// contraction index is enumerated as pi(s, g) = 16 (s / 4) + 4 g + (s % 4) for
-// MFMA number s and lane row-group g.  So the state never leaves registers:
+// The MFMA result layout (lane l holds row l % 16 and, in element r, column
+// 16 c + m(g, r) with g = l / 16 and m the instruction's accumulator row map)
+// is then exactly the B-operand layout of the next step, provided the
+// contraction index of MFMA number s is enumerated as
+// pi(s, g) = 16 (s / 4) + m(g, s % 4).  So the state never leaves registers:
 // its own tiles stay in the accumulators and the other waves' tiles arrive
 // through one 16-byte LDS write and (VT / TPW - 1) 16-byte LDS reads per lane
 // per step, with no shuffles or transposes.
@@ -94,19 +95,19 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
 #pragma unroll
     for (int s0 = 0; s0 < NS; ++s0) {
       const int s = (s0 + 4 * TPW * w) % NS;
-      const int l = 16 * (s >> 2) + 4 * g + (s & 3);
+      const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
       wa[p][s0] = (col < V && l < V) ? Wp[((int64_t)n * V + l) * V + col] : Real(0);
     }
   }
 
-  // ---- initial state: own tiles hold row `row`, columns 16 c + 4 g + r.
+  // ---- initial state: own tiles hold row `row`, columns 16 c + m(g, r).
   R4 hown[TPW];
   const int64_t state_base = (((int64_t)b * N + n) * K + row) * V;
 #pragma unroll
   for (int p = 0; p < TPW; ++p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int col = (w * TPW + p) * 16 + 4 * g + r;
+      const int col = (w * TPW + p) * 16 + acc_m<Real>(g, r);
       hown[p][r] = (a.H0 && row_ok && col < V) ? ((const Real*)a.H0)[state_base + col] : Real(0);
     }
   }
@@ -116,7 +117,7 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
     for (int p = 0; p < TPW; ++p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int col = (w * TPW + p) * 16 + 4 * g + r;
+        const int col = (w * TPW + p) * 16 + acc_m<Real>(g, r);
         if (row_ok && col < V) dst[col] = hown[p][r];
       }
     }
@@ -204,8 +205,9 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
       R4 acc[TPW];
 #pragma unroll
       for (int p = 0; p < TPW; ++p) {
-        const R4 vv = *(const R4*)&sm.v[sb][tt][(w * TPW + p) * 16 + 4 * g];
-        acc[p] = kv * vv;  // rank-1 write k_i v_j
+#pragma unroll
+        for (int r = 0; r < 4; ++r)  // rank-1 write k_i v_j
+          acc[p][r] = kv * sm.v[sb][tt][(w * TPW + p) * 16 + acc_m<Real>(g, r)];
       }
 #pragma unroll
       for (int s0 = 0; s0 < NS; ++s0) {
@@ -230,10 +232,13 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
       // readout of the updated state: sum over the 16 rows of the slab
 #pragma unroll
       for (int p = 0; p < TPW; ++p) {
-        R4 yv;
+        Real yv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) yv[r] = row16_sum(hown[p][r] * qv);
-        if (li == 0) *(R4*)&sm.y[sb][tt][(w * TPW + p) * 16 + 4 * g] = yv;
+        if (li == 0) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sm.y[sb][tt][(w * TPW + p) * 16 + acc_m<Real>(g, r)] = yv[r];
+        }
       }
       if (a.ckpt && ((t + 1) % a.C) == 0 && (t + 1) < T) {
         write_state((Real*)a.ckpt + ((((int64_t)b * N + n) * nck + (t + 1) / a.C) * K + row) * V);
