@@ -90,6 +90,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
   const int b = (int)(bn / N);
   const int row = slab * 16 + li;
   const bool row_ok = row < K;
+  const int64_t rowc = row_ok ? row : K - 1;  // clamped row for unconditional loads
 
   const InT* __restrict__ kp = (const InT*)a.k;
   const InT* __restrict__ vp = (const InT*)a.v;
@@ -172,25 +173,39 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
         for (int r = 0; r < 4; ++r) hb[4 * q0 + r] = t4[r];
       }
     }
-    for (int64_t tt = 0; tt < Lc; ++tt) {
-      const int64_t t = t0 + tt;
-      const int64_t tok = ((int64_t)b * T + t) * N + n;
-      const Real kv = row_ok ? load_as<Real>(kp + tok * K + row) : Real(0);
-      const Real ft = fp[tok];
-      R4 acc[TPW];
+    // inputs of one recompute step (issued a step ahead of their use)
+    struct FwdIn {
+      Real kv, ft;
+      R4 vv[TPW];
+    };
+    auto load_fwd_in = [&](int64_t t) {
+      FwdIn in;
+      const int64_t tok = ((int64_t)b * T + clamp_idx(t, T - 1)) * N + n;
+      in.kv = load_sel<Real>(kp, tok * K + rowc, row_ok);
+      in.ft = fp[tok];
 #pragma unroll
-      for (int p = 0; p < TPW; ++p) {
+      for (int p = 0; p < TPW; ++p)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int col = col_of(p, r);
-          acc[p][r] = kv * (col < V ? load_as<Real>(vp + tok * V + col) : Real(0));
+          in.vv[p][r] = load_sel<Real>(vp, tok * V + clamp_idx(col, V - 1), col < V);
         }
-      }
+      return in;
+    };
+    FwdIn fin = load_fwd_in(t0);
+    for (int64_t tt = 0; tt < Lc; ++tt) {
+      const int64_t t = t0 + tt;
+      const FwdIn cur = fin;
+      fin = load_fwd_in(t + 1);
+      R4 acc[TPW];
+#pragma unroll
+      for (int p = 0; p < TPW; ++p) acc[p] = cur.kv * cur.vv[p];
 #pragma unroll
       for (int s0 = 0; s0 < NS; ++s0) {
 #pragma unroll
         for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wf[p][s0], hb[s0], acc[p]);
       }
+      const Real ft = cur.ft;
       const Real omf = Real(1) - ft;
 #pragma unroll
       for (int p = 0; p < TPW; ++p) {
@@ -221,37 +236,63 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
     __syncthreads();  // recompute exchange reads are done before xb is reused
 
     // ---------------- 2. reverse scan over the interval
-    for (int64_t tt = Lc - 1; tt >= 0; --tt) {
-      const int64_t t = t0 + tt;
-      const int64_t tok = ((int64_t)b * T + t) * N + n;
-      const Real kv = row_ok ? load_as<Real>(kp + tok * K + row) : Real(0);
-      const Real qv = row_ok ? load_as<Real>(qp + tok * K + row) : Real(0);
-      const Real ft = fp[tok];
-      R4 Hp[TPW], Hc[TPW], Z[TPW], R[TPW], D[TPW], vv[TPW], uu[TPW];
-      Real dqp = 0, dkp = 0, dfp = 0;
+    // inputs of one reverse step (issued a step ahead of their use)
+    struct BwdIn {
+      Real kv, qv, ft;
+      R4 vv[TPW], uu[TPW], Hp[TPW], Z[TPW];
+    };
+    auto load_bwd_in = [&](int64_t tt) {
+      BwdIn in;
+      const int64_t ttc = tt < 0 ? 0 : tt;
+      const int64_t tok = ((int64_t)b * T + t0 + ttc) * N + n;
+      in.kv = load_sel<Real>(kp, tok * K + rowc, row_ok);
+      in.qv = load_sel<Real>(qp, tok * K + rowc, row_ok);
+      in.ft = fp[tok];
 #pragma unroll
       for (int p = 0; p < TPW; ++p) {
-        Hp[p] = slot_at(tt, p);
-        Hc[p] = slot_at(tt + 1, p);
-        Z[p] = slot_at(C + 1 + tt, p);
+        in.Hp[p] = slot_at(ttc, p);
+        in.Z[p] = slot_at(C + 1 + ttc, p);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int col = col_of(p, r);
-          const bool ok = col < V;
-          vv[p][r] = ok ? load_as<Real>(vp + tok * V + col) : Real(0);
-          uu[p][r] = ok ? dyp[tok * V + col] : Real(0);
-          R[p][r] = Cg[p][r] + qv * uu[p][r];
-          dqp += Hc[p][r] * uu[p][r];
-          D[p][r] = (Real(1) - ft) * R[p][r] * (Real(1) - Z[p][r] * Z[p][r]);
-          dfp += R[p][r] * (Hp[p][r] - Z[p][r]);
-          dkp += D[p][r] * vv[p][r];
+          const int64_t i = tok * V + clamp_idx(col, V - 1);
+          in.vv[p][r] = load_sel<Real>(vp, i, col < V);
+          in.uu[p][r] = load_sel<Real>(dyp, i, col < V);
+        }
+      }
+      return in;
+    };
+    R4 Hc[TPW];  // H_t, the state after the step being reversed
+#pragma unroll
+    for (int p = 0; p < TPW; ++p) Hc[p] = slot_at(Lc, p);
+    BwdIn bin = load_bwd_in(Lc - 1);
+    for (int64_t tt = Lc - 1; tt >= 0; --tt) {
+      const int64_t t = t0 + tt;
+      const int64_t tok = ((int64_t)b * T + t) * N + n;
+      const BwdIn cur = bin;
+      bin = load_bwd_in(tt - 1);
+      const Real kv = cur.kv, qv = cur.qv, ft = cur.ft;
+      R4 R[TPW], D[TPW];
+      Real dqp = 0, dkp = 0, dfp = 0;
+#pragma unroll
+      for (int p = 0; p < TPW; ++p) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const Real u = cur.uu[p][r];
+          const Real z = cur.Z[p][r];
+          R[p][r] = Cg[p][r] + qv * u;
+          dqp += Hc[p][r] * u;
+          D[p][r] = (Real(1) - ft) * R[p][r] * (Real(1) - z * z);
+          dfp += R[p][r] * (cur.Hp[p][r] - z);
+          dkp += D[p][r] * cur.vv[p][r];
         }
       }
       const int buf = (int)(t & 1);
 #pragma unroll
       for (int p = 0; p < TPW; ++p) {
         sm.xd[buf][w * TPW + p][lane] = D[p];
-        sm.xb[buf][w * TPW + p][lane] = Hp[p];
+        sm.xb[buf][w * TPW + p][lane] = cur.Hp[p];
+        Hc[p] = cur.Hp[p];  // H_{t-1} is the next (earlier) step's H_t
       }
       dqp = cross_row_sum(dqp);
       dkp = cross_row_sum(dkp);
@@ -270,7 +311,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
           const int col = col_of(p, r);
           if (li == 0 && col < V) {
             if (nslab == 1) {
-              ((Real*)a.dv)[tok * V + col] = s + wrp[(int64_t)n * V + col] * uu[p][r];
+              ((Real*)a.dv)[tok * V + col] = s + wrp[(int64_t)n * V + col] * cur.uu[p][r];
             } else {
               dv_part[slab * tok_stride * V + tok * V + col] = s;
             }

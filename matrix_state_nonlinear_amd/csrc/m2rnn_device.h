@@ -122,4 +122,15 @@ __device__ __forceinline__ Real load_as(const InT* p) {
   return (Real)load_in(p);
 }
 
+// Load p[i] when `ok`, else 0.  The caller passes an index that is in bounds
+// either way (clamped), so the load is issued unconditionally and the value is
+// selected afterwards: a guarded load would become a branch whose join waits
+// for the load, serialising the whole batch of prefetch loads.
+template <typename Real, typename InT>
+__device__ __forceinline__ Real load_sel(const InT* p, int64_t i, bool ok) {
+  const Real x = load_as<Real>(p + i);
+  return ok ? x : Real(0);
+}
+__device__ __forceinline__ int64_t clamp_idx(int64_t x, int64_t hi) { return x < hi ? x : hi; }
+
 }  // namespace m2rnn

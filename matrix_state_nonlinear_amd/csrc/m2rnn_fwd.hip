@@ -43,19 +43,20 @@ struct FwdTraits {
   static constexpr int NT = 64 * NW;                 // threads per workgroup
   static constexpr int NS = 4 * VT;                  // MFMAs per tile per step
   static constexpr int TC = sizeof(Real) == 4 ? (VP <= 64 ? 32 : 16)
-                                              : (VP <= 32 ? 32 : (VP <= 64 ? 16 : 4));
+                                              : (VP <= 32 ? 32 : (VP <= 64 ? 16 : 8));
   static constexpr int NV_PER = (TC * VP + NT - 1) / NT;   // staged v values per thread
   static constexpr int NKQ_PER = (TC * 32 + NT - 1) / NT;  // staged k and q values per thread
-  static constexpr int NY_PER = NV_PER;
+  static_assert(TC >= 4, "a staging chunk must hold at least 4 steps");
 };
 
-template <typename Real, int VT, int TC>
+template <typename Real, int VT, int TC, int NT>
 struct FwdSmem {
   using R4 = typename Vec4<Real>::type;
   R4 xb[2][VT][64];           // state exchange, double-buffered by step parity
+  R4 y[2][TC][4 * VT];        // partial readouts, lane order (16 c + 4 g + r), per chunk
+  R4 ydump[NT];               // sink for the readout writes of lanes that hold no result
   Real kq[2][TC][16][2];      // staged (k_i, q_i) per step
   Real v[2][TC][16 * VT];     // staged v per step
-  Real y[2][TC][16 * VT];     // readouts of a chunk, written back together
   Real f[2][TC];              // staged gate
   Real wr[16 * VT];           // w_r of this head
 };
@@ -66,7 +67,7 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
   using Tr = FwdTraits<Real, VT>;
   using R4 = typename Vec4<Real>::type;
   constexpr int VP = Tr::VP, TPW = Tr::TPW, NS = Tr::NS, TC = Tr::TC, NT = Tr::NT;
-  __shared__ FwdSmem<Real, VT, TC> sm;
+  __shared__ FwdSmem<Real, VT, TC, NT> sm;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, g = lane >> 4, li = lane & 15;
@@ -122,18 +123,27 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
       }
     }
   };
-  if (a.ckpt) write_state((Real*)a.ckpt + ((((int64_t)b * N + n) * nck + 0) * K + row) * V);
+  Real* ck_next = nullptr;   // where the next checkpoint goes
+  if (a.ckpt) {
+    Real* ck0 = (Real*)a.ckpt + ((((int64_t)b * N + n) * nck) * K + row) * V;
+    write_state(ck0);
+    ck_next = ck0 + K * V;
+  }
+  const int64_t ck_stride = K * V;
 
   // ---- staging of k, q, v, f for one chunk of TC steps.
   Real st_v[Tr::NV_PER], st_kq[Tr::NKQ_PER], st_f = Real(0);
+  // Every load is issued unconditionally from a clamped (in-bounds) address and
+  // masked afterwards, so the loads of a chunk are all in flight at once.
   auto load_chunk = [&](int64_t t0) {
 #pragma unroll
     for (int m = 0; m < Tr::NV_PER; ++m) {
       const int e = tid + m * NT;
       const int tt = e / VP, j = e % VP;
       const int64_t t = t0 + tt;
-      st_v[m] = (tt < TC && j < V && t < T)
-                    ? load_as<Real>(vp + (((int64_t)b * T + t) * N + n) * V + j) : Real(0);
+      const bool ok = tt < TC && j < V && t < T;
+      const int64_t tc = clamp_idx(t, T - 1);
+      st_v[m] = load_sel<Real>(vp, (((int64_t)b * T + tc) * N + n) * V + clamp_idx(j, V - 1), ok);
     }
 #pragma unroll
     for (int m = 0; m < Tr::NKQ_PER; ++m) {
@@ -141,13 +151,15 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
       const int tt = e >> 5, which = (e >> 4) & 1, i = e & 15;
       const int64_t t = t0 + tt;
       const int rr = slab * 16 + i;
+      const bool ok = tt < TC && rr < K && t < T;
+      const int64_t tc = clamp_idx(t, T - 1);
       const InT* src = which ? qp : kp;
-      st_kq[m] = (tt < TC && rr < K && t < T)
-                     ? load_as<Real>(src + (((int64_t)b * T + t) * N + n) * K + rr) : Real(0);
+      st_kq[m] = load_sel<Real>(src, (((int64_t)b * T + tc) * N + n) * K + clamp_idx(rr, K - 1), ok);
     }
-    if (tid < TC) {
+    {
       const int64_t t = t0 + tid;
-      st_f = (t < T) ? fp[((int64_t)b * T + t) * N + n] : Real(0);
+      const bool ok = tid < TC && t < T;
+      st_f = load_sel<Real>(fp, ((int64_t)b * T + clamp_idx(t, T - 1)) * N + n, ok);
     }
   };
   auto store_chunk = [&](int buf) {
@@ -164,9 +176,34 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
     if (tid < TC) sm.f[buf][tid] = st_f;
   };
 
+  Real* __restrict__ yout = (Real*)a.y;
+  Real* __restrict__ ypart = (Real*)a.ypart;
+  const int64_t slab_stride = B * T * N * V;
+  // write back one chunk of partial readouts (the y staging is in lane order)
+  auto flush = [&](int64_t ch, int buf) {
+    const int64_t t0 = ch * TC;
+    const int tn = (int)((T - t0) < TC ? (T - t0) : TC);
+    for (int e = tid; e < TC * VP; e += NT) {
+      const int tt = e / VP, jl = e % VP;
+      const int c = jl >> 4, gg = (jl >> 2) & 3, rr = jl & 3;
+      const int j = c * 16 + acc_m<Real>(gg, rr);
+      if (tt < tn && j < V) {
+        const int64_t off = (((int64_t)b * T + t0 + tt) * N + n) * V + j;
+        const Real val = sm.y[buf][tt][jl >> 2][rr];
+        if (nslab == 1) {
+          yout[off] = val + sm.wr[j] * sm.v[buf][tt][j];
+        } else {
+          ypart[slab * slab_stride + off] = val;
+        }
+      }
+    }
+  };
+
+  const int64_t nchunks = (T + TC - 1) / TC;
   for (int j = tid; j < VP; j += NT) sm.wr[j] = j < V ? wrp[(int64_t)n * V + j] : Real(0);
   load_chunk(0);
   store_chunk(0);
+  if (nchunks > 1) load_chunk(TC);
 
   // ---- first exchange: the full slab of H_0 as the B operand.
   Real hb[NS];
@@ -175,105 +212,156 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
   __syncthreads();
 #pragma unroll
   for (int q0 = 0; q0 < VT; ++q0) {
-    R4 t4;
-    if (q0 < TPW) {
-      t4 = hown[q0];
-    } else {
-      t4 = sm.xb[1][(q0 + TPW * w) % VT][lane];
-    }
+    const R4 t4 = q0 < TPW ? hown[q0] : sm.xb[1][(q0 + TPW * w) % VT][lane];
 #pragma unroll
     for (int r = 0; r < 4; ++r) hb[4 * q0 + r] = t4[r];
   }
 
-  Real* __restrict__ yout = (Real*)a.y;
-  Real* __restrict__ ypart = (Real*)a.ypart;
-  const int64_t slab_stride = B * T * N * V;
+  // ---- inputs of step 0
+  R4 acc_init[TPW];
+  Real q_cur, f_cur;
+  {
+    const Real kv = sm.kq[0][0][li][0];
+    q_cur = sm.kq[0][0][li][1];
+    f_cur = sm.f[0][0];
+#pragma unroll
+    for (int p = 0; p < TPW; ++p)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        acc_init[p][r] = kv * sm.v[0][0][(w * TPW + p) * 16 + acc_m<Real>(g, r)];
+  }
+  Real q_prev = Real(0);
+  // Readout destination of the previous step.  Lane 0 of each 16-lane group
+  // holds the row sums and writes them (tile p at yslot + 4 p); every other
+  // lane writes its own slot of ydump, so the store needs no branch.  Step 0
+  // has no previous step: everyone writes ydump.
+  R4* const ydump_me = &sm.ydump[tid];
+  R4* yslot = ydump_me;
+  const int ystep_writer = li == 0 ? 4 : 0;
+  int ystep = 0;
+  // y staging address of this lane for circular slot 0 (writers only)
+  R4* const ybase = li == 0 ? &sm.y[0][0][(w * TPW) * 4 + g] : ydump_me;
+  const int yslot_stride = li == 0 ? 4 * VT : 0;  // R4 elements per staging slot
 
-  const int64_t nchunks = (T + TC - 1) / TC;
-  for (int64_t ch = 0; ch < nchunks; ++ch) {
-    const int64_t t0 = ch * TC;
-    const int tn = (int)((T - t0) < TC ? (T - t0) : TC);
-    const int sb = (int)(ch & 1);
-    const bool more = ch + 1 < nchunks;
-    if (more) load_chunk(t0 + TC);
+  // One recurrence step.  si is the circular staging slot (0 .. 2 TC - 1) of
+  // step t; the staging arrays are [2][TC] = [2 TC] consecutive slots.
+  auto step = [&](int64_t t, int si) {
+    const int si1 = si + 1 == 2 * TC ? 0 : si + 1;   // slot of step t + 1
+    const Real* kq1 = &sm.kq[0][0][0][0] + si1 * 32;
+    const Real* v1 = &sm.v[0][0][0] + si1 * VP;
 
-    for (int tt = 0; tt < tn; ++tt) {
-      const int64_t t = t0 + tt;
-      const Real kv = sm.kq[sb][tt][li][0];
-      const Real qv = sm.kq[sb][tt][li][1];
-      const Real ft = sm.f[sb][tt];
-      R4 acc[TPW];
+    R4 acc[TPW];
 #pragma unroll
-      for (int p = 0; p < TPW; ++p) {
+    for (int p = 0; p < TPW; ++p) acc[p] = acc_init[p];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)  // rank-1 write k_i v_j
-          acc[p][r] = kv * sm.v[sb][tt][(w * TPW + p) * 16 + acc_m<Real>(g, r)];
-      }
+    for (int s0 = 0; s0 < NS; ++s0) {
 #pragma unroll
-      for (int s0 = 0; s0 < NS; ++s0) {
+      for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wa[p][s0], hb[s0], acc[p]);
+    }
+    // ---- work independent of the MFMA chain (scheduled into its shadow)
+    // readout of the previous step, y_{t-1} = H_t^T q_{t-1} over this slab's rows
 #pragma unroll
-        for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wa[p][s0], hb[s0], acc[p]);
-      }
-      // tanh and the gate interpolation H = f H_prev + (1 - f) Z, written as in
-      // Eq. (11) so that f = 1 keeps H exactly and f = 0 gives exactly Z
-      const Real omf = Real(1) - ft;
+    for (int p = 0; p < TPW; ++p) {
+      R4 yv;
 #pragma unroll
-      for (int p = 0; p < TPW; ++p) {
+      for (int r = 0; r < 4; ++r) yv[r] = row16_sum(hown[p][r] * q_prev);
+      yslot[p * ystep] = yv;
+    }
+    // next step's inputs
+    const Real kv = kq1[li * 2 + 0];
+    const Real qn = kq1[li * 2 + 1];
+    const Real fn = (&sm.f[0][0])[si1];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const Real z = tanh_fast(acc[p][r]);
-          hown[p][r] = ft * hown[p][r] + omf * z;
-        }
-      }
-      const int xbuf = (int)(t & 1);
+    for (int p = 0; p < TPW; ++p)
 #pragma unroll
-      for (int p = 0; p < TPW; ++p) sm.xb[xbuf][w * TPW + p][lane] = hown[p];
-
-      // readout of the updated state: sum over the 16 rows of the slab
+      for (int r = 0; r < 4; ++r) acc_init[p][r] = kv * v1[(w * TPW + p) * 16 + acc_m<Real>(g, r)];
+    q_prev = q_cur;
+    q_cur = qn;
+    // interleave: one MFMA, then up to two VALU ops and one LDS read
 #pragma unroll
-      for (int p = 0; p < TPW; ++p) {
-        Real yv[4];
+    for (int s0 = 0; s0 < NS * TPW; ++s0) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    // ---- dependent tail: tanh, gate interpolation H = f H + (1 - f) Z
+    const Real ft = f_cur;
+    const Real omf = Real(1) - ft;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) yv[r] = row16_sum(hown[p][r] * qv);
-        if (li == 0) {
+    for (int p = 0; p < TPW; ++p) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sm.y[sb][tt][(w * TPW + p) * 16 + acc_m<Real>(g, r)] = yv[r];
-        }
-      }
-      if (a.ckpt && ((t + 1) % a.C) == 0 && (t + 1) < T) {
-        write_state((Real*)a.ckpt + ((((int64_t)b * N + n) * nck + (t + 1) / a.C) * K + row) * V);
-      }
-      if (more && tt == tn - 1) store_chunk(sb ^ 1);
-      __syncthreads();
-#pragma unroll
-      for (int q0 = TPW; q0 < VT; ++q0) {
-        const R4 t4 = sm.xb[xbuf][(q0 + TPW * w) % VT][lane];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hb[4 * q0 + r] = t4[r];
-      }
-#pragma unroll
-      for (int p = 0; p < TPW; ++p) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hb[4 * p + r] = hown[p][r];
+      for (int r = 0; r < 4; ++r) {
+        const Real z = tanh_fast(acc[p][r]);
+        hown[p][r] = ft * hown[p][r] + omf * z;
       }
     }
-
-    // write back this chunk's readouts (partial over the slab's rows)
+    f_cur = fn;
+    const int xbuf = (int)(t & 1);
 #pragma unroll
-    for (int m = 0; m < Tr::NY_PER; ++m) {
-      const int e = tid + m * NT;
-      const int tt = e / VP, j = e % VP;
-      if (tt < tn && j < V) {
-        const int64_t off = (((int64_t)b * T + t0 + tt) * N + n) * V + j;
-        const Real val = sm.y[sb][tt][j];
-        if (nslab == 1) {
-          yout[off] = val + sm.wr[j] * sm.v[sb][tt][j];
-        } else {
-          ypart[slab * slab_stride + off] = val;
-        }
+    for (int p = 0; p < TPW; ++p) sm.xb[xbuf][w * TPW + p][lane] = hown[p];
+    // the readout of this step lands in staging slot si
+    yslot = ybase + si * yslot_stride;
+    ystep = ystep_writer;
+    __syncthreads();
+#pragma unroll
+    for (int q0 = TPW; q0 < VT; ++q0) {
+      const R4 t4 = sm.xb[xbuf][(q0 + TPW * w) % VT][lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hb[4 * q0 + r] = t4[r];
+    }
+#pragma unroll
+    for (int p = 0; p < TPW; ++p)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hb[4 * p + r] = hown[p][r];
+  };
+
+  // Steps run in branch-free segments; the rare events (checkpoint, LDS
+  // staging of the next chunk, write-back of readouts, prefetch) happen only
+  // between segments.  Event points, as the last step of a segment:
+  //   local step 0 of chunk ch > 0 : chunk ch - 1 is complete -> write back
+  //   local step TC - 3            : stage chunk ch + 1 into LDS
+  //   local step TC - 1            : end of chunk -> prefetch chunk ch + 2
+  //   (t + 1) % C == 0             : checkpoint H_{t+1}
+  int64_t next_ck = a.ckpt ? a.C - 1 : T;  // step after which the next checkpoint is taken
+  int64_t ch = 0;
+  int64_t t = 0;
+  while (t < T) {
+    const int64_t t0 = ch * TC;
+    const int tt = (int)(t - t0);
+    int64_t e = t0 + TC - 1;
+    if (tt <= TC - 3) e = t0 + TC - 3;
+    if (tt == 0) e = t0;
+    if (next_ck < e) e = next_ck;
+    if (T - 1 < e) e = T - 1;
+    const int sb = (int)(ch & 1);
+    int si = sb * TC + tt;
+    for (; t <= e; ++t, ++si) step(t, si);
+    // ---- events after step e (uniform)
+    const int te = (int)(e - t0);
+    if (e == next_ck) {
+      if (e + 1 < T) {
+        write_state(ck_next);
+        ck_next += ck_stride;
       }
+      next_ck += a.C;
+    }
+    if (te == 0 && ch > 0) flush(ch - 1, sb ^ 1);
+    if (te == TC - 3 && ch + 1 < nchunks) store_chunk(sb ^ 1);
+    if (te == TC - 1) {
+      if (ch + 2 < nchunks) load_chunk((ch + 2) * TC);
+      ++ch;
     }
   }
+  // readout of the last step, then the last chunk
+#pragma unroll
+  for (int p = 0; p < TPW; ++p) {
+    R4 yv;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) yv[r] = row16_sum(hown[p][r] * q_prev);
+    yslot[p * ystep] = yv;
+  }
+  __syncthreads();
+  flush(nchunks - 1, (int)((nchunks - 1) & 1));
   if (a.HT) write_state((Real*)a.HT + state_base);
 }
 
@@ -296,7 +384,7 @@ __global__ void __launch_bounds__(256)
 template <typename InT, typename Real, int VT>
 static hipError_t launch_fwd_vt(const FwdArgs& a, hipStream_t stream) {
   using Tr = FwdTraits<Real, VT>;
-  static_assert(sizeof(FwdSmem<Real, VT, Tr::TC>) <= 65536, "LDS budget");
+  static_assert(sizeof(FwdSmem<Real, VT, Tr::TC, Tr::NT>) <= 160 * 1024, "LDS budget");
   const int64_t units = a.B * a.N * a.nslab;
   hipLaunchKernelGGL((m2rnn_fwd_kernel<InT, Real, VT>), dim3((unsigned)units), dim3(Tr::NT), 0,
                      stream, a);
