@@ -17,7 +17,7 @@ SOURCES = ["m2rnn_api.hip", "m2rnn_gates.hip", "m2rnn_fwd.hip", "m2rnn_bwd.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are switched off for every kernel.
-HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+HIP_FLAGS = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-fno-gpu-rdc", "-Wall", "-Wno-unused-function"]
 

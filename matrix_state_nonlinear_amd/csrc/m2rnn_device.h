@@ -12,6 +12,19 @@ namespace m2rnn {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+
+template <typename Real>
+struct Vec2;
+template <>
+struct Vec2<float> {
+  using type = f32x2;
+};
+template <>
+struct Vec2<double> {
+  using type = f64x2;
+};
 
 template <typename Real>
 struct Vec4;
@@ -61,6 +74,18 @@ __device__ __forceinline__ float tanh_fast(float x) {
   return __builtin_copysignf(t, x);
 }
 __device__ __forceinline__ double tanh_fast(double x) { return ::tanh(x); }
+
+// 1 / (1 + e^{2x}), so that tanh(x) = 1 - 2 / (1 + e^{2x}).  For large |x| the
+// exponential saturates to inf or 0 and the result to 0 or 1, so the identity
+// still gives +-1.  fp32: hardware base-2 exponential and reciprocal.
+__device__ __forceinline__ float sigmoid_neg2x(float x) {
+  const float two_log2e = 2.885390081777926814f;  // 2 / ln 2
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(two_log2e * x));
+}
+__device__ __forceinline__ double sigmoid_neg2x(double x) { return 1.0 / (1.0 + ::exp(2.0 * x)); }
+
+__device__ __forceinline__ float fma_r(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+__device__ __forceinline__ double fma_r(double a, double b, double c) { return __builtin_fma(a, b, c); }
 
 // DPP: read the value of another lane of the same 16-lane row.
 template <int CTRL>

@@ -11,24 +11,29 @@
 // rows becomes ceil(K / 16) workgroups on different compute units, and their
 // partial readouts are summed by a second, elementwise kernel.
 //
-// Inside a workgroup each wave owns TPW 16-column tiles of the slab.  The step
-// is computed transposed, (H W)^T = W^T H^T, on the 16x16x4 MFMA: W^T is the
-// A operand (held in registers for the whole sequence), H^T the B operand.
-// The MFMA result layout (lane l holds row l % 16 and, in element r, column
-// 16 c + m(g, r) with g = l / 16 and m the instruction's accumulator row map)
-// is then exactly the B-operand layout of the next step, provided the
-// contraction index of MFMA number s is enumerated as
-// pi(s, g) = 16 (s / 4) + m(g, s % 4).  So the state never leaves registers:
-// its own tiles stay in the accumulators and the other waves' tiles arrive
-// through one 16-byte LDS write and (VT / TPW - 1) 16-byte LDS reads per lane
-// per step, with no shuffles or transposes.
+// MFMA formulation.  The step is computed transposed, (H W)^T = W^T H^T, on
+// the 16x16x4 MFMA: W^T is the A operand (held in registers for the whole
+// sequence), H^T the B operand.  The MFMA result layout (lane l holds row
+// l % 16 and, in element r, column 16 c + m(g, r) with g = l / 16 and m the
+// instruction's accumulator row map) is exactly the B-operand layout of the
+// next step when the contraction index of MFMA number s is enumerated as
+// pi(s, g) = 16 (s / 4) + m(g, s % 4).  So a wave's own 16-column tiles never
+// leave registers, and the other tiles of the slab arrive through one 16-byte
+// LDS write and (VT / TPW - 1) 16-byte LDS reads per lane per step.  The
+// rank-1 write k v^T is one more MFMA whose contraction has a single non-zero
+// slice (A = v in lane group 0, zero elsewhere; B = k).
 //
-// Per step: rank-1 term k_i v_j as the accumulator's initial value, 4 * VT
-// MFMAs per tile, tanh, the f-lerp, an LDS exchange with one barrier, and the
-// readout y_j = sum_i H_ij q_i as a DPP reduction over the 16 lanes of a row.
-// k, q, v, f are staged through LDS in chunks of TC steps (coalesced global
-// loads issued one chunk ahead); readouts are staged per chunk and written
-// back coalesced.
+// Step schedule.  On gfx950 a wave issues nothing else while its MFMA chain
+// runs, so every VALU instruction of a step adds to the step time.  The step
+// is therefore: MFMAs (own tiles first: no LDS wait), tanh and the gate
+// interpolation, the exchange write, then the readout y_t = H_t^T q_t as a DPP
+// reduction over the 16 rows -- placed where the wave would otherwise wait for
+// its exchange write to land -- then the barrier and the exchange reads.
+// Inputs come from an LDS staging ring laid out so that each step needs only
+// immediate-offset reads; each staging chunk of TC steps is unrolled, and all
+// global traffic (prefetch, write-back, checkpoints) happens between chunks.
+
+#include <type_traits>
 
 #include "m2rnn_device.h"
 #include "m2rnn_internal.h"
@@ -41,24 +46,24 @@ struct FwdTraits {
   static constexpr int NW = VT <= 4 ? VT : VT / 2;   // waves per workgroup
   static constexpr int TPW = VT / NW;                // 16-column tiles per wave
   static constexpr int NT = 64 * NW;                 // threads per workgroup
-  static constexpr int NS = 4 * VT;                  // MFMAs per tile per step
-  static constexpr int TC = sizeof(Real) == 4 ? (VP <= 64 ? 32 : 16)
-                                              : (VP <= 32 ? 32 : (VP <= 64 ? 16 : 8));
-  static constexpr int NV_PER = (TC * VP + NT - 1) / NT;   // staged v values per thread
-  static constexpr int NKQ_PER = (TC * 32 + NT - 1) / NT;  // staged k and q values per thread
-  static_assert(TC >= 4, "a staging chunk must hold at least 4 steps");
+  static constexpr int NS = 4 * VT;                  // MFMAs per tile per step (H W)
+  static constexpr int TC = sizeof(Real) == 4 ? 16 : 8;   // steps per staging chunk (unrolled)
+  static constexpr int RING = 2 * TC;                     // staging ring: two chunks
+  // per chunk: v and k as rank-1 operands [TC][VT][16], q [TC][16], f [TC]
+  static constexpr int NR1_PER = (TC * VT * 16 + NT - 1) / NT;   // (v, k) pairs per thread
+  static constexpr int NQ_PER = (TC * 16 + NT - 1) / NT;
 };
 
-template <typename Real, int VT, int TC, int NT>
+template <typename Real, int VT, int NW, int RING>
 struct FwdSmem {
   using R4 = typename Vec4<Real>::type;
+  using R2 = typename Vec2<Real>::type;
   R4 xb[2][VT][64];           // state exchange, double-buffered by step parity
-  R4 y[2][TC][4 * VT];        // partial readouts, lane order (16 c + 4 g + r), per chunk
-  R4 ydump[NT];               // sink for the readout writes of lanes that hold no result
-  Real kq[2][TC][16][2];      // staged (k_i, q_i) per step
-  Real v[2][TC][16 * VT];     // staged v per step
-  Real f[2][TC];              // staged gate
-  Real wr[16 * VT];           // w_r of this head
+  R4 y[RING][VT][4];          // readouts (this slab's rows), lane order [tile][g][r]
+  R4 ydump[NW * 64];          // sink for readout stores of lanes that hold no result
+  R2 r1[RING][VT][16];        // rank-1 operands of a step: (v_{16 c + i}, k_i)
+  R2 fg[RING];                // (f, 1 - f) of a step
+  Real q[RING][16];           // q_i of a step
 };
 
 template <typename InT, typename Real, int VT>
@@ -66,8 +71,10 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
     m2rnn_fwd_kernel(FwdArgs a) {
   using Tr = FwdTraits<Real, VT>;
   using R4 = typename Vec4<Real>::type;
+  using R2 = typename Vec2<Real>::type;
   constexpr int VP = Tr::VP, TPW = Tr::TPW, NS = Tr::NS, TC = Tr::TC, NT = Tr::NT;
-  __shared__ FwdSmem<Real, VT, TC, NT> sm;
+  constexpr int RING = Tr::RING;
+  __shared__ FwdSmem<Real, VT, Tr::NW, RING> sm;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, g = lane >> 4, li = lane & 15;
@@ -80,6 +87,7 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
   const int b = (int)(bn / N);
   const int row = slab * 16 + li;
   const bool row_ok = row < K;
+  const int64_t state_base = (((int64_t)b * N + n) * K + row) * V;
 
   const InT* __restrict__ kp = (const InT*)a.k;
   const InT* __restrict__ vp = (const InT*)a.v;
@@ -87,6 +95,10 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
   const Real* __restrict__ fp = (const Real*)a.f;
   const Real* __restrict__ Wp = (const Real*)a.W;
   const Real* __restrict__ wrp = (const Real*)a.w_r;
+  Real* __restrict__ yout = (Real*)a.y;
+  Real* __restrict__ ypart = (Real*)a.ypart;
+  const int64_t slab_stride = B * T * N * V;
+  auto col_of = [&](int p, int r) { return (w * TPW + p) * 16 + acc_m<Real>(g, r); };
 
   // ---- W^T as the MFMA A operand, rotated so this wave's own tiles come first.
   Real wa[TPW][NS];
@@ -103,95 +115,85 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
 
   // ---- initial state: own tiles hold row `row`, columns 16 c + m(g, r).
   R4 hown[TPW];
-  const int64_t state_base = (((int64_t)b * N + n) * K + row) * V;
 #pragma unroll
-  for (int p = 0; p < TPW; ++p) {
+  for (int p = 0; p < TPW; ++p)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int col = (w * TPW + p) * 16 + acc_m<Real>(g, r);
+      const int col = col_of(p, r);
       hown[p][r] = (a.H0 && row_ok && col < V) ? ((const Real*)a.H0)[state_base + col] : Real(0);
     }
-  }
   const int64_t nck = a.ckpt ? (T + a.C - 1) / a.C : 0;
   auto write_state = [&](Real* dst) {
+    if (!row_ok) return;
 #pragma unroll
-    for (int p = 0; p < TPW; ++p) {
+    for (int p = 0; p < TPW; ++p)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int col = (w * TPW + p) * 16 + acc_m<Real>(g, r);
-        if (row_ok && col < V) dst[col] = hown[p][r];
+        const int col = col_of(p, r);
+        if (col < V) dst[col] = hown[p][r];
       }
-    }
   };
-  Real* ck_next = nullptr;   // where the next checkpoint goes
-  if (a.ckpt) {
-    Real* ck0 = (Real*)a.ckpt + ((((int64_t)b * N + n) * nck) * K + row) * V;
-    write_state(ck0);
-    ck_next = ck0 + K * V;
-  }
-  const int64_t ck_stride = K * V;
+  Real* const ck0 = a.ckpt ? (Real*)a.ckpt + (((int64_t)b * N + n) * nck * K + row) * V : nullptr;
+  if (a.ckpt) write_state(ck0);
 
-  // ---- staging of k, q, v, f for one chunk of TC steps.
-  Real st_v[Tr::NV_PER], st_kq[Tr::NKQ_PER], st_f = Real(0);
-  // Every load is issued unconditionally from a clamped (in-bounds) address and
-  // masked afterwards, so the loads of a chunk are all in flight at once.
-  auto load_chunk = [&](int64_t t0) {
+  // ---- staging of one chunk of TC steps: unconditional loads from clamped
+  // addresses, masked afterwards, so all of a chunk's loads are in flight at once.
+  R2 st_r1[Tr::NR1_PER];
+  Real st_q[Tr::NQ_PER], st_f;
+  auto load_chunk = [&](int64_t ch) {
+    const int64_t t0 = ch * TC;
 #pragma unroll
-    for (int m = 0; m < Tr::NV_PER; ++m) {
-      const int e = tid + m * NT;
-      const int tt = e / VP, j = e % VP;
+    for (int m = 0; m < Tr::NR1_PER; ++m) {
+      const int e = tid + m * NT;                      // [tt][c][i]
+      const int tt = e / VP, c = (e / 16) % VT, i = e % 16;
       const int64_t t = t0 + tt;
-      const bool ok = tt < TC && j < V && t < T;
-      const int64_t tc = clamp_idx(t, T - 1);
-      st_v[m] = load_sel<Real>(vp, (((int64_t)b * T + tc) * N + n) * V + clamp_idx(j, V - 1), ok);
+      const int64_t tok = ((int64_t)b * T + clamp_idx(t, T - 1)) * N + n;
+      const int j = c * 16 + i, rr = slab * 16 + i;
+      const bool tok_ok = tt < TC && t < T;
+      st_r1[m][0] = load_sel<Real>(vp, tok * V + clamp_idx(j, V - 1), tok_ok && j < V);
+      st_r1[m][1] = load_sel<Real>(kp, tok * K + clamp_idx(rr, K - 1), tok_ok && rr < K);
     }
 #pragma unroll
-    for (int m = 0; m < Tr::NKQ_PER; ++m) {
-      const int e = tid + m * NT;
-      const int tt = e >> 5, which = (e >> 4) & 1, i = e & 15;
+    for (int m = 0; m < Tr::NQ_PER; ++m) {
+      const int e = tid + m * NT;                      // [tt][i]
+      const int tt = e / 16, i = e % 16;
       const int64_t t = t0 + tt;
+      const int64_t tok = ((int64_t)b * T + clamp_idx(t, T - 1)) * N + n;
       const int rr = slab * 16 + i;
-      const bool ok = tt < TC && rr < K && t < T;
-      const int64_t tc = clamp_idx(t, T - 1);
-      const InT* src = which ? qp : kp;
-      st_kq[m] = load_sel<Real>(src, (((int64_t)b * T + tc) * N + n) * K + clamp_idx(rr, K - 1), ok);
+      st_q[m] = load_sel<Real>(qp, tok * K + clamp_idx(rr, K - 1), tt < TC && t < T && rr < K);
     }
     {
       const int64_t t = t0 + tid;
-      const bool ok = tid < TC && t < T;
-      st_f = load_sel<Real>(fp, ((int64_t)b * T + clamp_idx(t, T - 1)) * N + n, ok);
+      st_f = load_sel<Real>(fp, ((int64_t)b * T + clamp_idx(t, T - 1)) * N + n, tid < TC && t < T);
     }
   };
-  auto store_chunk = [&](int buf) {
+  auto store_chunk = [&](int64_t ch) {
+    const int base = (int)(ch & 1) * TC;
 #pragma unroll
-    for (int m = 0; m < Tr::NV_PER; ++m) {
+    for (int m = 0; m < Tr::NR1_PER; ++m) {
       const int e = tid + m * NT;
-      if (e < TC * VP) sm.v[buf][e / VP][e % VP] = st_v[m];
+      if (e < TC * VP) sm.r1[base + e / VP][(e / 16) % VT][e % 16] = st_r1[m];
     }
 #pragma unroll
-    for (int m = 0; m < Tr::NKQ_PER; ++m) {
+    for (int m = 0; m < Tr::NQ_PER; ++m) {
       const int e = tid + m * NT;
-      if (e < TC * 32) sm.kq[buf][e >> 5][e & 15][(e >> 4) & 1] = st_kq[m];
+      if (e < TC * 16) sm.q[base + e / 16][e % 16] = st_q[m];
     }
-    if (tid < TC) sm.f[buf][tid] = st_f;
+    if (tid < TC) sm.fg[base + tid] = R2{st_f, Real(1) - st_f};
   };
-
-  Real* __restrict__ yout = (Real*)a.y;
-  Real* __restrict__ ypart = (Real*)a.ypart;
-  const int64_t slab_stride = B * T * N * V;
-  // write back one chunk of partial readouts (the y staging is in lane order)
-  auto flush = [&](int64_t ch, int buf) {
+  // write back one chunk of readouts (staged in lane order)
+  auto flush = [&](int64_t ch) {
     const int64_t t0 = ch * TC;
-    const int tn = (int)((T - t0) < TC ? (T - t0) : TC);
+    const int base = (int)(ch & 1) * TC;
     for (int e = tid; e < TC * VP; e += NT) {
       const int tt = e / VP, jl = e % VP;
       const int c = jl >> 4, gg = (jl >> 2) & 3, rr = jl & 3;
       const int j = c * 16 + acc_m<Real>(gg, rr);
-      if (tt < tn && j < V) {
+      if (t0 + tt < T && j < V) {
         const int64_t off = (((int64_t)b * T + t0 + tt) * N + n) * V + j;
-        const Real val = sm.y[buf][tt][jl >> 2][rr];
+        const Real val = sm.y[base + tt][c][gg][rr];
         if (nslab == 1) {
-          yout[off] = val + sm.wr[j] * sm.v[buf][tt][j];
+          yout[off] = val + wrp[(int64_t)n * V + j] * sm.r1[base + tt][c][acc_m<Real>(gg, rr)][0];
         } else {
           ypart[slab * slab_stride + off] = val;
         }
@@ -200,10 +202,9 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
   };
 
   const int64_t nchunks = (T + TC - 1) / TC;
-  for (int j = tid; j < VP; j += NT) sm.wr[j] = j < V ? wrp[(int64_t)n * V + j] : Real(0);
   load_chunk(0);
   store_chunk(0);
-  if (nchunks > 1) load_chunk(TC);
+  if (nchunks > 1) load_chunk(1);
 
   // ---- first exchange: the full slab of H_0 as the B operand.
   Real hb[NS];
@@ -217,95 +218,64 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
     for (int r = 0; r < 4; ++r) hb[4 * q0 + r] = t4[r];
   }
 
-  // ---- inputs of step 0
-  R4 acc_init[TPW];
-  Real q_cur, f_cur;
-  {
-    const Real kv = sm.kq[0][0][li][0];
-    q_cur = sm.kq[0][0][li][1];
-    f_cur = sm.f[0][0];
-#pragma unroll
-    for (int p = 0; p < TPW; ++p)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        acc_init[p][r] = kv * sm.v[0][0][(w * TPW + p) * 16 + acc_m<Real>(g, r)];
-  }
-  Real q_prev = Real(0);
-  // Readout destination of the previous step.  Lane 0 of each 16-lane group
-  // holds the row sums and writes them (tile p at yslot + 4 p); every other
-  // lane writes its own slot of ydump, so the store needs no branch.  Step 0
-  // has no previous step: everyone writes ydump.
+  // Per-lane LDS base addresses.  Within a chunk every step's address is this
+  // base plus a compile-time offset.  A-operand of the rank-1 MFMA: v in lane
+  // group 0, zero elsewhere (the mask is applied when read).
+  const Real a_mask = g == 0 ? Real(1) : Real(0);
   R4* const ydump_me = &sm.ydump[tid];
-  R4* yslot = ydump_me;
-  const int ystep_writer = li == 0 ? 4 : 0;
-  int ystep = 0;
-  // y staging address of this lane for circular slot 0 (writers only)
-  R4* const ybase = li == 0 ? &sm.y[0][0][(w * TPW) * 4 + g] : ydump_me;
-  const int yslot_stride = li == 0 ? 4 * VT : 0;  // R4 elements per staging slot
 
-  // One recurrence step.  si is the circular staging slot (0 .. 2 TC - 1) of
-  // step t; the staging arrays are [2][TC] = [2 TC] consecutive slots.
-  auto step = [&](int64_t t, int si) {
-    const int si1 = si + 1 == 2 * TC ? 0 : si + 1;   // slot of step t + 1
-    const Real* kq1 = &sm.kq[0][0][0][0] + si1 * 32;
-    const Real* v1 = &sm.v[0][0][0] + si1 * VP;
-
+  // One step at ring slot SI (compile-time within the chunk); P = parity.
+  auto step = [&](auto si_c, int base) {
+    constexpr int SI = decltype(si_c)::value;   // slot within the chunk, 0 .. TC - 1
+    constexpr int P = SI & 1;
+    const int slot = base + SI;
     R4 acc[TPW];
 #pragma unroll
-    for (int p = 0; p < TPW; ++p) acc[p] = acc_init[p];
+    for (int p = 0; p < TPW; ++p) acc[p] = R4{0, 0, 0, 0};
 #pragma unroll
-    for (int s0 = 0; s0 < NS; ++s0) {
+    for (int s0 = 0; s0 < 4 * TPW; ++s0) {
 #pragma unroll
       for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wa[p][s0], hb[s0], acc[p]);
     }
-    // ---- work independent of the MFMA chain (scheduled into its shadow)
-    // readout of the previous step, y_{t-1} = H_t^T q_{t-1} over this slab's rows
 #pragma unroll
     for (int p = 0; p < TPW; ++p) {
-      R4 yv;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) yv[r] = row16_sum(hown[p][r] * q_prev);
-      yslot[p * ystep] = yv;
+      const R2 vk = sm.r1[slot][w * TPW + p][li];
+      acc[p] = mfma_16x16x4(vk[0] * a_mask, vk[1], acc[p]);
     }
-    // next step's inputs
-    const Real kv = kq1[li * 2 + 0];
-    const Real qn = kq1[li * 2 + 1];
-    const Real fn = (&sm.f[0][0])[si1];
 #pragma unroll
-    for (int p = 0; p < TPW; ++p)
+    for (int s0 = 4 * TPW; s0 < NS; ++s0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc_init[p][r] = kv * v1[(w * TPW + p) * 16 + acc_m<Real>(g, r)];
-    q_prev = q_cur;
-    q_cur = qn;
-    // interleave: one MFMA, then up to two VALU ops and one LDS read
-#pragma unroll
-    for (int s0 = 0; s0 < NS * TPW; ++s0) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wa[p][s0], hb[s0], acc[p]);
     }
-    // ---- dependent tail: tanh, gate interpolation H = f H + (1 - f) Z
-    const Real ft = f_cur;
-    const Real omf = Real(1) - ft;
+    // H = f H + (1 - f) tanh(A), with tanh(A) = 1 - 2 / (1 + e^{2A}):
+    // H = (f H + (1 - f)) - 2 (1 - f) / (1 + e^{2A}).  f = 1 gives H exactly.
+    const R2 fg = sm.fg[slot];
+    const Real m2omf = Real(-2) * fg[1];
 #pragma unroll
     for (int p = 0; p < TPW; ++p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const Real z = tanh_fast(acc[p][r]);
-        hown[p][r] = ft * hown[p][r] + omf * z;
+        const Real rc = sigmoid_neg2x(acc[p][r]);
+        hown[p][r] = fma_r(m2omf, rc, fma_r(fg[0], hown[p][r], fg[1]));
       }
+      sm.xb[P][w * TPW + p][lane] = hown[p];
     }
-    f_cur = fn;
-    const int xbuf = (int)(t & 1);
+    // readout y_t = H_t^T q_t over this slab's rows, while the write lands
+    const Real qv = sm.q[slot][li];
+    R4 ys[TPW];
 #pragma unroll
-    for (int p = 0; p < TPW; ++p) sm.xb[xbuf][w * TPW + p][lane] = hown[p];
-    // the readout of this step lands in staging slot si
-    yslot = ybase + si * yslot_stride;
-    ystep = ystep_writer;
+    for (int p = 0; p < TPW; ++p)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ys[p][r] = row16_sum(hown[p][r] * qv);
+#pragma unroll
+    for (int p = 0; p < TPW; ++p) {
+      R4* dst = li == 0 ? &sm.y[slot][w * TPW + p][g] : ydump_me;
+      *dst = ys[p];
+    }
     __syncthreads();
 #pragma unroll
     for (int q0 = TPW; q0 < VT; ++q0) {
-      const R4 t4 = sm.xb[xbuf][(q0 + TPW * w) % VT][lane];
+      const R4 t4 = sm.xb[P][(q0 + TPW * w) % VT][lane];
 #pragma unroll
       for (int r = 0; r < 4; ++r) hb[4 * q0 + r] = t4[r];
     }
@@ -314,54 +284,46 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
 #pragma unroll
       for (int r = 0; r < 4; ++r) hb[4 * p + r] = hown[p][r];
   };
+  // A whole chunk, unrolled; `store_next` stages chunk ch + 1 after step TC - 2
+  // (the barrier of step TC - 1 then makes it visible before chunk ch + 1).
+  auto full_chunk = [&](int base, bool store_next, int64_t ch) {
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      ((step(std::integral_constant<int, I>{}, base),
+        (I == TC - 2 && store_next ? store_chunk(ch + 1) : void())),
+       ...);
+    }(std::make_integer_sequence<int, TC>{});
+  };
 
-  // Steps run in branch-free segments; the rare events (checkpoint, LDS
-  // staging of the next chunk, write-back of readouts, prefetch) happen only
-  // between segments.  Event points, as the last step of a segment:
-  //   local step 0 of chunk ch > 0 : chunk ch - 1 is complete -> write back
-  //   local step TC - 3            : stage chunk ch + 1 into LDS
-  //   local step TC - 1            : end of chunk -> prefetch chunk ch + 2
-  //   (t + 1) % C == 0             : checkpoint H_{t+1}
-  int64_t next_ck = a.ckpt ? a.C - 1 : T;  // step after which the next checkpoint is taken
+  // Checkpoints need a chunk boundary at every multiple of C; with C a
+  // multiple of TC they all fall between chunks.
+  const bool ck_at_chunks = !a.ckpt || (a.C % TC) == 0;
   int64_t ch = 0;
-  int64_t t = 0;
-  while (t < T) {
+  for (; ch < nchunks; ++ch) {
     const int64_t t0 = ch * TC;
-    const int tt = (int)(t - t0);
-    int64_t e = t0 + TC - 1;
-    if (tt <= TC - 3) e = t0 + TC - 3;
-    if (tt == 0) e = t0;
-    if (next_ck < e) e = next_ck;
-    if (T - 1 < e) e = T - 1;
-    const int sb = (int)(ch & 1);
-    int si = sb * TC + tt;
-    for (; t <= e; ++t, ++si) step(t, si);
-    // ---- events after step e (uniform)
-    const int te = (int)(e - t0);
-    if (e == next_ck) {
-      if (e + 1 < T) {
-        write_state(ck_next);
-        ck_next += ck_stride;
+    const int base = (int)(ch & 1) * TC;
+    const bool last = ch + 1 == nchunks;
+    if (!last && ck_at_chunks) {
+      full_chunk(base, true, ch);
+    } else {
+      // generic path: the partial last chunk, or checkpoints inside chunks
+      const int tn = (int)((T - t0) < TC ? (T - t0) : TC);
+      for (int tt = 0; tt < tn; ++tt) {
+        // dispatch the compile-time slot (the generic path is rare)
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+          ((tt == I ? step(std::integral_constant<int, I>{}, base) : void()), ...);
+        }(std::make_integer_sequence<int, TC>{});
+        if (tt == TC - 2 && !last) store_chunk(ch + 1);
+        const int64_t t = t0 + tt;
+        if (a.ckpt && !ck_at_chunks && (t + 1) % a.C == 0 && t + 1 < T)
+          write_state(ck0 + ((t + 1) / a.C) * K * V);
       }
-      next_ck += a.C;
     }
-    if (te == 0 && ch > 0) flush(ch - 1, sb ^ 1);
-    if (te == TC - 3 && ch + 1 < nchunks) store_chunk(sb ^ 1);
-    if (te == TC - 1) {
-      if (ch + 2 < nchunks) load_chunk((ch + 2) * TC);
-      ++ch;
-    }
+    // ---- between chunks: checkpoint, write-back of this chunk, prefetch
+    const int64_t tend = t0 + TC;   // steps done after this chunk (if not last)
+    if (!last && a.ckpt && ck_at_chunks && tend % a.C == 0) write_state(ck0 + (tend / a.C) * K * V);
+    flush(ch);                                   // readouts of chunk ch are complete
+    if (ch + 2 < nchunks) load_chunk(ch + 2);    // into registers; stored during chunk ch + 1
   }
-  // readout of the last step, then the last chunk
-#pragma unroll
-  for (int p = 0; p < TPW; ++p) {
-    R4 yv;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) yv[r] = row16_sum(hown[p][r] * q_prev);
-    yslot[p * ystep] = yv;
-  }
-  __syncthreads();
-  flush(nchunks - 1, (int)((nchunks - 1) & 1));
   if (a.HT) write_state((Real*)a.HT + state_base);
 }
 
@@ -384,7 +346,7 @@ __global__ void __launch_bounds__(256)
 template <typename InT, typename Real, int VT>
 static hipError_t launch_fwd_vt(const FwdArgs& a, hipStream_t stream) {
   using Tr = FwdTraits<Real, VT>;
-  static_assert(sizeof(FwdSmem<Real, VT, Tr::TC, Tr::NT>) <= 160 * 1024, "LDS budget");
+  static_assert(sizeof(FwdSmem<Real, VT, Tr::NW, Tr::RING>) <= 160 * 1024, "LDS budget");
   const int64_t units = a.B * a.N * a.nslab;
   hipLaunchKernelGGL((m2rnn_fwd_kernel<InT, Real, VT>), dim3((unsigned)units), dim3(Tr::NT), 0,
                      stream, a);
