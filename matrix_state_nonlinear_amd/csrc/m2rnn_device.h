@@ -84,6 +84,16 @@ __device__ __forceinline__ float sigmoid_neg2x(float x) {
 }
 __device__ __forceinline__ double sigmoid_neg2x(double x) { return 1.0 / (1.0 + ::exp(2.0 * x)); }
 
+// Forces `x` to be computed at this point of the program (an empty volatile
+// asm that reads and writes it cannot move across other volatile operations
+// such as a barrier), without emitting any instruction.
+__device__ __forceinline__ void pin_value(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin_value(double& x) { asm volatile("" : "+v"(x)); }
+template <typename Real>
+__device__ __forceinline__ void pin_values(Real& a, Real& b, Real& c, Real& d) {
+  asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
 __device__ __forceinline__ float fma_r(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
 __device__ __forceinline__ double fma_r(double a, double b, double c) { return __builtin_fma(a, b, c); }
 
@@ -115,6 +125,45 @@ __device__ __forceinline__ Real row16_sum(Real x) {
   x += dpp_move<kDppRowRor2>(x);
   x += dpp_move<kDppRowRor1>(x);
   return x;
+}
+
+// Four independent 16-lane row sums of h[r] * q, computed level by level
+// (row_ror by 8, 4, 2, 1) so that each DPP reads a value written three
+// instructions earlier (the DPP read-after-VALU-write hazard needs two).
+// Lane 16 k of each row holds the row's sums, in a fixed association order.
+// The volatile asm also keeps the reduction where it is placed in the step.
+__device__ __forceinline__ f32x4 row16_sum_x4(f32x4 h, float q) {
+  float y0, y1, y2, y3;
+  asm volatile(
+      "v_mul_f32 %0, %4, %8\n"
+      "v_mul_f32 %1, %5, %8\n"
+      "v_mul_f32 %2, %6, %8\n"
+      "v_mul_f32 %3, %7, %8\n"
+      "v_add_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %1, %1, %1 row_ror:8 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %2, %2, %2 row_ror:8 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %3, %3, %3 row_ror:8 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %1, %1, %1 row_ror:4 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %2, %2, %2 row_ror:4 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %3, %3, %3 row_ror:4 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %0, %0, %0 row_ror:2 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %1, %1, %1 row_ror:2 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %2, %2, %2 row_ror:2 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %3, %3, %3 row_ror:2 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %0, %0, %0 row_ror:1 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %1, %1, %1 row_ror:1 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %2, %2, %2 row_ror:1 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %3, %3, %3 row_ror:1 row_mask:0xf bank_mask:0xf\n"
+      : "=&v"(y0), "=&v"(y1), "=&v"(y2), "=&v"(y3)
+      : "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "v"(q));
+  return f32x4{y0, y1, y2, y3};
+}
+__device__ __forceinline__ f64x4 row16_sum_x4(f64x4 h, double q) {
+  f64x4 y;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) y[r] = row16_sum(h[r] * q);
+  return y;
 }
 
 // Sum over the four 16-lane rows (lanes l, l^16, l^32, l^48), via ds_swizzle-free

@@ -136,35 +136,61 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
   Real* const ck0 = a.ckpt ? (Real*)a.ckpt + (((int64_t)b * N + n) * nck * K + row) * V : nullptr;
   if (a.ckpt) write_state(ck0);
 
-  // ---- staging of one chunk of TC steps: unconditional loads from clamped
-  // addresses, masked afterwards, so all of a chunk's loads are in flight at once.
+  // ---- staging of one chunk of TC steps.  Each thread owns a fixed set of
+  // (step-in-chunk, index) elements, so its global addresses for chunk ch are
+  // fixed offsets plus ch * TC * (elements per step); they are computed once.
+  // Loads are unconditional (a chunk's loads are all in flight at once); in
+  // the last chunk the step index is clamped to T - 1 and the value masked.
+  const int64_t NV = N * V, NK = N * K;
+  const int64_t tok0 = (int64_t)b * T * N + n;       // token index of (b, t = 0, n)
+  int64_t r1_vofs[Tr::NR1_PER], r1_kofs[Tr::NR1_PER], q_ofs[Tr::NQ_PER];
+  int r1_tt[Tr::NR1_PER], q_tt[Tr::NQ_PER];
+  bool r1_vok[Tr::NR1_PER], r1_kok[Tr::NR1_PER], q_ok[Tr::NQ_PER];
+#pragma unroll
+  for (int m = 0; m < Tr::NR1_PER; ++m) {
+    const int e = tid + m * NT;                      // [tt][c][i]
+    const int tt = e / VP, c = (e / 16) % VT, i = e % 16;
+    const int j = c * 16 + i, rr = slab * 16 + i;
+    r1_tt[m] = tt < TC ? tt : TC;                    // TC marks a padding element
+    r1_vok[m] = tt < TC && j < V;
+    r1_kok[m] = tt < TC && rr < K;
+    r1_vofs[m] = tok0 * V + (j < V ? j : V - 1);
+    r1_kofs[m] = tok0 * K + (rr < K ? rr : K - 1);
+  }
+#pragma unroll
+  for (int m = 0; m < Tr::NQ_PER; ++m) {
+    const int e = tid + m * NT;                      // [tt][i]
+    const int tt = e / 16, i = e % 16, rr = slab * 16 + i;
+    q_tt[m] = tt < TC ? tt : TC;
+    q_ok[m] = tt < TC && rr < K;
+    q_ofs[m] = tok0 * K + (rr < K ? rr : K - 1);
+  }
   R2 st_r1[Tr::NR1_PER];
   Real st_q[Tr::NQ_PER], st_f;
   auto load_chunk = [&](int64_t ch) {
     const int64_t t0 = ch * TC;
+    const bool full = t0 + TC <= T;
+    auto tok = [&](int tt) {   // token offset (in tokens) of step t0 + tt, clamped
+      const int64_t t = t0 + (tt < TC ? tt : 0);
+      return full ? t : (t < T ? t : T - 1);
+    };
 #pragma unroll
     for (int m = 0; m < Tr::NR1_PER; ++m) {
-      const int e = tid + m * NT;                      // [tt][c][i]
-      const int tt = e / VP, c = (e / 16) % VT, i = e % 16;
-      const int64_t t = t0 + tt;
-      const int64_t tok = ((int64_t)b * T + clamp_idx(t, T - 1)) * N + n;
-      const int j = c * 16 + i, rr = slab * 16 + i;
-      const bool tok_ok = tt < TC && t < T;
-      st_r1[m][0] = load_sel<Real>(vp, tok * V + clamp_idx(j, V - 1), tok_ok && j < V);
-      st_r1[m][1] = load_sel<Real>(kp, tok * K + clamp_idx(rr, K - 1), tok_ok && rr < K);
+      const int64_t t = tok(r1_tt[m]);
+      const bool in = full || t0 + r1_tt[m] < T;
+      st_r1[m][0] = load_sel<Real>(vp, r1_vofs[m] + t * NV, r1_vok[m] && in);
+      st_r1[m][1] = load_sel<Real>(kp, r1_kofs[m] + t * NK, r1_kok[m] && in);
     }
 #pragma unroll
     for (int m = 0; m < Tr::NQ_PER; ++m) {
-      const int e = tid + m * NT;                      // [tt][i]
-      const int tt = e / 16, i = e % 16;
-      const int64_t t = t0 + tt;
-      const int64_t tok = ((int64_t)b * T + clamp_idx(t, T - 1)) * N + n;
-      const int rr = slab * 16 + i;
-      st_q[m] = load_sel<Real>(qp, tok * K + clamp_idx(rr, K - 1), tt < TC && t < T && rr < K);
+      const int64_t t = tok(q_tt[m]);
+      const bool in = full || t0 + q_tt[m] < T;
+      st_q[m] = load_sel<Real>(qp, q_ofs[m] + t * NK, q_ok[m] && in);
     }
     {
-      const int64_t t = t0 + tid;
-      st_f = load_sel<Real>(fp, ((int64_t)b * T + clamp_idx(t, T - 1)) * N + n, tid < TC && t < T);
+      const int tt = tid < TC ? tid : 0;
+      const int64_t t = tok(tt);
+      st_f = load_sel<Real>(fp, (tok0 + t * N), tid < TC && (full || t0 + tt < T));
     }
   };
   auto store_chunk = [&](int64_t ch) {
@@ -181,21 +207,40 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
     }
     if (tid < TC) sm.fg[base + tid] = R2{st_f, Real(1) - st_f};
   };
-  // write back one chunk of readouts (staged in lane order)
+  // write back one chunk of readouts (staged in lane order); element e of the
+  // chunk is (step e / VP, lane-order column e % VP)
+  constexpr int NY_PER = (TC * VP + NT - 1) / NT;
+  int64_t y_ofs[NY_PER];
+  Real y_wr[NY_PER];
+  int y_tt[NY_PER], y_c[NY_PER], y_g[NY_PER], y_r[NY_PER];
+  bool y_ok[NY_PER];
+#pragma unroll
+  for (int k = 0; k < NY_PER; ++k) {
+    const int e = tid + k * NT;
+    const int tt = e / VP, jl = e % VP;
+    y_tt[k] = tt < TC ? tt : 0;
+    y_c[k] = jl >> 4;
+    y_g[k] = (jl >> 2) & 3;
+    y_r[k] = jl & 3;
+    const int j = y_c[k] * 16 + acc_m<Real>(y_g[k], y_r[k]);
+    y_ok[k] = tt < TC && j < V;
+    y_ofs[k] = (tok0 + (int64_t)y_tt[k] * N) * V + (j < V ? j : 0);
+    y_wr[k] = j < V ? wrp[(int64_t)n * V + j] : Real(0);
+  }
   auto flush = [&](int64_t ch) {
     const int64_t t0 = ch * TC;
     const int base = (int)(ch & 1) * TC;
-    for (int e = tid; e < TC * VP; e += NT) {
-      const int tt = e / VP, jl = e % VP;
-      const int c = jl >> 4, gg = (jl >> 2) & 3, rr = jl & 3;
-      const int j = c * 16 + acc_m<Real>(gg, rr);
-      if (t0 + tt < T && j < V) {
-        const int64_t off = (((int64_t)b * T + t0 + tt) * N + n) * V + j;
-        const Real val = sm.y[base + tt][c][gg][rr];
+    const int64_t cofs = t0 * NV;
+#pragma unroll
+    for (int k = 0; k < NY_PER; ++k) {
+      if (y_ok[k] && t0 + y_tt[k] < T) {
+        const int slot = base + y_tt[k];
+        const Real val = sm.y[slot][y_c[k]][y_g[k]][y_r[k]];
         if (nslab == 1) {
-          yout[off] = val + wrp[(int64_t)n * V + j] * sm.r1[base + tt][c][acc_m<Real>(gg, rr)][0];
+          const Real vv = sm.r1[slot][y_c[k]][acc_m<Real>(y_g[k], y_r[k])][0];
+          yout[y_ofs[k] + cofs] = val + y_wr[k] * vv;
         } else {
-          ypart[slab * slab_stride + off] = val;
+          ypart[slab * slab_stride + y_ofs[k] + cofs] = val;
         }
       }
     }
@@ -218,30 +263,45 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
     for (int r = 0; r < 4; ++r) hb[4 * q0 + r] = t4[r];
   }
 
-  // Per-lane LDS base addresses.  Within a chunk every step's address is this
-  // base plus a compile-time offset.  A-operand of the rank-1 MFMA: v in lane
-  // group 0, zero elsewhere (the mask is applied when read).
+  // A-operand of the rank-1 MFMA: v in lane group 0, zero elsewhere (the mask
+  // is applied when the operand is formed).
   const Real a_mask = g == 0 ? Real(1) : Real(0);
   R4* const ydump_me = &sm.ydump[tid];
 
-  // One step at ring slot SI (compile-time within the chunk); P = parity.
-  auto step = [&](auto si_c, int base) {
-    constexpr int SI = decltype(si_c)::value;   // slot within the chunk, 0 .. TC - 1
-    constexpr int P = SI & 1;
-    const int slot = base + SI;
+  // Inputs of one step, read from the staging ring one step ahead of use so
+  // their LDS latency is hidden behind the previous step's MFMA chain.
+  struct StepIn {
+    R2 vk[TPW];   // rank-1 operands (v_{16 c + li}, k_li) of this wave's tiles
+    R2 fg;        // (f, 1 - f)
+    Real q;       // q_li
+  };
+  auto read_in = [&](int slot) {
+    StepIn in;
+#pragma unroll
+    for (int p = 0; p < TPW; ++p) in.vk[p] = sm.r1[slot][w * TPW + p][li];
+    in.fg = sm.fg[slot];
+    in.q = sm.q[slot][li];
+    return in;
+  };
+
+  // One step; P = parity of the step (static LDS offsets).  `nxt_slot` is the
+  // ring slot of the following step, whose inputs are read at the start.
+  auto step = [&](auto par, int slot, const StepIn& cur, StepIn& nxt, int nxt_slot) {
+    constexpr int P = decltype(par)::value;
+    nxt = read_in(nxt_slot);
     R4 acc[TPW];
 #pragma unroll
     for (int p = 0; p < TPW; ++p) acc[p] = R4{0, 0, 0, 0};
+    // own tiles first (operands in registers), the rank-1 write, then the
+    // tiles received through LDS
 #pragma unroll
     for (int s0 = 0; s0 < 4 * TPW; ++s0) {
 #pragma unroll
       for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wa[p][s0], hb[s0], acc[p]);
     }
 #pragma unroll
-    for (int p = 0; p < TPW; ++p) {
-      const R2 vk = sm.r1[slot][w * TPW + p][li];
-      acc[p] = mfma_16x16x4(vk[0] * a_mask, vk[1], acc[p]);
-    }
+    for (int p = 0; p < TPW; ++p)
+      acc[p] = mfma_16x16x4(cur.vk[p][0] * a_mask, cur.vk[p][1], acc[p]);
 #pragma unroll
     for (int s0 = 4 * TPW; s0 < NS; ++s0) {
 #pragma unroll
@@ -249,30 +309,32 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
     }
     // H = f H + (1 - f) tanh(A), with tanh(A) = 1 - 2 / (1 + e^{2A}):
     // H = (f H + (1 - f)) - 2 (1 - f) / (1 + e^{2A}).  f = 1 gives H exactly.
-    const R2 fg = sm.fg[slot];
-    const Real m2omf = Real(-2) * fg[1];
+    const Real m2omf = Real(-2) * cur.fg[1];
 #pragma unroll
     for (int p = 0; p < TPW; ++p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const Real rc = sigmoid_neg2x(acc[p][r]);
-        hown[p][r] = fma_r(m2omf, rc, fma_r(fg[0], hown[p][r], fg[1]));
+        hown[p][r] = fma_r(m2omf, rc, fma_r(cur.fg[0], hown[p][r], cur.fg[1]));
       }
       sm.xb[P][w * TPW + p][lane] = hown[p];
     }
+    // keep the exchange write ahead of the readout, so its latency overlaps it
+    __builtin_amdgcn_sched_barrier(0);
     // readout y_t = H_t^T q_t over this slab's rows, while the write lands
-    const Real qv = sm.q[slot][li];
+    // (the reduction is volatile asm for fp32, so it also stays before the barrier)
     R4 ys[TPW];
 #pragma unroll
-    for (int p = 0; p < TPW; ++p)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ys[p][r] = row16_sum(hown[p][r] * qv);
+    for (int p = 0; p < TPW; ++p) ys[p] = row16_sum_x4(hown[p], cur.q);
+    __syncthreads();
+    // the readout store goes after the barrier (its latency then overlaps the
+    // own-tile MFMAs of the next step); the barrier ending the chunk's last
+    // step is followed by one more before the write-back reads it
 #pragma unroll
     for (int p = 0; p < TPW; ++p) {
       R4* dst = li == 0 ? &sm.y[slot][w * TPW + p][g] : ydump_me;
       *dst = ys[p];
     }
-    __syncthreads();
 #pragma unroll
     for (int q0 = TPW; q0 < VT; ++q0) {
       const R4 t4 = sm.xb[P][(q0 + TPW * w) % VT][lane];
@@ -283,16 +345,24 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
     for (int p = 0; p < TPW; ++p)
 #pragma unroll
       for (int r = 0; r < 4; ++r) hb[4 * p + r] = hown[p][r];
+    // the exchange reads are issued before any MFMA of the next step
+    __builtin_amdgcn_sched_barrier(0);
   };
-  // A whole chunk, unrolled; `store_next` stages chunk ch + 1 after step TC - 2
-  // (the barrier of step TC - 1 then makes it visible before chunk ch + 1).
+  // A whole chunk, unrolled.  Chunk ch + 1 is staged after step TC - 3, so
+  // the barrier of step TC - 2 orders it before step TC - 1 reads its first
+  // slot.  Inputs alternate between two StepIn buffers by step parity.
+  StepIn ins[2];
   auto full_chunk = [&](int base, bool store_next, int64_t ch) {
+    const int nbase = base ^ TC;
     [&]<int... I>(std::integer_sequence<int, I...>) {
-      ((step(std::integral_constant<int, I>{}, base),
-        (I == TC - 2 && store_next ? store_chunk(ch + 1) : void())),
+      ((step(std::integral_constant<int, I & 1>{}, base + I, ins[I & 1], ins[(I + 1) & 1],
+             I + 1 < TC ? base + I + 1 : nbase),
+        (I == TC - 3 && store_next ? store_chunk(ch + 1) : void())),
        ...);
     }(std::make_integer_sequence<int, TC>{});
   };
+
+  ins[0] = read_in(0);
 
   // Checkpoints need a chunk boundary at every multiple of C; with C a
   // multiple of TC they all fall between chunks.
@@ -308,11 +378,12 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
       // generic path: the partial last chunk, or checkpoints inside chunks
       const int tn = (int)((T - t0) < TC ? (T - t0) : TC);
       for (int tt = 0; tt < tn; ++tt) {
-        // dispatch the compile-time slot (the generic path is rare)
-        [&]<int... I>(std::integer_sequence<int, I...>) {
-          ((tt == I ? step(std::integral_constant<int, I>{}, base) : void()), ...);
-        }(std::make_integer_sequence<int, TC>{});
-        if (tt == TC - 2 && !last) store_chunk(ch + 1);
+        const int nslot = tt + 1 < TC ? base + tt + 1 : (base ^ TC);
+        if ((tt & 1) == 0)
+          step(std::integral_constant<int, 0>{}, base + tt, ins[0], ins[1], nslot);
+        else
+          step(std::integral_constant<int, 1>{}, base + tt, ins[1], ins[0], nslot);
+        if (tt == TC - 3 && !last) store_chunk(ch + 1);
         const int64_t t = t0 + tt;
         if (a.ckpt && !ck_at_chunks && (t + 1) % a.C == 0 && t + 1 < T)
           write_state(ck0 + ((t + 1) / a.C) * K * V);
@@ -321,6 +392,7 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
     // ---- between chunks: checkpoint, write-back of this chunk, prefetch
     const int64_t tend = t0 + TC;   // steps done after this chunk (if not last)
     if (!last && a.ckpt && ck_at_chunks && tend % a.C == 0) write_state(ck0 + (tend / a.C) * K * V);
+    __syncthreads();                             // the chunk's last readout stores
     flush(ch);                                   // readouts of chunk ch are complete
     if (ch + 2 < nchunks) load_chunk(ch + 2);    // into registers; stored during chunk ch + 1
   }
