@@ -19,7 +19,8 @@ bool sizes_ok(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V) {
 
 bool sizes_supported(int64_t B, int64_t N, int64_t K, int64_t V) {
   if (K > 256 || V > 128) return false;
-  return (double)B * (double)N * (double)num_slabs(K) <= (double)INT_MAX;
+  // one workgroup (at most 1024 threads) per slab: the grid stays below 2^32 threads
+  return (double)B * (double)N * (double)num_slabs(K) < (double)(1 << 22);
 }
 
 size_t real_size(int state_dtype) { return state_dtype == M2RNN_F64 ? 8 : 4; }
@@ -48,7 +49,7 @@ size_t fwd_ws_bytes(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V, int s
 
 size_t bwd_ws_bytes(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V, int64_t C,
                     int state_dtype) {
-  const BwdWorkspace L = bwd_workspace_layout(B, T, N, K, V, C);
+  const BwdWorkspace L = bwd_workspace_layout(B, T, N, K, V, C, state_dtype);
   return align_up(L.total_elems * real_size(state_dtype), 256);
 }
 

@@ -1,40 +1,119 @@
 // Reverse-time M²RNN backward for gfx950.
 //
 // Implements the corrected BPTT chain rule of the M²RNN review (section 2.7),
-// with the value-residual branch restored, and the review's section 2.6
-// scheme of rerunning the recurrence before the reverse scan -- restricted to
-// one checkpoint interval at a time.  For each (b, n) and each interval
-// [cC, cC + L) taken from last to first:
-//   1. recompute the L steps from ckpt[c] = H_{cC} (same MFMA step as the
-//      forward), keeping H_{t-1} and Z_t of every step in a per-slab
-//      workspace (each lane stores and reloads its own tiles);
-//   2. walk the L steps backwards:
-//        R = C + q u^T,  D = (1 - f) R (.) (1 - Z^2),  C <- f R + D W^T  (MFMA)
-//        dW += H_{t-1}^T D                                              (MFMA)
-//        dq = H_t u, dk = D v (row sums), dv = D^T k (sum over the slab's rows),
-//        df = <R, H_{t-1} - Z>.
-// As in the forward, a workgroup owns one 16-row slab; rows are independent
-// in the backward as well (W^T acts on columns), so only dv, df and dW need
-// sums across slabs, done by fixed-order reduction kernels afterwards.
+// with the value-residual branch restored, and recomputes the forward states
+// from checkpoints as the review's section 2.6 describes.  With u_t = dy_t and
+// C_t the gradient arriving at the state H_t from later steps:
+//   R_t = C_t + q_t u_t^T,  D_t = (1 - f_t) R_t (.) (1 - Z_t^2),
+//   C_{t-1} = f_t R_t + D_t W^T,  dW += H_{t-1}^T D_t,
+//   dq_t = H_t u_t,  dk_t = D_t v_t,  dv_t = D_t^T k_t + w_r (.) u_t,
+//   df_t = <R_t, H_{t-1} - Z_t>.
+// Token t here is 0-based: step t reads state S_t and writes S_{t+1}.
 //
-// MFMA layouts.  C W-product: (D W^T)^T = W D^T, A = W (registers), B = D^T,
-// with the same contraction enumeration pi(s, g) = 16 (s / 4) + m(g, s % 4) as
-// the forward, so D's own tiles feed the B operand straight from registers and
-// the other waves' tiles come through LDS.  dW: output tile (l, j), A[l][i] =
-// H_{t-1}[i][l], B[i][j] = D[i][j], contraction over the 16 slab rows in four
-// k-steps; both operands are read transposed from the LDS exchange buffers.
+// Decomposition.  As in the forward, one workgroup per 16-row slab of one
+// (b, n): rows are independent in the backward as well (W^T acts on columns),
+// so only dv, df and dW need sums across slabs, done by fixed-order reduction
+// kernels afterwards.
+//
+// Two wave roles per workgroup, one wave of each role on every SIMD:
+//  * forward role: reruns the recurrence chunk by chunk (S steps per chunk,
+//    chunks from last to first), each chunk from its stored start state, with
+//    exactly the forward kernel's arithmetic.  Every step's state S_{t+1} and
+//    rc_t = 1 / (1 + e^{2 A_t}) (tanh(A_t) = 1 - 2 rc_t) go into LDS rings.
+//    The same waves form dq_t = S_{t+1} u_t and accumulate dW on MFMA from the
+//    D tiles the reverse role publishes.
+//  * reverse role: walks the chunk recomputed in the previous period from its
+//    last step to its first, one phase behind, carrying C through the MFMA
+//    product (D W^T)^T = W D^T, and forms dk, dv and df.
+// Both roles finish one step per phase (one barrier per phase).  Sharing the
+// SIMDs, one role's VALU and LDS work overlaps the other's MFMA chain.  The
+// rings hold 2 S entries; with the reverse role one phase behind, no ring
+// entry, staging slot or exchange buffer is read and written in the same
+// phase (the schedule is checked step by step on the host in the tests).
+//
+// MFMA layouts.  Recompute: A = W^T (registers), B = S^T, exactly as in the
+// forward.  C-chain: A = W, B = D^T with the same contraction enumeration
+// pi(s, g) = 16 (s / 4) + m(g, s % 4), so a wave's own D tiles feed the B
+// operand from registers and the others come through LDS.  dW: output tile
+// (l, j), A[l][i] = S_t[i][l], B[i][j] = D_t[i][j], contraction over the 16
+// slab rows in four k-steps; both operands are read transposed from LDS.
+
+#include <utility>
 
 #include "m2rnn_device.h"
 #include "m2rnn_internal.h"
 
 namespace m2rnn {
 
+constexpr size_t kLdsBytes = 160 * 1024;
+
+template <typename Real, int VT>
+struct BwdShape {
+  static constexpr int VP = 16 * VT;                       // padded value width
+  static constexpr int NW = VT <= 4 ? VT : VT / 2;         // waves per role
+  static constexpr int TPW = VT / NW;                      // 16-column tiles per wave
+  static constexpr int NS = 4 * VT;                        // MFMAs per tile per step
+  static constexpr int NT = 2 * 64 * NW;                   // threads (both roles)
+  static constexpr int E = (32 + 2 * VP + 1 + 3) / 4 * 4;  // staged values per step
+  static constexpr size_t kTileset = (size_t)VT * 64 * 4 * sizeof(Real);
+};
+
+// LDS of the backward for chunk length S: two rings of 2 S slab states, the
+// D exchange, the staging slots and the reduction partials.
+template <typename Real, int VT>
+constexpr size_t bwd_smem_bytes(int S) {
+  using Sh = BwdShape<Real, VT>;
+  return (size_t)(4 * S + 2) * Sh::kTileset + (size_t)(S >= 2 ? 3 : 4) * S * Sh::E * sizeof(Real) +
+         (size_t)(2 * 2 * 16 * 4 * Sh::NW + 2 * 4 * Sh::NW) * sizeof(Real);
+}
+
+template <typename Real, int VT>
+struct BwdTraits : BwdShape<Real, VT> {
+  using Sh = BwdShape<Real, VT>;
+  // the longest chunk (at most 8 steps, a power of two) whose LDS fits
+  static constexpr int S = bwd_smem_bytes<Real, VT>(8) <= kLdsBytes   ? 8
+                           : bwd_smem_bytes<Real, VT>(4) <= kLdsBytes ? 4
+                           : bwd_smem_bytes<Real, VT>(2) <= kLdsBytes ? 2
+                                                                      : 1;
+  static constexpr int M = 2 * S;                              // ring length
+  static constexpr int NSLOT = S >= 2 ? 3 : 4;                 // staging slots (chunks)
+  static constexpr int NLD = (S * Sh::E + Sh::NT - 1) / Sh::NT;  // staged values per thread
+};
+
+template <typename Real, int VT>
+struct BwdSmem {
+  using Tr = BwdTraits<Real, VT>;
+  using R4 = typename Vec4<Real>::type;
+  R4 hr[Tr::M][VT][64];           // states S_x at ring position x mod M
+  R4 zr[Tr::M][VT][64];           // rc_t at ring position t mod M
+  R4 xd[2][VT][64];               // D tiles, double-buffered by phase parity
+  // staged inputs of a chunk, per step: k[16] q[16] v[VP] dy[VP] f (padded)
+  Real st[Tr::NSLOT][Tr::S * Tr::E];
+  Real rq[2][16][4 * Tr::NW];     // dq lane partials [row][wave, lane group]
+  Real rk[2][16][4 * Tr::NW];     // dk lane partials
+  Real rf[2][4 * Tr::NW];         // df partials [wave, lane group]
+};
+
+int bwd_period(int state_dtype, int64_t V) {
+  const bool f64 = state_dtype == kF64;
+  switch (value_tiles(V)) {
+    case 1: return f64 ? BwdTraits<double, 1>::S : BwdTraits<float, 1>::S;
+    case 2: return f64 ? BwdTraits<double, 2>::S : BwdTraits<float, 2>::S;
+    case 3: return f64 ? BwdTraits<double, 3>::S : BwdTraits<float, 3>::S;
+    case 4: return f64 ? BwdTraits<double, 4>::S : BwdTraits<float, 4>::S;
+    case 6: return f64 ? BwdTraits<double, 6>::S : BwdTraits<float, 6>::S;
+    case 8: return f64 ? BwdTraits<double, 8>::S : BwdTraits<float, 8>::S;
+    default: return 1;
+  }
+}
+
 BwdWorkspace bwd_workspace_layout(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V,
-                                  int64_t C) {
+                                  int64_t C, int state_dtype) {
   BwdWorkspace L{};
   const int64_t ns = num_slabs(K);
-  const int64_t vt = value_tiles(V);
-  const size_t units = (size_t)(B * N * ns);
+  L.period = bwd_period(state_dtype, V);
+  L.nch = (T + L.period - 1) / L.period;
+  L.subck_needed = (L.period % C) != 0;
   const int64_t rows = B * T;
   L.row_blocks = (rows + 255) / 256;
   size_t off = 0;
@@ -43,8 +122,7 @@ BwdWorkspace bwd_workspace_layout(int64_t B, int64_t T, int64_t N, int64_t K, in
     off = align_up(off + elems, 64);
     return at;
   };
-  L.slot_elems = (size_t)vt * 64 * 4;
-  L.states = take(units * (size_t)(2 * C + 1) * L.slot_elems);
+  L.subck = take(L.subck_needed ? (size_t)B * N * L.nch * K * V : 0);
   L.dv_part = take(ns > 1 ? (size_t)ns * B * T * N * V : 0);
   L.df_part = take((size_t)ns * B * T * N);
   L.dW_part = take((size_t)B * ns * N * V * V);
@@ -53,60 +131,550 @@ BwdWorkspace bwd_workspace_layout(int64_t B, int64_t T, int64_t N, int64_t K, in
   return L;
 }
 
-template <typename Real, int VT>
-struct BwdTraits {
-  static constexpr int VP = 16 * VT;
-  static constexpr int NW = VT <= 4 ? VT : VT / 2;
-  static constexpr int TPW = VT / NW;
-  static constexpr int NT = 64 * NW;
-  static constexpr int NS = 4 * VT;
-};
-
-template <typename Real, int VT, int NW>
-struct BwdSmem {
-  using R4 = typename Vec4<Real>::type;
-  R4 xb[2][VT][64];      // H exchange (recompute) / H_{t-1} for dW (reverse)
-  R4 xd[2][VT][64];      // D exchange
-  Real red[2][2][NW][16];  // per-wave row partials of dq and dk
-  Real redf[2][NW];        // per-wave partials of df
-};
+// Four values of columns 16 c + m(g, r), r = 0..3, from a row of staged values
+// starting at column 16 c.
+__device__ __forceinline__ f32x4 cols4(const float* p, int g) {
+  return *(const f32x4*)(p + 4 * g);
+}
+__device__ __forceinline__ f64x4 cols4(const double* p, int g) {
+  return f64x4{p[g], p[4 + g], p[8 + g], p[12 + g]};
+}
 
 template <typename InT, typename Real, int VT>
 __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
     m2rnn_bwd_kernel(BwdArgs a, BwdWorkspace L) {
   using Tr = BwdTraits<Real, VT>;
   using R4 = typename Vec4<Real>::type;
-  constexpr int TPW = Tr::TPW, NS = Tr::NS, NW = Tr::NW;
-  __shared__ BwdSmem<Real, VT, NW> sm;
+  constexpr int TPW = Tr::TPW, NS = Tr::NS, NW = Tr::NW, NT = Tr::NT, VP = Tr::VP;
+  constexpr int S = Tr::S, M = Tr::M, NSLOT = Tr::NSLOT, E = Tr::E, NLD = Tr::NLD;
+  constexpr int OFF_Q = 16, OFF_V = 32, OFF_U = 32 + VP, OFF_F = 32 + 2 * VP;
+  __shared__ BwdSmem<Real, VT> sm;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, g = lane >> 4, li = lane & 15;
+  const bool fwd_role = w < NW;
+  const int wr = fwd_role ? w : w - NW;
   const int unit = xcd_remap(blockIdx.x, gridDim.x);
   const int nslab = a.nslab;
   const int slab = unit % nslab;
   const int bn = unit / nslab;
-  const int64_t B = a.B, T = a.T, N = a.N, K = a.K, V = a.V, C = a.C;
+  const int64_t B = a.B, T = a.T, N = a.N, K = a.K, V = a.V;
   const int n = (int)(bn % N);
   const int b = (int)(bn / N);
   const int row = slab * 16 + li;
   const bool row_ok = row < K;
-  const int64_t rowc = row_ok ? row : K - 1;  // clamped row for unconditional loads
+  const int64_t nch = (T + S - 1) / S;
+  const int64_t jlast = nch * S + S + 1;        // last phase
+  const int64_t nper = jlast / S + 1;           // periods of S phases covering 0..jlast
+  const int64_t tok0 = (int64_t)b * T * N + n;  // token (b, t, n) is tok0 + t N
+  const int64_t tok_stride = B * T * N;
+  const int64_t state_base = ((int64_t)bn * K + row) * V;
 
   const InT* __restrict__ kp = (const InT*)a.k;
   const InT* __restrict__ vp = (const InT*)a.v;
   const InT* __restrict__ qp = (const InT*)a.q;
   const Real* __restrict__ fp = (const Real*)a.f;
   const Real* __restrict__ Wp = (const Real*)a.W;
-  const Real* __restrict__ wrp = (const Real*)a.w_r;
   const Real* __restrict__ dyp = (const Real*)a.dy;
   Real* __restrict__ ws = (Real*)a.ws;
-  R4* __restrict__ slots = (R4*)(ws + L.states + (size_t)unit * (size_t)(2 * C + 1) * L.slot_elems);
-  Real* __restrict__ dv_part = ws + L.dv_part;
-  Real* __restrict__ df_part = ws + L.df_part;
-  const int64_t tok_stride = B * T * N;
+  auto col_of = [&](int p, int r) { return (wr * TPW + p) * 16 + acc_m<Real>(g, r); };
 
-  // A operands: W^T for the recompute (as in the forward), W for C <- f R + D W^T.
-  Real wf[TPW][NS], wb[TPW][NS];
+  // the first reverse step has no later step: its D exchange reads zeros
+  for (int i = tid; i < 2 * VT * 64; i += NT) (&sm.xd[0][0][0])[i] = R4{0, 0, 0, 0};
+
+  // ---- staging of one chunk's inputs.  Thread tid owns the staged values
+  // e = tid + m NT of a chunk (step e / E, field by e % E); its source offsets
+  // for chunk c are fixed offsets plus the step index times a stride.  Steps
+  // past T are padding: f = 1 and dy = 0 make them exact identities.
+  // Each value comes from an InT array (k, q, v) or a Real array (dy, f); both
+  // source pointers are kept valid, and the unused one is never selected.
+  const InT* ld_pin[NLD];
+  const Real* ld_pre[NLD];
+  int64_t ld_ts[NLD];
+  int ld_dst[NLD], ld_tt[NLD];
+  bool ld_in[NLD], ld_ok[NLD], ld_isf[NLD];
+#pragma unroll
+  for (int m = 0; m < NLD; ++m) {
+    const int e = tid + m * NT;
+    const int tt = e / E, r = e % E;
+    const InT* pin = kp;
+    const Real* pre = fp;
+    bool from_in = false, ok = false, isf = false;
+    int64_t ts = 0;
+    if (e < S * E) {
+      if (r < 32) {  // k (r < 16) or q, slab row r mod 16
+        const int rr = slab * 16 + (r & 15);
+        ok = rr < K;
+        from_in = true;
+        pin = (r < 16 ? kp : qp) + tok0 * K + (ok ? rr : 0);
+        ts = N * K;
+      } else if (r < OFF_U) {  // v, column r - 32
+        const int j = r - OFF_V;
+        ok = j < V;
+        from_in = true;
+        pin = vp + tok0 * V + (ok ? j : 0);
+        ts = N * V;
+      } else if (r < OFF_F) {  // dy, column r - 32 - VP
+        const int j = r - OFF_U;
+        ok = j < V;
+        pre = dyp + tok0 * V + (ok ? j : 0);
+        ts = N * V;
+      } else if (r == OFF_F) {  // f
+        ok = true;
+        isf = true;
+        pre = fp + tok0;
+        ts = N;
+      }
+    }
+    ld_pin[m] = pin;
+    ld_pre[m] = pre;
+    ld_ts[m] = ts;
+    ld_dst[m] = e < S * E ? e : -1;
+    ld_tt[m] = e < S * E ? tt : 0;
+    ld_in[m] = from_in;
+    ld_ok[m] = ok;
+    ld_isf[m] = isf;
+  }
+  Real stx[NLD];
+  auto stage_load = [&](int64_t c) {
+    const int64_t t0 = c * S;
+#pragma unroll
+    for (int m = 0; m < NLD; ++m) {
+      const int64_t t = t0 + ld_tt[m];
+      const bool tv = t < T;
+      const int64_t o = (tv ? t : T - 1) * ld_ts[m];
+      const Real xi = load_as<Real>(ld_pin[m] + (ld_in[m] ? o : 0));
+      const Real xr = ld_pre[m][ld_in[m] ? 0 : o];
+      const Real x = ld_in[m] ? xi : xr;
+      stx[m] = (ld_ok[m] && tv) ? x : (ld_isf[m] ? Real(1) : Real(0));
+    }
+  };
+  auto stage_store = [&](int64_t c) {
+    Real* dst = sm.st[(int)(c % NSLOT)];
+#pragma unroll
+    for (int m = 0; m < NLD; ++m)
+      if (ld_dst[m] >= 0) dst[ld_dst[m]] = stx[m];
+  };
+
+  if (fwd_role) {
+    // ================================================================ forward role
+    // W^T as the A operand, rotated so this wave's own tiles come first
+    Real wop[TPW][NS];
+#pragma unroll
+    for (int p = 0; p < TPW; ++p) {
+      const int col = (wr * TPW + p) * 16 + li;
+#pragma unroll
+      for (int s0 = 0; s0 < NS; ++s0) {
+        const int s = (s0 + 4 * TPW * wr) % NS;
+        const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
+        wop[p][s0] = (col < V && l < V) ? Wp[((int64_t)n * V + l) * V + col] : Real(0);
+      }
+    }
+    // start state of a chunk: all VT tiles of row `row`, in B-operand order
+    // (entry q0 holds tile (q0 + TPW wr) mod VT, so this wave's own tiles come first)
+    auto load_start = [&](int64_t c, R4 (&dst)[VT]) {
+      const Real* src =
+          (const Real*)a.cks + (((int64_t)bn * a.cks_count + c * a.cks_step) * K + (row_ok ? row : 0)) * V;
+#pragma unroll
+      for (int q0 = 0; q0 < VT; ++q0)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int col = 16 * ((q0 + TPW * wr) % VT) + acc_m<Real>(g, r);
+          dst[q0][r] = load_sel<Real>(src, col < V ? col : 0, row_ok && col < V);
+        }
+    };
+    R4 ckc[VT], ckn[VT];
+    load_start(nch - 1, ckn);
+    R4 h[TPW];
+    Real hb[NS];
+    R4 dWacc[TPW][VT];
+    Real aop[TPW][4];
+#pragma unroll
+    for (int p = 0; p < TPW; ++p) {
+      h[p] = R4{0, 0, 0, 0};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) aop[p][kk] = Real(0);
+#pragma unroll
+      for (int jt = 0; jt < VT; ++jt) dWacc[p][jt] = R4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int s0 = 0; s0 < NS; ++s0) hb[s0] = Real(0);
+    const Real a_mask = g == 0 ? Real(1) : Real(0);
+    // transposed LDS element (row 4 kk + g, column li) of a tile: lane
+    // 16 acc_g(li) + 4 kk + g, element acc_r(li)
+    auto tidx = [&](int kk) { return (16 * acc_g<Real>(li) + 4 * kk + g) * 4 + acc_r<Real>(li); };
+
+    stage_load(nch - 1);
+    stage_store(nch - 1);
+    __syncthreads();
+
+    auto phase = [&](auto Ic, int64_t k, int64_t cF, bool rec, int slot, int hbase) {
+      constexpr int I = decltype(Ic)::value;
+      const int64_t j = k * S + I;
+      const int jp = (int)(j & 1);
+      // dq of the previous phase's step: the per-wave partials, summed by wave 0
+      if (wr == 0 && g == 0 && j >= 1 && j <= nch * S) {
+        const int64_t tp = I > 0 ? cF * S + I - 1 : (cF + 1) * S + S - 1;
+        if (tp < T && row_ok) {
+          Real s = 0;
+#pragma unroll
+          for (int i = 0; i < 4 * NW; ++i) s += sm.rq[jp ^ 1][li][i];
+          ((Real*)a.dq)[(tok0 + tp * N) * K + row] = s;
+        }
+      }
+      auto dw_mfma = [&]() {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int idx = tidx(kk);
+#pragma unroll
+          for (int jt = 0; jt < VT; ++jt) {
+            const Real bop = ((const Real*)&sm.xd[jp ^ 1][jt][0])[idx];
+#pragma unroll
+            for (int p = 0; p < TPW; ++p) dWacc[p][jt] = mfma_16x16x4(aop[p][kk], bop, dWacc[p][jt]);
+          }
+        }
+      };
+      if (rec) {
+        // the step t = cF S + I from state S_t
+        if constexpr (I == 0) {
+#pragma unroll
+          for (int p = 0; p < TPW; ++p) h[p] = ckc[p];
+#pragma unroll
+          for (int q0 = 0; q0 < VT; ++q0)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hb[4 * q0 + r] = ckc[q0][r];
+        } else {
+#pragma unroll
+          for (int q0 = TPW; q0 < VT; ++q0) {
+            const R4 t4 = sm.hr[hbase + I][(q0 + TPW * wr) % VT][lane];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hb[4 * q0 + r] = t4[r];
+          }
+#pragma unroll
+          for (int p = 0; p < TPW; ++p)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hb[4 * p + r] = h[p][r];
+        }
+        const Real* stp = &sm.st[slot][I * E];
+        const Real f = stp[OFF_F];
+        const Real omf = Real(1) - f;
+        const Real kli = stp[li];
+        R4 acc[TPW];
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) acc[p] = R4{0, 0, 0, 0};
+#pragma unroll
+        for (int s0 = 0; s0 < 4 * TPW; ++s0)
+#pragma unroll
+          for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wop[p][s0], hb[s0], acc[p]);
+#pragma unroll
+        for (int p = 0; p < TPW; ++p)
+          acc[p] = mfma_16x16x4(stp[OFF_V + (wr * TPW + p) * 16 + li] * a_mask, kli, acc[p]);
+#pragma unroll
+        for (int s0 = 4 * TPW; s0 < NS; ++s0)
+#pragma unroll
+          for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wop[p][s0], hb[s0], acc[p]);
+        // dW += S_t'^T D_t' for the reverse role's previous step t' (zero
+        // A operands when it had none), then the accumulators are read here, in
+        // the block of the MFMAs: the first read of an MFMA result must not sit
+        // behind a branch, where the wait states it needs are not inserted
+        dw_mfma();
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) pin_vec(acc[p]);
+        const Real m2omf = Real(-2) * omf;
+        Real dqp = 0;
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) {
+          R4 rc;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            rc[r] = sigmoid_neg2x(acc[p][r]);
+            h[p][r] = fma_r(m2omf, rc[r], fma_r(f, h[p][r], omf));
+          }
+          sm.hr[(hbase + I + 1) & (M - 1)][wr * TPW + p][lane] = h[p];
+          sm.zr[hbase + I][wr * TPW + p][lane] = rc;
+          const R4 u = cols4(stp + OFF_U + (wr * TPW + p) * 16, g);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dqp = fma_r(h[p][r], u[r], dqp);
+        }
+        sm.rq[jp][li][wr * 4 + g] = dqp;
+      } else {
+        dw_mfma();
+      }
+      // dW operands of the step the reverse role takes in this phase: S_t
+      // transposed, or zeros when it takes none
+      {
+        const bool ract = j >= S + 1 && j <= nch * S + S;
+        const int pos = (int)((nch * S + S - j) & (M - 1));
+#pragma unroll
+        for (int p = 0; p < TPW; ++p)
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const Real x = ((const Real*)&sm.hr[ract ? pos : 0][wr * TPW + p][0])[tidx(kk)];
+            aop[p][kk] = ract ? x : Real(0);
+          }
+      }
+      // S_0 (the initial state) for the reverse role's last step
+      if (j == nch * S) {
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) {
+          R4 h0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int col = col_of(p, r);
+            h0[r] = (a.H0 && row_ok && col < V) ? ((const Real*)a.H0)[state_base + col] : Real(0);
+          }
+          sm.hr[0][wr * TPW + p][lane] = h0;
+        }
+      }
+    };
+
+    for (int64_t k = 0; k < nper; ++k) {
+      const int64_t cF = nch - 1 - k;  // chunk recomputed in this period
+      const bool rec = cF >= 0;
+      const int slot = rec ? (int)(cF % NSLOT) : 0;
+      const int hbase = rec ? (int)(cF & 1) * S : 0;  // ring position of S_{cF S}
+      if (rec) {
+#pragma unroll
+        for (int q = 0; q < VT; ++q) ckc[q] = ckn[q];
+        if (cF >= 1) load_start(cF - 1, ckn);
+      }
+      const bool stage = cF >= 1;
+      if (stage) stage_load(cF - 1);
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        ((phase(std::integral_constant<int, I>{}, k, cF, rec, slot, hbase),
+          (I == S - 1 && stage ? stage_store(cF - 1) : void()), __syncthreads()),
+         ...);
+      }(std::make_integer_sequence<int, S>{});
+    }
+
+    // this slab's share of dW: lane holds dW[16 c + m(g, r)][16 jt + li].
+    // The last dW MFMAs sit in the loop; sleep before the accumulators are read.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_sleep(2);
+    __builtin_amdgcn_sched_barrier(0);
+    Real* dWp = ws + L.dW_part + (((size_t)b * nslab + slab) * N + n) * V * V;
+#pragma unroll
+    for (int p = 0; p < TPW; ++p)
+#pragma unroll
+      for (int jt = 0; jt < VT; ++jt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int l = col_of(p, r);
+          const int jj = jt * 16 + li;
+          if (l < V && jj < V) dWp[(int64_t)l * V + jj] = dWacc[p][jt][r];
+        }
+  } else {
+    // ================================================================ reverse role
+    // W as the A operand of (D W^T)^T = W D^T, rotated like the forward role's
+    Real wop[TPW][NS];
+#pragma unroll
+    for (int p = 0; p < TPW; ++p) {
+      const int col = (wr * TPW + p) * 16 + li;
+#pragma unroll
+      for (int s0 = 0; s0 < NS; ++s0) {
+        const int s = (s0 + 4 * TPW * wr) % NS;
+        const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
+        wop[p][s0] = (col < V && l < V) ? Wp[((int64_t)n * V + col) * V + l] : Real(0);
+      }
+    }
+    R4 fR[TPW], Dp[TPW], rcn[TPW];
+    Real wrc[TPW][4];
+#pragma unroll
+    for (int p = 0; p < TPW; ++p) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int col = col_of(p, r);
+        fR[p][r] = (a.dHT && row_ok && col < V) ? ((const Real*)a.dHT)[state_base + col] : Real(0);
+        wrc[p][r] = col < V ? ((const Real*)a.w_r)[(int64_t)n * V + col] : Real(0);
+      }
+      Dp[p] = R4{0, 0, 0, 0};
+      rcn[p] = R4{0, 0, 0, 0};
+    }
+    Real* __restrict__ df_part = ws + L.df_part;
+    Real* __restrict__ dv_part = ws + L.dv_part;
+
+    stage_load(nch - 1);
+    stage_store(nch - 1);
+    __syncthreads();
+
+    auto phase = [&](auto Ic, int64_t k, int slotA, int slotB, int par) {
+      constexpr int I = decltype(Ic)::value;
+      const int64_t j = k * S + I;
+      const int jp = (int)(j & 1);
+      const int64_t t = nch * S + S - j;  // step reversed in this phase
+      const bool act = j >= S + 1 && j <= nch * S + S;
+      const bool fin = j == jlast;
+      // dk and df of the previous phase's step: per-wave partials summed by wave 0
+      if (wr == 0 && j >= S + 2 && j <= jlast) {
+        const int64_t tp = t + 1;
+        if (tp < T) {
+          if (g == 0 && row_ok) {
+            Real s = 0;
+#pragma unroll
+            for (int i = 0; i < 4 * NW; ++i) s += sm.rk[jp ^ 1][li][i];
+            ((Real*)a.dk)[(tok0 + tp * N) * K + row] = s;
+          }
+          if (lane == 0) {
+            Real s = 0;
+#pragma unroll
+            for (int i = 0; i < 4 * NW; ++i) s += sm.rf[jp ^ 1][i];
+            df_part[slab * tok_stride + tok0 + tp * N] = s;
+          }
+        }
+      }
+      if (act || fin) {
+        // C = f R + D W^T of step t + 1 (other waves' D tiles from phase j - 1)
+        Real db[NS];
+#pragma unroll
+        for (int q0 = 0; q0 < VT; ++q0) {
+          const R4 t4 = q0 < TPW ? Dp[q0] : sm.xd[jp ^ 1][(q0 + TPW * wr) % VT][lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) db[4 * q0 + r] = t4[r];
+        }
+        R4 acc[TPW];
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) acc[p] = fR[p];
+#pragma unroll
+        for (int s0 = 0; s0 < NS; ++s0)
+#pragma unroll
+          for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wop[p][s0], db[s0], acc[p]);
+        // read the accumulators before the branch below (see the forward role)
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) pin_vec(acc[p]);
+        if (fin) {
+          if (a.dH0 && row_ok) {
+#pragma unroll
+            for (int p = 0; p < TPW; ++p)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int col = col_of(p, r);
+                if (col < V) ((Real*)a.dH0)[state_base + col] = acc[p][r];
+              }
+          }
+        } else {
+          // phase I >= 1 reverses step (cF + 1) S + S - I, phase 0 step (cF + 2) S
+          constexpr int tt = I >= 1 ? S - I : 0;
+          const Real* stp = &sm.st[I >= 1 ? slotA : slotB][tt * E];
+          const Real f = stp[OFF_F];
+          const Real omf = Real(1) - f;
+          const Real qli = stp[OFF_Q + li];
+          const Real kli = stp[li];
+          const int pos = (par * S - I) & (M - 1);  // ring position of t
+          Real dfp = 0, dkp = 0;
+          R4 u[TPW];
+#pragma unroll
+          for (int p = 0; p < TPW; ++p) {
+            const R4 hp = sm.hr[pos][wr * TPW + p][lane];
+            u[p] = cols4(stp + OFF_U + (wr * TPW + p) * 16, g);
+            const R4 vv = cols4(stp + OFF_V + (wr * TPW + p) * 16, g);
+            R4 D;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const Real rc = rcn[p][r];
+              const Real z = fma_r(Real(-2), rc, Real(1));
+              const Real sech2 = Real(4) * rc * (Real(1) - rc);
+              const Real Rm = fma_r(qli, u[p][r], acc[p][r]);
+              D[r] = omf * Rm * sech2;
+              fR[p][r] = f * Rm;
+              dfp = fma_r(Rm, hp[r] - z, dfp);
+              dkp = fma_r(D[r], vv[r], dkp);
+            }
+            Dp[p] = D;
+            sm.xd[jp][wr * TPW + p][lane] = D;
+          }
+          sm.rk[jp][li][wr * 4 + g] = dkp;
+          dfp = row16_sum(dfp);
+          if (li == 0) sm.rf[jp][wr * 4 + g] = dfp;
+          // dv_t = D^T k over this slab's rows (+ w_r (.) u when the slab is the whole head)
+#pragma unroll
+          for (int p = 0; p < TPW; ++p) {
+            const R4 s = row16_sum_x4(Dp[p], kli);
+            if (li == 0 && t < T) {
+              const int64_t tok = tok0 + t * N;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int col = col_of(p, r);
+                if (col < V) {
+                  if (nslab == 1)
+                    ((Real*)a.dv)[tok * V + col] = fma_r(wrc[p][r], u[p][r], s[r]);
+                  else
+                    dv_part[slab * tok_stride * V + tok * V + col] = s[r];
+                }
+              }
+            }
+          }
+          // rc of step t - 1, for the next phase
+          if (t >= 1) {
+#pragma unroll
+            for (int p = 0; p < TPW; ++p) rcn[p] = sm.zr[(pos - 1) & (M - 1)][wr * TPW + p][lane];
+          }
+        }
+      }
+      if (j == S) {  // rc of the first reversed step
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) rcn[p] = sm.zr[(nch * S - 1) & (M - 1)][wr * TPW + p][lane];
+      }
+    };
+
+    for (int64_t k = 0; k < nper; ++k) {
+      const int64_t cF = nch - 1 - k;  // chunk the forward role recomputes
+      const bool stage = cF >= 1;
+      if (stage) stage_load(cF - 1);
+      const int64_t cA = cF + 1, cB = cF + 2;
+      const int slotA = cA >= 0 ? (int)(cA % NSLOT) : 0;
+      const int slotB = cB >= 0 ? (int)(cB % NSLOT) : 0;
+      // step (cF + 1) S + S - I sits at ring position ((cF + 2) S - I) mod 2 S
+      const int par = (int)(cB & 1);
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        ((phase(std::integral_constant<int, I>{}, k, slotA, slotB, par),
+          (I == S - 1 && stage ? stage_store(cF - 1) : void()), __syncthreads()),
+         ...);
+      }(std::make_integer_sequence<int, S>{});
+    }
+  }
+}
+
+// Chunk-start states at every multiple of S, recomputed from the forward's
+// checkpoints when C does not divide S.  One workgroup per (slab, checkpoint
+// interval): the intervals are independent, so they all run at once and the
+// matrix units stay busy in spite of the step-to-step latency.  The step is
+// the forward kernel's, operation for operation, so the states are bitwise
+// the ones the forward produced.
+template <typename InT, typename Real, int VT>
+__global__ void __launch_bounds__((BwdShape<Real, VT>::NW * 64))
+    m2rnn_bwd_starts_kernel(BwdArgs a, int64_t nch, int64_t id0, Real* __restrict__ out) {
+  using Sh = BwdShape<Real, VT>;
+  constexpr int S = BwdTraits<Real, VT>::S;
+  using R4 = typename Vec4<Real>::type;
+  constexpr int TPW = Sh::TPW, NS = Sh::NS;
+  __shared__ R4 xb[2][VT][64];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, g = lane >> 4, li = lane & 15;
+  const int64_t units = a.B * a.N * a.nslab;
+  const int64_t id = id0 + blockIdx.x;
+  const int unit = (int)(id % units);
+  const int64_t c = id / units;  // checkpoint interval
+  const int nslab = a.nslab;
+  const int slab = unit % nslab;
+  const int bn = unit / nslab;
+  const int64_t T = a.T, N = a.N, K = a.K, V = a.V, C = a.C;
+  const int n = (int)(bn % N);
+  const int b = (int)(bn / N);
+  const int row = slab * 16 + li;
+  const bool row_ok = row < K;
+  const int64_t nck = (T + C - 1) / C;
+  const int64_t t0 = c * C;
+  const int64_t xmax = (nch - 1) * S;  // last chunk start
+  if (t0 > xmax) return;               // uniform over the workgroup
+  const int64_t tend = (t0 + C < T ? t0 + C : T) < xmax ? (t0 + C < T ? t0 + C : T) : xmax;
+  const int64_t tok0 = (int64_t)b * T * N + n;
+  const InT* __restrict__ kp = (const InT*)a.k;
+  const InT* __restrict__ vp = (const InT*)a.v;
+  const Real* __restrict__ fp = (const Real*)a.f;
+  const Real* __restrict__ Wp = (const Real*)a.W;
+
+  Real wa[TPW][NS];
 #pragma unroll
   for (int p = 0; p < TPW; ++p) {
     const int col = (w * TPW + p) * 16 + li;
@@ -114,284 +682,81 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
     for (int s0 = 0; s0 < NS; ++s0) {
       const int s = (s0 + 4 * TPW * w) % NS;
       const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
-      const bool ok = col < V && l < V;
-      wf[p][s0] = ok ? Wp[((int64_t)n * V + l) * V + col] : Real(0);
-      wb[p][s0] = ok ? Wp[((int64_t)n * V + col) * V + l] : Real(0);
+      wa[p][s0] = (col < V && l < V) ? Wp[((int64_t)n * V + l) * V + col] : Real(0);
     }
   }
-
-  auto slot_at = [&](int64_t s, int p) -> R4& {
-    return slots[((size_t)s * VT + (w * TPW + p)) * 64 + lane];
-  };
-  auto col_of = [&](int p, int r) { return (w * TPW + p) * 16 + acc_m<Real>(g, r); };
-  const int64_t state_base = (((int64_t)b * N + n) * K + row) * V;
-
-  // state gradient C_T = dHT
-  R4 Cg[TPW];
+  const Real* ck = (const Real*)a.ckpt + (((int64_t)bn * nck + c) * K + (row_ok ? row : 0)) * V;
+  Real hb[NS];
+  R4 h[TPW];
 #pragma unroll
-  for (int p = 0; p < TPW; ++p) {
+  for (int q0 = 0; q0 < VT; ++q0) {
+    const int q = (q0 + TPW * w) % VT;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int col = col_of(p, r);
-      Cg[p][r] = (a.dHT && row_ok && col < V) ? ((const Real*)a.dHT)[state_base + col] : Real(0);
+      const int col = 16 * q + acc_m<Real>(g, r);
+      hb[4 * q0 + r] = load_sel<Real>(ck, col < V ? col : 0, row_ok && col < V);
     }
   }
-  R4 dWacc[TPW][VT];
 #pragma unroll
   for (int p = 0; p < TPW; ++p)
 #pragma unroll
-    for (int jt = 0; jt < VT; ++jt) dWacc[p][jt] = R4{0, 0, 0, 0};
-
-  const int64_t nck = (T + C - 1) / C;
-  for (int64_t c = nck - 1; c >= 0; --c) {
-    const int64_t t0 = c * C;
-    const int64_t Lc = (T - t0) < C ? (T - t0) : C;
-    __syncthreads();  // previous interval's LDS reads are done
-
-    // ---------------- 1. recompute the interval from ckpt[c]
-    R4 h[TPW];
-    const Real* ck = (const Real*)a.ckpt + ((((int64_t)b * N + n) * nck + c) * K + row) * V;
+    for (int r = 0; r < 4; ++r) h[p][r] = hb[4 * p + r];
+  auto write_start = [&](int64_t x) {
+    if (!row_ok) return;
+    Real* dst = out + (((int64_t)bn * nch + x / S) * K + row) * V;
+#pragma unroll
+    for (int p = 0; p < TPW; ++p)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int col = (w * TPW + p) * 16 + acc_m<Real>(g, r);
+        if (col < V) dst[col] = h[p][r];
+      }
+  };
+  if ((t0 & (S - 1)) == 0) write_start(t0);
+  const Real a_mask = g == 0 ? Real(1) : Real(0);
+  for (int64_t t = t0; t < tend; ++t) {
+    const int64_t tok = tok0 + t * N;
+    const Real f = fp[tok];
+    const Real kli = load_sel<Real>(kp, tok * K + (row_ok ? row : 0), row_ok);
+    R4 acc[TPW];
+#pragma unroll
+    for (int p = 0; p < TPW; ++p) acc[p] = R4{0, 0, 0, 0};
+#pragma unroll
+    for (int s0 = 0; s0 < 4 * TPW; ++s0)
+#pragma unroll
+      for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wa[p][s0], hb[s0], acc[p]);
+#pragma unroll
+    for (int p = 0; p < TPW; ++p) {
+      const int col = (w * TPW + p) * 16 + li;
+      const Real vv = load_sel<Real>(vp, tok * V + (col < V ? col : 0), col < V);
+      acc[p] = mfma_16x16x4(vv * a_mask, kli, acc[p]);
+    }
+#pragma unroll
+    for (int s0 = 4 * TPW; s0 < NS; ++s0)
+#pragma unroll
+      for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wa[p][s0], hb[s0], acc[p]);
+    const Real omf = Real(1) - f;
+    const Real m2omf = Real(-2) * omf;
+    const int P = (int)(t & 1);
 #pragma unroll
     for (int p = 0; p < TPW; ++p) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int col = col_of(p, r);
-        h[p][r] = (row_ok && col < V) ? ck[col] : Real(0);
-      }
-      slot_at(0, p) = h[p];
+      for (int r = 0; r < 4; ++r)
+        h[p][r] = fma_r(m2omf, sigmoid_neg2x(acc[p][r]), fma_r(f, h[p][r], omf));
+      xb[P][w * TPW + p][lane] = h[p];
     }
-    Real hb[NS];
-    {
-      const int ib = (int)((t0 + 1) & 1);
+    __syncthreads();
+    if (((t + 1) & (S - 1)) == 0) write_start(t + 1);
 #pragma unroll
-      for (int p = 0; p < TPW; ++p) sm.xb[ib][w * TPW + p][lane] = h[p];
-      __syncthreads();
+    for (int q0 = TPW; q0 < VT; ++q0) {
+      const R4 t4 = xb[P][(q0 + TPW * w) % VT][lane];
 #pragma unroll
-      for (int q0 = 0; q0 < VT; ++q0) {
-        const R4 t4 = q0 < TPW ? h[q0] : sm.xb[ib][(q0 + TPW * w) % VT][lane];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hb[4 * q0 + r] = t4[r];
-      }
+      for (int r = 0; r < 4; ++r) hb[4 * q0 + r] = t4[r];
     }
-    // inputs of one recompute step (issued a step ahead of their use)
-    struct FwdIn {
-      Real kv, ft;
-      R4 vv[TPW];
-    };
-    auto load_fwd_in = [&](int64_t t) {
-      FwdIn in;
-      const int64_t tok = ((int64_t)b * T + clamp_idx(t, T - 1)) * N + n;
-      in.kv = load_sel<Real>(kp, tok * K + rowc, row_ok);
-      in.ft = fp[tok];
 #pragma unroll
-      for (int p = 0; p < TPW; ++p)
+    for (int p = 0; p < TPW; ++p)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int col = col_of(p, r);
-          in.vv[p][r] = load_sel<Real>(vp, tok * V + clamp_idx(col, V - 1), col < V);
-        }
-      return in;
-    };
-    FwdIn fin = load_fwd_in(t0);
-    for (int64_t tt = 0; tt < Lc; ++tt) {
-      const int64_t t = t0 + tt;
-      const FwdIn cur = fin;
-      fin = load_fwd_in(t + 1);
-      R4 acc[TPW];
-#pragma unroll
-      for (int p = 0; p < TPW; ++p) acc[p] = cur.kv * cur.vv[p];
-#pragma unroll
-      for (int s0 = 0; s0 < NS; ++s0) {
-#pragma unroll
-        for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wf[p][s0], hb[s0], acc[p]);
-      }
-      const Real ft = cur.ft;
-      const Real omf = Real(1) - ft;
-#pragma unroll
-      for (int p = 0; p < TPW; ++p) {
-        R4 z;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          z[r] = tanh_fast(acc[p][r]);
-          h[p][r] = ft * h[p][r] + omf * z[r];
-        }
-        slot_at(C + 1 + tt, p) = z;
-        slot_at(tt + 1, p) = h[p];
-      }
-      const int xbuf = (int)(t & 1);
-#pragma unroll
-      for (int p = 0; p < TPW; ++p) sm.xb[xbuf][w * TPW + p][lane] = h[p];
-      __syncthreads();
-#pragma unroll
-      for (int q0 = TPW; q0 < VT; ++q0) {
-        const R4 t4 = sm.xb[xbuf][(q0 + TPW * w) % VT][lane];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hb[4 * q0 + r] = t4[r];
-      }
-#pragma unroll
-      for (int p = 0; p < TPW; ++p)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hb[4 * p + r] = h[p][r];
-    }
-    __syncthreads();  // recompute exchange reads are done before xb is reused
-
-    // ---------------- 2. reverse scan over the interval
-    // inputs of one reverse step (issued a step ahead of their use)
-    struct BwdIn {
-      Real kv, qv, ft;
-      R4 vv[TPW], uu[TPW], Hp[TPW], Z[TPW];
-    };
-    auto load_bwd_in = [&](int64_t tt) {
-      BwdIn in;
-      const int64_t ttc = tt < 0 ? 0 : tt;
-      const int64_t tok = ((int64_t)b * T + t0 + ttc) * N + n;
-      in.kv = load_sel<Real>(kp, tok * K + rowc, row_ok);
-      in.qv = load_sel<Real>(qp, tok * K + rowc, row_ok);
-      in.ft = fp[tok];
-#pragma unroll
-      for (int p = 0; p < TPW; ++p) {
-        in.Hp[p] = slot_at(ttc, p);
-        in.Z[p] = slot_at(C + 1 + ttc, p);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int col = col_of(p, r);
-          const int64_t i = tok * V + clamp_idx(col, V - 1);
-          in.vv[p][r] = load_sel<Real>(vp, i, col < V);
-          in.uu[p][r] = load_sel<Real>(dyp, i, col < V);
-        }
-      }
-      return in;
-    };
-    R4 Hc[TPW];  // H_t, the state after the step being reversed
-#pragma unroll
-    for (int p = 0; p < TPW; ++p) Hc[p] = slot_at(Lc, p);
-    BwdIn bin = load_bwd_in(Lc - 1);
-    for (int64_t tt = Lc - 1; tt >= 0; --tt) {
-      const int64_t t = t0 + tt;
-      const int64_t tok = ((int64_t)b * T + t) * N + n;
-      const BwdIn cur = bin;
-      bin = load_bwd_in(tt - 1);
-      const Real kv = cur.kv, qv = cur.qv, ft = cur.ft;
-      R4 R[TPW], D[TPW];
-      Real dqp = 0, dkp = 0, dfp = 0;
-#pragma unroll
-      for (int p = 0; p < TPW; ++p) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const Real u = cur.uu[p][r];
-          const Real z = cur.Z[p][r];
-          R[p][r] = Cg[p][r] + qv * u;
-          dqp += Hc[p][r] * u;
-          D[p][r] = (Real(1) - ft) * R[p][r] * (Real(1) - z * z);
-          dfp += R[p][r] * (cur.Hp[p][r] - z);
-          dkp += D[p][r] * cur.vv[p][r];
-        }
-      }
-      const int buf = (int)(t & 1);
-#pragma unroll
-      for (int p = 0; p < TPW; ++p) {
-        sm.xd[buf][w * TPW + p][lane] = D[p];
-        sm.xb[buf][w * TPW + p][lane] = cur.Hp[p];
-        Hc[p] = cur.Hp[p];  // H_{t-1} is the next (earlier) step's H_t
-      }
-      dqp = cross_row_sum(dqp);
-      dkp = cross_row_sum(dkp);
-      dfp = cross_row_sum(row16_sum(dfp));
-      if (g == 0) {
-        sm.red[buf][0][w][li] = dqp;
-        sm.red[buf][1][w][li] = dkp;
-      }
-      if (lane == 0) sm.redf[buf][w] = dfp;
-      // dv_t = D^T k over this slab's rows (+ w_r (.) u when the slab is the whole head)
-#pragma unroll
-      for (int p = 0; p < TPW; ++p) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const Real s = row16_sum(D[p][r] * kv);
-          const int col = col_of(p, r);
-          if (li == 0 && col < V) {
-            if (nslab == 1) {
-              ((Real*)a.dv)[tok * V + col] = s + wrp[(int64_t)n * V + col] * cur.uu[p][r];
-            } else {
-              dv_part[slab * tok_stride * V + tok * V + col] = s;
-            }
-          }
-        }
-      }
-      __syncthreads();
-      if (w == 0) {
-        if (lane < 32) {
-          const int which = lane >> 4;
-          Real s = 0;
-#pragma unroll
-          for (int ww = 0; ww < NW; ++ww) s += sm.red[buf][which][ww][li];
-          if (row_ok) ((Real*)(which ? a.dk : a.dq))[tok * K + row] = s;
-        } else if (lane == 32) {
-          Real s = 0;
-#pragma unroll
-          for (int ww = 0; ww < NW; ++ww) s += sm.redf[buf][ww];
-          df_part[slab * tok_stride + tok] = s;
-        }
-      }
-      // C_{t-1} = f R + D W^T
-      Real db[NS];
-#pragma unroll
-      for (int q0 = 0; q0 < VT; ++q0) {
-        const R4 t4 = q0 < TPW ? D[q0] : sm.xd[buf][(q0 + TPW * w) % VT][lane];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) db[4 * q0 + r] = t4[r];
-      }
-#pragma unroll
-      for (int p = 0; p < TPW; ++p) Cg[p] = ft * R[p];
-#pragma unroll
-      for (int s0 = 0; s0 < NS; ++s0) {
-#pragma unroll
-        for (int p = 0; p < TPW; ++p) Cg[p] = mfma_16x16x4(wb[p][s0], db[s0], Cg[p]);
-      }
-      // dW += H_{t-1}^T D over the slab's rows
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        // element (row 4 kk + g, column 16 c + li) of a tile in the exchange
-        // buffer sits in lane 16 acc_g(li) + row, element acc_r(li)
-        const int idx = 16 * acc_g<Real>(li) + 4 * kk + g;
-        const int rr = acc_r<Real>(li);
-        Real aop[TPW];
-#pragma unroll
-        for (int p = 0; p < TPW; ++p)
-          aop[p] = ((const Real*)&sm.xb[buf][w * TPW + p][0])[idx * 4 + rr];
-#pragma unroll
-        for (int jt = 0; jt < VT; ++jt) {
-          const Real bop = ((const Real*)&sm.xd[buf][jt][0])[idx * 4 + rr];
-#pragma unroll
-          for (int p = 0; p < TPW; ++p) dWacc[p][jt] = mfma_16x16x4(aop[p], bop, dWacc[p][jt]);
-        }
-      }
-    }
-  }
-
-  if (a.dH0) {
-#pragma unroll
-    for (int p = 0; p < TPW; ++p) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int col = col_of(p, r);
-        if (row_ok && col < V) ((Real*)a.dH0)[state_base + col] = Cg[p][r];
-      }
-    }
-  }
-  // this slab's share of dW: lane holds dW[16 c + m(g, r)][16 jt + li]
-  Real* dWp = ws + L.dW_part + (((size_t)b * nslab + slab) * N + n) * V * V;
-#pragma unroll
-  for (int p = 0; p < TPW; ++p) {
-#pragma unroll
-    for (int jt = 0; jt < VT; ++jt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int l = (w * TPW + p) * 16 + acc_m<Real>(g, r);
-        const int j = jt * 16 + li;
-        if (l < V && j < V) dWp[(int64_t)l * V + j] = dWacc[p][jt][r];
-      }
-    }
+      for (int r = 0; r < 4; ++r) hb[4 * p + r] = h[p][r];
   }
 }
 
@@ -531,17 +896,37 @@ static unsigned grid_for(int64_t total) {
 }
 
 template <typename InT, typename Real, int VT>
-static hipError_t launch_bwd_vt(const BwdArgs& a, hipStream_t stream) {
+static hipError_t launch_bwd_vt(const BwdArgs& a0, hipStream_t stream) {
   using Tr = BwdTraits<Real, VT>;
-  static_assert(sizeof(BwdSmem<Real, VT, Tr::NW>) <= 160 * 1024, "LDS budget");
-  const BwdWorkspace L = bwd_workspace_layout(a.B, a.T, a.N, a.K, a.V, a.C);
+  static_assert(sizeof(BwdSmem<Real, VT>) <= kLdsBytes, "LDS budget");
+  BwdArgs a = a0;
+  const BwdWorkspace L =
+      bwd_workspace_layout(a.B, a.T, a.N, a.K, a.V, a.C, sizeof(Real) == 8 ? kF64 : kF32);
+  Real* ws = (Real*)a.ws;
   const int64_t units = a.B * a.N * a.nslab;
+  const int64_t nck = (a.T + a.C - 1) / a.C;
+  hipError_t err;
+  if (L.subck_needed) {
+    // one workgroup per (slab, checkpoint interval), in launches of at most 2^24 workgroups
+    const int64_t total = units * nck;
+    for (int64_t id0 = 0; id0 < total; id0 += (int64_t)1 << 24) {
+      const int64_t cnt = total - id0 < ((int64_t)1 << 24) ? total - id0 : ((int64_t)1 << 24);
+      hipLaunchKernelGGL((m2rnn_bwd_starts_kernel<InT, Real, VT>), dim3((unsigned)cnt),
+                         dim3(Tr::NW * 64), 0, stream, a, L.nch, id0, ws + L.subck);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    a.cks = ws + L.subck;
+    a.cks_count = L.nch;
+    a.cks_step = 1;
+  } else {
+    a.cks = a.ckpt;
+    a.cks_count = nck;
+    a.cks_step = Tr::S / a.C;
+  }
   hipLaunchKernelGGL((m2rnn_bwd_kernel<InT, Real, VT>), dim3((unsigned)units), dim3(Tr::NT), 0,
                      stream, a, L);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if ((err = hipGetLastError()) != hipSuccess) return err;
 
-  Real* ws = (Real*)a.ws;
   const int64_t tokens = a.B * a.T * a.N;
   hipLaunchKernelGGL((m2rnn_bwd_token_kernel<Real>), dim3(grid_for(tokens)), dim3(256), 0, stream,
                      tokens, a.N, a.nslab, a.gate_kind, ws + L.df_part, (const Real*)a.f,

@@ -93,6 +93,10 @@ template <typename Real>
 __device__ __forceinline__ void pin_values(Real& a, Real& b, Real& c, Real& d) {
   asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }
+// The same for a 4-vector (e.g. MFMA accumulators, which this moves into VGPRs
+// at this point of the program).
+__device__ __forceinline__ void pin_vec(f32x4& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin_vec(f64x4& x) { asm volatile("" : "+v"(x)); }
 
 __device__ __forceinline__ float fma_r(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
 __device__ __forceinline__ double fma_r(double a, double b, double c) { return __builtin_fma(a, b, c); }

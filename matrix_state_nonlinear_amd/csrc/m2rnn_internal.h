@@ -68,6 +68,11 @@ struct BwdArgs {
   void* dbeta;       // may be null
   void* dH0;         // may be null
   void* ws;          // workspace base
+  // Chunk-start states of the reverse sweep, [B, N, cks_count, K, V]: chunk c
+  // (steps [cS, cS + S)) starts from entry c * cks_step.  Either the forward's
+  // checkpoints (when C divides S) or states recomputed into the workspace.
+  const void* cks;
+  int64_t cks_count, cks_step;
   int64_t B, T, N, K, V, C;
   int nslab;
   int gate_kind;
@@ -76,8 +81,10 @@ struct BwdArgs {
 // Workspace layout of the backward: offsets in elements of the state type,
 // each region aligned to 64 elements.
 struct BwdWorkspace {
-  size_t states;      // per unit: (2 C + 1) slots of one slab's state tiles
-  size_t slot_elems;  // elements of one slot (VT * 64 lanes * 4)
+  int period;         // S: steps per chunk of the reverse sweep (depends on V and dtype)
+  int64_t nch;        // ceil(T / S)
+  bool subck_needed;  // C does not divide S: chunk starts are recomputed first
+  size_t subck;       // [B, N, nch, K, V] chunk-start states (subck_needed only)
   size_t dv_part;     // [nslab, B, T, N, V]  (nslab > 1 only)
   size_t df_part;     // [nslab, B, T, N]
   size_t dW_part;     // [B * nslab, N, V, V]
@@ -86,7 +93,7 @@ struct BwdWorkspace {
   size_t total_elems;
 };
 BwdWorkspace bwd_workspace_layout(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V,
-                                  int64_t C);
+                                  int64_t C, int state_dtype);
 
 hipError_t launch_gates(int64_t B, int64_t T, int64_t N, int gate_kind, int dtype,
                         const void* logit, const void* alpha, const void* beta, void* f,

@@ -1,0 +1,148 @@
+"""Host-side check of the backward kernel's phase schedule (no GPU).
+
+m2rnn_bwd runs two wave roles in lock step, one barrier per phase: the forward
+role recomputes chunk cF = nch - 1 - k of S steps in period k and writes each
+step's state and tanh term into LDS rings of 2 S entries; the reverse role
+walks the previously recomputed chunk backwards one phase behind, reading
+those rings, a staging ring of input chunks and a parity-buffered D exchange.
+This test replays, phase by phase, the ring positions and slots exactly as the
+kernel computes them (same expressions as m2rnn_bwd.hip) and checks that
+
+* every read finds the item it needs, written in an earlier phase;
+* no location is read and written in the same phase (no barrier between);
+* the forward role recomputes, and the reverse role reverses, every step of
+  the padded sequence exactly once, in the required orders.
+"""
+import pytest
+
+
+def replay(S, nch):
+    M = 2 * S
+    NSLOT = 3 if S >= 2 else 4
+    jlast = nch * S + S + 1
+    nper = jlast // S + 1
+    store = {}          # (buffer, position) -> (item, phase written)
+    errors = []
+    fwd_steps, rev_steps = [], []
+
+    # prologue: staging of the last chunk, before the first barrier
+    store[("st", (nch - 1) % NSLOT)] = (("chunk", nch - 1), -1)
+    for k in range(nper):
+        cF = nch - 1 - k
+        rec = cF >= 0
+        slot = cF % NSLOT if rec else 0
+        hbase = (cF & 1) * S if rec else 0
+        cA, cB = cF + 1, cF + 2
+        slotA = cA % NSLOT if cA >= 0 else 0
+        slotB = cB % NSLOT if cB >= 0 else 0
+        par = cB & 1
+        for I in range(S):
+            j = k * S + I
+            jp = j & 1
+            reads, writes = [], []
+            # ---------------- forward role
+            if rec:
+                t = cF * S + I
+                fwd_steps.append(t)
+                reads.append(("st", slot, ("chunk", t // S)))
+                if I > 0:
+                    reads.append(("hr", hbase + I, ("S", t)))
+                writes.append(("hr", (hbase + I + 1) & (M - 1), ("S", t + 1)))
+                writes.append(("zr", hbase + I, ("Z", t)))
+            if S + 2 <= j <= jlast:      # dW from the reverse role's previous step
+                reads.append(("xd", jp ^ 1, ("D", nch * S + S - (j - 1))))
+            if S + 1 <= j <= nch * S + S:   # dW A-operands of this phase's reverse step
+                reads.append(("hr", (nch * S + S - j) & (M - 1), ("S", nch * S + S - j)))
+            if j == nch * S:
+                writes.append(("hr", 0, ("S", 0)))
+            # ---------------- reverse role
+            t = nch * S + S - j
+            act = S + 1 <= j <= nch * S + S
+            fin = j == jlast
+            if act or fin:
+                reads.append(("xd", jp ^ 1, ("D", t + 1) if j > S + 1 else ("D", "zero")))
+            if act:
+                rev_steps.append(t)
+                tt = S - I if I >= 1 else 0
+                sl = slotA if I >= 1 else slotB
+                if tt != t % S:
+                    errors.append(f"j={j}: staged step index {tt} != {t % S}")
+                reads.append(("st", sl, ("chunk", t // S)))
+                pos = (par * S - I) & (M - 1)
+                if pos != t % M:
+                    errors.append(f"j={j}: ring position {pos} != {t % M}")
+                reads.append(("hr", pos, ("S", t)))
+                writes.append(("xd", jp, ("D", t)))
+                if t >= 1:
+                    reads.append(("zr", (pos - 1) & (M - 1), ("Z", t - 1)))
+            if j == S:
+                reads.append(("zr", (nch * S - 1) & (M - 1), ("Z", nch * S - 1)))
+            # ---------------- staging of chunk cF - 1 at the period's last phase
+            if I == S - 1 and cF >= 1:
+                writes.append(("st", (cF - 1) % NSLOT, ("chunk", cF - 1)))
+            # ---------------- checks
+            wpos = {(b, p) for b, p, _ in writes}
+            for b, p, item in reads:
+                if (b, p) in wpos:
+                    errors.append(f"j={j}: {b}[{p}] read ({item}) and written in one phase")
+                have = store.get((b, p))
+                if item == ("D", "zero"):
+                    if have is not None:
+                        errors.append(f"j={j}: {b}[{p}] should still hold zeros")
+                    continue
+                if have is None or have[0] != item or have[1] >= j:
+                    errors.append(f"j={j}: {b}[{p}] wants {item}, holds {have}")
+            for b, p, item in writes:
+                store[(b, p)] = (item, j)
+    return errors, fwd_steps, rev_steps
+
+
+@pytest.mark.parametrize("S", [1, 2, 4, 8])
+@pytest.mark.parametrize("nch", [1, 2, 3, 4, 5, 9, 16])
+def test_backward_phase_schedule(S, nch):
+    errors, fwd, rev = replay(S, nch)
+    assert not errors, errors[:5]
+    Tp = nch * S
+    # forward role: chunks last to first, each chunk's steps in time order
+    assert fwd == [c * S + i for c in range(nch - 1, -1, -1) for i in range(S)]
+    # reverse role: every step once, from the last to the first
+    assert rev == list(range(Tp - 1, -1, -1))
+
+
+def test_schedule_replay_detects_short_rings():
+    """The replay must catch rings one chunk long (too short) and pass 2 S."""
+    for S in (2, 4, 8):
+        assert replay_with_ring(S, 5, ring=S)
+        assert not replay_with_ring(S, 5, ring=2 * S)
+
+
+def replay_with_ring(S, nch, ring):
+    """Like replay(), but with every ring position taken mod `ring`."""
+    errors = []
+    store = {}
+    jlast = nch * S + S + 1
+    for j in range(jlast + 1):
+        k, I = divmod(j, S)
+        cF = nch - 1 - k
+        reads, writes = [], []
+        if cF >= 0:
+            t = cF * S + I
+            if I > 0:
+                reads.append(("hr", t % ring, ("S", t)))
+            writes.append(("hr", (t + 1) % ring, ("S", t + 1)))
+            writes.append(("zr", t % ring, ("Z", t)))
+        t = nch * S + S - j
+        if S + 1 <= j <= nch * S + S:
+            reads.append(("hr", t % ring, ("S", t)))
+            if t >= 1:
+                reads.append(("zr", (t - 1) % ring, ("Z", t - 1)))
+        if j == nch * S:
+            writes.append(("hr", 0, ("S", 0)))
+        wpos = {(b, p) for b, p, _ in writes}
+        for b, p, item in reads:
+            have = store.get((b, p))
+            if (b, p) in wpos or have is None or have[0] != item:
+                errors.append((j, b, p, item))
+        for b, p, item in writes:
+            store[(b, p)] = (item, j)
+    return errors
