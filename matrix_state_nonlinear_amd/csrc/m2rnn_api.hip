@@ -17,8 +17,9 @@ bool sizes_ok(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V) {
   return elems < 4.0e18;
 }
 
-bool sizes_supported(int64_t B, int64_t N, int64_t K, int64_t V) {
+bool sizes_supported(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V) {
   if (K > 256 || V > 128) return false;
+  if (T >= ((int64_t)1 << 30)) return false;  // step indices are 32-bit in the kernels
   // one workgroup (at most 1024 threads) per slab: the grid stays below 2^32 threads
   return (double)B * (double)N * (double)num_slabs(K) < (double)(1 << 22);
 }
@@ -72,7 +73,7 @@ const char* m2rnn_status_string(int status) {
 
 size_t m2rnn_workspace_bytes(int is_bwd, int64_t B, int64_t T, int64_t n_heads, int64_t K,
                              int64_t V, int64_t C, int state_dtype) {
-  if (!sizes_ok(B, T, n_heads, K, V) || !sizes_supported(B, n_heads, K, V) ||
+  if (!sizes_ok(B, T, n_heads, K, V) || !sizes_supported(B, T, n_heads, K, V) ||
       !state_dtype_known(state_dtype) || (is_bwd && C < 1))
     return 0;
   return is_bwd ? bwd_ws_bytes(B, T, n_heads, K, V, C, state_dtype)
@@ -103,7 +104,7 @@ int m2rnn_fwd(int64_t B, int64_t T, int64_t n_heads, int64_t K, int64_t V, int i
   if (!in_dtype_known(in_dtype) || !state_dtype_known(state_dtype)) return M2RNN_ERR_INVALID_ARG;
   if (!k || !v || !q || !f || !W || !w_r || !y) return M2RNN_ERR_INVALID_ARG;
   if (ckpt && C < 1) return M2RNN_ERR_INVALID_ARG;
-  if (!sizes_supported(B, n_heads, K, V) || !dtypes_ok(in_dtype, state_dtype))
+  if (!sizes_supported(B, T, n_heads, K, V) || !dtypes_ok(in_dtype, state_dtype))
     return M2RNN_ERR_UNSUPPORTED;
   const size_t need = fwd_ws_bytes(B, T, n_heads, K, V, state_dtype);
   if (need && (!workspace || workspace_bytes < need)) return M2RNN_ERR_WORKSPACE;
@@ -134,7 +135,7 @@ int m2rnn_bwd(int64_t B, int64_t T, int64_t n_heads, int64_t K, int64_t V, int i
   } else {
     return M2RNN_ERR_INVALID_ARG;
   }
-  if (!sizes_supported(B, n_heads, K, V) || !dtypes_ok(in_dtype, state_dtype))
+  if (!sizes_supported(B, T, n_heads, K, V) || !dtypes_ok(in_dtype, state_dtype))
     return M2RNN_ERR_UNSUPPORTED;
   const size_t need = bwd_ws_bytes(B, T, n_heads, K, V, C, state_dtype);
   if (need && (!workspace || workspace_bytes < need)) return M2RNN_ERR_WORKSPACE;

@@ -15,28 +15,37 @@
 // so only dv, df and dW need sums across slabs, done by fixed-order reduction
 // kernels afterwards.
 //
-// Two wave roles per workgroup, one wave of each role on every SIMD:
+// Three wave roles per workgroup, one wave of each role on every SIMD, so the
+// three MFMA streams of a step share each SIMD's matrix unit and one role's
+// VALU and LDS work runs while another's MFMAs execute:
 //  * forward role: reruns the recurrence chunk by chunk (S steps per chunk,
 //    chunks from last to first), each chunk from its stored start state, with
 //    exactly the forward kernel's arithmetic.  Every step's state S_{t+1} and
-//    rc_t = 1 / (1 + e^{2 A_t}) (tanh(A_t) = 1 - 2 rc_t) go into LDS rings.
-//    The same waves form dq_t = S_{t+1} u_t and accumulate dW on MFMA from the
-//    D tiles the reverse role publishes.
+//    rc_t = 1 / (1 + e^{2 A_t}) (tanh(A_t) = 1 - 2 rc_t) go into LDS rings;
+//    it also forms the lane partials of dq_t = S_{t+1} u_t.
 //  * reverse role: walks the chunk recomputed in the previous period from its
 //    last step to its first, one phase behind, carrying C through the MFMA
-//    product (D W^T)^T = W D^T, and forms dk, dv and df.
-// Both roles finish one step per phase (one barrier per phase).  Sharing the
-// SIMDs, one role's VALU and LDS work overlaps the other's MFMA chain.  The
-// rings hold 2 S entries; with the reverse role one phase behind, no ring
-// entry, staging slot or exchange buffer is read and written in the same
-// phase (the schedule is checked step by step on the host in the tests).
+//    product (D W^T)^T = W D^T; it publishes D (plain and transposed) and the
+//    lane partials of dk and df.
+//  * side role: accumulates dW += S_t^T D_t on MFMA one phase behind the
+//    reverse role, finishes dq, dk, dv and df and stores them, and stages the
+//    next chunk's inputs and start state from HBM into LDS.
+// All roles finish one step per phase (one barrier per phase).  The rings hold
+// 2 S entries; no ring entry, staging slot or buffer is read and written in
+// the same phase (the schedule is replayed step by step on the host in the
+// tests).
 //
-// MFMA layouts.  Recompute: A = W^T (registers), B = S^T, exactly as in the
-// forward.  C-chain: A = W, B = D^T with the same contraction enumeration
+// MFMA layouts.  Recompute: A = W^T (registers), B = S^T, as in the forward.
+// C-chain: A = W, B = D^T with the forward's contraction enumeration
 // pi(s, g) = 16 (s / 4) + m(g, s % 4), so a wave's own D tiles feed the B
 // operand from registers and the others come through LDS.  dW: output tile
 // (l, j), A[l][i] = S_t[i][l], B[i][j] = D_t[i][j], contraction over the 16
-// slab rows in four k-steps; both operands are read transposed from LDS.
+// slab rows in four k-steps; B comes from the transposed D copy in one 16-byte
+// read per tile.
+//
+// The first read of an MFMA result is kept in the basic block of the MFMA
+// (the accumulators are pinned right after the chain): behind a branch, the
+// compiler did not insert the wait states such a read needs.
 
 #include <utility>
 
@@ -53,18 +62,26 @@ struct BwdShape {
   static constexpr int NW = VT <= 4 ? VT : VT / 2;         // waves per role
   static constexpr int TPW = VT / NW;                      // 16-column tiles per wave
   static constexpr int NS = 4 * VT;                        // MFMAs per tile per step
-  static constexpr int NT = 2 * 64 * NW;                   // threads (both roles)
+  static constexpr int NT = 3 * 64 * NW;                   // threads (three roles)
   static constexpr int E = (32 + 2 * VP + 1 + 3) / 4 * 4;  // staged values per step
   static constexpr size_t kTileset = (size_t)VT * 64 * 4 * sizeof(Real);
+  // the transposed D copy (16-byte dW operand reads) is kept for fp32; the
+  // fp64 instantiations read the operands from the plain copy to fit in LDS
+  static constexpr bool kXdt = sizeof(Real) == 4;
 };
 
+constexpr int bwd_slots(int S) { return S >= 4 ? 3 : (S == 2 ? 4 : 5); }
+
 // LDS of the backward for chunk length S: two rings of 2 S slab states, the
-// D exchange, the staging slots and the reduction partials.
+// D exchange (plain and transposed, double-buffered), two chunk-start
+// buffers, the staging slots and the reduction partials.
 template <typename Real, int VT>
 constexpr size_t bwd_smem_bytes(int S) {
   using Sh = BwdShape<Real, VT>;
-  return (size_t)(4 * S + 2) * Sh::kTileset + (size_t)(S >= 2 ? 3 : 4) * S * Sh::E * sizeof(Real) +
-         (size_t)(2 * 2 * 16 * 4 * Sh::NW + 2 * 4 * Sh::NW) * sizeof(Real);
+  return (size_t)(4 * S + (Sh::kXdt ? 6 : 4)) * Sh::kTileset +
+         (size_t)bwd_slots(S) * S * Sh::E * sizeof(Real) +
+         (size_t)(2 * 16 * 4 + 2 * 16 * 20 + 2 * 4 * Sh::NW) * sizeof(Real) +
+         (Sh::kXdt ? (size_t)2 * VT * 16 * 4 * sizeof(Real) : 0);
 }
 
 template <typename Real, int VT>
@@ -75,23 +92,30 @@ struct BwdTraits : BwdShape<Real, VT> {
                            : bwd_smem_bytes<Real, VT>(4) <= kLdsBytes ? 4
                            : bwd_smem_bytes<Real, VT>(2) <= kLdsBytes ? 2
                                                                       : 1;
-  static constexpr int M = 2 * S;                              // ring length
-  static constexpr int NSLOT = S >= 2 ? 3 : 4;                 // staging slots (chunks)
-  static constexpr int NLD = (S * Sh::E + Sh::NT - 1) / Sh::NT;  // staged values per thread
+  static constexpr int M = 2 * S;                    // ring length
+  static constexpr int NSLOT = bwd_slots(S);         // staging slots (chunks)
+  static constexpr int NX = 64 * Sh::NW;             // side-role threads
+  static constexpr int NLD = (S * Sh::E + NX - 1) / NX;         // staged values per thread
+  static constexpr int NCK = (16 * Sh::VP + NX - 1) / NX;       // start-state values per thread
 };
 
 template <typename Real, int VT>
 struct BwdSmem {
   using Tr = BwdTraits<Real, VT>;
   using R4 = typename Vec4<Real>::type;
-  R4 hr[Tr::M][VT][64];           // states S_x at ring position x mod M
-  R4 zr[Tr::M][VT][64];           // rc_t at ring position t mod M
-  R4 xd[2][VT][64];               // D tiles, double-buffered by phase parity
+  R4 hr[Tr::M][VT][64];            // states S_x at ring position x mod M
+  R4 zr[Tr::M][VT][64];            // rc_t at ring position t mod M
+  R4 xd[2][VT][64];                // D tiles in register layout, by phase parity
+  // D transposed: [tile][column][4 (row % 4) + row / 4] (fp32 only); rows of
+  // 20 so that both the scattered writes and the 16-byte reads of 8
+  // consecutive lanes spread over the banks
+  Real xdT[Tr::kXdt ? 2 : 1][VT][16][Tr::kXdt ? 20 : 1];
+  R4 ck[2][VT][64];                // chunk start states in register layout, by chunk parity
   // staged inputs of a chunk, per step: k[16] q[16] v[VP] dy[VP] f (padded)
   Real st[Tr::NSLOT][Tr::S * Tr::E];
-  Real rq[2][16][4 * Tr::NW];     // dq lane partials [row][wave, lane group]
-  Real rk[2][16][4 * Tr::NW];     // dk lane partials
-  Real rf[2][4 * Tr::NW];         // df partials [wave, lane group]
+  Real rq[2][16][4];               // dq per-wave row sums [row][wave] (at most 4 waves)
+  Real rk[2][16][20];              // dk lane partials [row][wave, lane group] (rows of 20)
+  Real rf[2][4 * Tr::NW];          // df partials [wave, lane group]
 };
 
 int bwd_period(int state_dtype, int64_t V) {
@@ -145,15 +169,16 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
     m2rnn_bwd_kernel(BwdArgs a, BwdWorkspace L) {
   using Tr = BwdTraits<Real, VT>;
   using R4 = typename Vec4<Real>::type;
-  constexpr int TPW = Tr::TPW, NS = Tr::NS, NW = Tr::NW, NT = Tr::NT, VP = Tr::VP;
-  constexpr int S = Tr::S, M = Tr::M, NSLOT = Tr::NSLOT, E = Tr::E, NLD = Tr::NLD;
+  constexpr int TPW = Tr::TPW, NS = Tr::NS, NW = Tr::NW, VP = Tr::VP;
+  constexpr int S = Tr::S, M = Tr::M, NSLOT = Tr::NSLOT, E = Tr::E;
+  constexpr int NX = Tr::NX, NLD = Tr::NLD, NCK = Tr::NCK;
   constexpr int OFF_Q = 16, OFF_V = 32, OFF_U = 32 + VP, OFF_F = 32 + 2 * VP;
   __shared__ BwdSmem<Real, VT> sm;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, g = lane >> 4, li = lane & 15;
-  const bool fwd_role = w < NW;
-  const int wr = fwd_role ? w : w - NW;
+  const int role = w / NW;  // 0 forward, 1 reverse, 2 side
+  const int wr = w - role * NW;
   const int unit = xcd_remap(blockIdx.x, gridDim.x);
   const int nslab = a.nslab;
   const int slab = unit % nslab;
@@ -163,100 +188,20 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
   const int b = (int)(bn / N);
   const int row = slab * 16 + li;
   const bool row_ok = row < K;
-  const int64_t nch = (T + S - 1) / S;
-  const int64_t jlast = nch * S + S + 1;        // last phase
-  const int64_t nper = jlast / S + 1;           // periods of S phases covering 0..jlast
+  // phase, step and chunk indices fit in 32 bits (T < 2^30)
+  const int T32 = (int)T;
+  const int nch = (T32 + S - 1) / S;
+  const int jlast = nch * S + S + 1;  // last phase
+  const int nper = jlast / S + 1;     // periods of S phases covering 0..jlast
   const int64_t tok0 = (int64_t)b * T * N + n;  // token (b, t, n) is tok0 + t N
-  const int64_t tok_stride = B * T * N;
   const int64_t state_base = ((int64_t)bn * K + row) * V;
-
-  const InT* __restrict__ kp = (const InT*)a.k;
-  const InT* __restrict__ vp = (const InT*)a.v;
-  const InT* __restrict__ qp = (const InT*)a.q;
-  const Real* __restrict__ fp = (const Real*)a.f;
   const Real* __restrict__ Wp = (const Real*)a.W;
-  const Real* __restrict__ dyp = (const Real*)a.dy;
-  Real* __restrict__ ws = (Real*)a.ws;
   auto col_of = [&](int p, int r) { return (wr * TPW + p) * 16 + acc_m<Real>(g, r); };
+  // the reverse role's step in phase j, and whether it takes one
+  auto rstep = [&](int j) { return nch * S + S - j; };
+  auto ractive = [&](int j) { return j >= S + 1 && j <= nch * S + S; };
 
-  // the first reverse step has no later step: its D exchange reads zeros
-  for (int i = tid; i < 2 * VT * 64; i += NT) (&sm.xd[0][0][0])[i] = R4{0, 0, 0, 0};
-
-  // ---- staging of one chunk's inputs.  Thread tid owns the staged values
-  // e = tid + m NT of a chunk (step e / E, field by e % E); its source offsets
-  // for chunk c are fixed offsets plus the step index times a stride.  Steps
-  // past T are padding: f = 1 and dy = 0 make them exact identities.
-  // Each value comes from an InT array (k, q, v) or a Real array (dy, f); both
-  // source pointers are kept valid, and the unused one is never selected.
-  const InT* ld_pin[NLD];
-  const Real* ld_pre[NLD];
-  int64_t ld_ts[NLD];
-  int ld_dst[NLD], ld_tt[NLD];
-  bool ld_in[NLD], ld_ok[NLD], ld_isf[NLD];
-#pragma unroll
-  for (int m = 0; m < NLD; ++m) {
-    const int e = tid + m * NT;
-    const int tt = e / E, r = e % E;
-    const InT* pin = kp;
-    const Real* pre = fp;
-    bool from_in = false, ok = false, isf = false;
-    int64_t ts = 0;
-    if (e < S * E) {
-      if (r < 32) {  // k (r < 16) or q, slab row r mod 16
-        const int rr = slab * 16 + (r & 15);
-        ok = rr < K;
-        from_in = true;
-        pin = (r < 16 ? kp : qp) + tok0 * K + (ok ? rr : 0);
-        ts = N * K;
-      } else if (r < OFF_U) {  // v, column r - 32
-        const int j = r - OFF_V;
-        ok = j < V;
-        from_in = true;
-        pin = vp + tok0 * V + (ok ? j : 0);
-        ts = N * V;
-      } else if (r < OFF_F) {  // dy, column r - 32 - VP
-        const int j = r - OFF_U;
-        ok = j < V;
-        pre = dyp + tok0 * V + (ok ? j : 0);
-        ts = N * V;
-      } else if (r == OFF_F) {  // f
-        ok = true;
-        isf = true;
-        pre = fp + tok0;
-        ts = N;
-      }
-    }
-    ld_pin[m] = pin;
-    ld_pre[m] = pre;
-    ld_ts[m] = ts;
-    ld_dst[m] = e < S * E ? e : -1;
-    ld_tt[m] = e < S * E ? tt : 0;
-    ld_in[m] = from_in;
-    ld_ok[m] = ok;
-    ld_isf[m] = isf;
-  }
-  Real stx[NLD];
-  auto stage_load = [&](int64_t c) {
-    const int64_t t0 = c * S;
-#pragma unroll
-    for (int m = 0; m < NLD; ++m) {
-      const int64_t t = t0 + ld_tt[m];
-      const bool tv = t < T;
-      const int64_t o = (tv ? t : T - 1) * ld_ts[m];
-      const Real xi = load_as<Real>(ld_pin[m] + (ld_in[m] ? o : 0));
-      const Real xr = ld_pre[m][ld_in[m] ? 0 : o];
-      const Real x = ld_in[m] ? xi : xr;
-      stx[m] = (ld_ok[m] && tv) ? x : (ld_isf[m] ? Real(1) : Real(0));
-    }
-  };
-  auto stage_store = [&](int64_t c) {
-    Real* dst = sm.st[(int)(c % NSLOT)];
-#pragma unroll
-    for (int m = 0; m < NLD; ++m)
-      if (ld_dst[m] >= 0) dst[ld_dst[m]] = stx[m];
-  };
-
-  if (fwd_role) {
+  if (role == 0) {
     // ================================================================ forward role
     // W^T as the A operand, rotated so this wave's own tiles come first
     Real wop[TPW][NS];
@@ -270,79 +215,58 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
         wop[p][s0] = (col < V && l < V) ? Wp[((int64_t)n * V + l) * V + col] : Real(0);
       }
     }
-    // start state of a chunk: all VT tiles of row `row`, in B-operand order
-    // (entry q0 holds tile (q0 + TPW wr) mod VT, so this wave's own tiles come first)
-    auto load_start = [&](int64_t c, R4 (&dst)[VT]) {
-      const Real* src =
-          (const Real*)a.cks + (((int64_t)bn * a.cks_count + c * a.cks_step) * K + (row_ok ? row : 0)) * V;
+    // wait for these loads before the loop (a wait left for inside the loop
+    // would also wait for the stores in flight there)
 #pragma unroll
-      for (int q0 = 0; q0 < VT; ++q0)
+    for (int p = 0; p < TPW; ++p)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int col = 16 * ((q0 + TPW * wr) % VT) + acc_m<Real>(g, r);
-          dst[q0][r] = load_sel<Real>(src, col < V ? col : 0, row_ok && col < V);
-        }
-    };
-    R4 ckc[VT], ckn[VT];
-    load_start(nch - 1, ckn);
+      for (int s0 = 0; s0 < NS; s0 += 4) pin_values(wop[p][s0], wop[p][s0 + 1], wop[p][s0 + 2], wop[p][s0 + 3]);
     R4 h[TPW];
     Real hb[NS];
-    R4 dWacc[TPW][VT];
-    Real aop[TPW][4];
 #pragma unroll
-    for (int p = 0; p < TPW; ++p) {
-      h[p] = R4{0, 0, 0, 0};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) aop[p][kk] = Real(0);
-#pragma unroll
-      for (int jt = 0; jt < VT; ++jt) dWacc[p][jt] = R4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int s0 = 0; s0 < NS; ++s0) hb[s0] = Real(0);
+    for (int p = 0; p < TPW; ++p) h[p] = R4{0, 0, 0, 0};
     const Real a_mask = g == 0 ? Real(1) : Real(0);
-    // transposed LDS element (row 4 kk + g, column li) of a tile: lane
-    // 16 acc_g(li) + 4 kk + g, element acc_r(li)
-    auto tidx = [&](int kk) { return (16 * acc_g<Real>(li) + 4 * kk + g) * 4 + acc_r<Real>(li); };
-
-    stage_load(nch - 1);
-    stage_store(nch - 1);
-    __syncthreads();
-
-    auto phase = [&](auto Ic, int64_t k, int64_t cF, bool rec, int slot, int hbase) {
-      constexpr int I = decltype(Ic)::value;
-      const int64_t j = k * S + I;
-      const int jp = (int)(j & 1);
-      // dq of the previous phase's step: the per-wave partials, summed by wave 0
-      if (wr == 0 && g == 0 && j >= 1 && j <= nch * S) {
-        const int64_t tp = I > 0 ? cF * S + I - 1 : (cF + 1) * S + S - 1;
-        if (tp < T && row_ok) {
-          Real s = 0;
+    // w_r of this lane's dv columns (completed here, see above); where a lane's
+    // four columns are consecutive (fp32) dv is written with one 16-byte store
+    Real wrc[TPW][4];
 #pragma unroll
-          for (int i = 0; i < 4 * NW; ++i) s += sm.rq[jp ^ 1][li][i];
-          ((Real*)a.dq)[(tok0 + tp * N) * K + row] = s;
-        }
+    for (int p = 0; p < TPW; ++p)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int col = col_of(p, r);
+        wrc[p][r] = col < V ? ((const Real*)a.w_r)[(int64_t)n * V + col] : Real(0);
       }
-      auto dw_mfma = [&]() {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int idx = tidx(kk);
-#pragma unroll
-          for (int jt = 0; jt < VT; ++jt) {
-            const Real bop = ((const Real*)&sm.xd[jp ^ 1][jt][0])[idx];
-#pragma unroll
-            for (int p = 0; p < TPW; ++p) dWacc[p][jt] = mfma_16x16x4(aop[p][kk], bop, dWacc[p][jt]);
-          }
-        }
-      };
+    for (int p = 0; p < TPW; ++p) pin_values(wrc[p][0], wrc[p][1], wrc[p][2], wrc[p][3]);
+    const bool dv_vec = sizeof(Real) == 4 && (V & 3) == 0;
+    // output pointers at token (b, t = 0, n); step t adds t N rows
+    Real* const dq_row = (Real*)a.dq + tok0 * K + row;
+    Real* const dv_tok = nslab == 1 ? (Real*)a.dv + tok0 * V
+                                    : (Real*)a.ws + L.dv_part + ((int64_t)slab * B * T * N + tok0) * V;
+    const int64_t NK = N * K, NV = N * V;
+
+    __syncthreads();  // prologue staging by the side role
+
+    auto phase = [&](auto Ic, int k, int cF, bool rec, int slot, int hbase, int slotA, int slotB,
+                     int slotC) {
+      constexpr int I = decltype(Ic)::value;
+      const int j = k * S + I;
+      const int jp = j & 1;
       if (rec) {
         // the step t = cF S + I from state S_t
+        const Real* stp = &sm.st[slot][I * E];
         if constexpr (I == 0) {
+          const int cb = (int)(cF & 1);
 #pragma unroll
-          for (int p = 0; p < TPW; ++p) h[p] = ckc[p];
+          for (int q0 = 0; q0 < VT; ++q0) {
+            const R4 t4 = sm.ck[cb][(q0 + TPW * wr) % VT][lane];
 #pragma unroll
-          for (int q0 = 0; q0 < VT; ++q0)
+            for (int r = 0; r < 4; ++r) hb[4 * q0 + r] = t4[r];
+          }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) hb[4 * q0 + r] = ckc[q0][r];
+          for (int p = 0; p < TPW; ++p)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) h[p][r] = hb[4 * p + r];
         } else {
 #pragma unroll
           for (int q0 = TPW; q0 < VT; ++q0) {
@@ -355,10 +279,12 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
 #pragma unroll
             for (int r = 0; r < 4; ++r) hb[4 * p + r] = h[p][r];
         }
-        const Real* stp = &sm.st[slot][I * E];
         const Real f = stp[OFF_F];
         const Real omf = Real(1) - f;
         const Real kli = stp[li];
+        Real vli[TPW];
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) vli[p] = stp[OFF_V + (wr * TPW + p) * 16 + li];
         R4 acc[TPW];
 #pragma unroll
         for (int p = 0; p < TPW; ++p) acc[p] = R4{0, 0, 0, 0};
@@ -367,17 +293,11 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
 #pragma unroll
           for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wop[p][s0], hb[s0], acc[p]);
 #pragma unroll
-        for (int p = 0; p < TPW; ++p)
-          acc[p] = mfma_16x16x4(stp[OFF_V + (wr * TPW + p) * 16 + li] * a_mask, kli, acc[p]);
+        for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(vli[p] * a_mask, kli, acc[p]);
 #pragma unroll
         for (int s0 = 4 * TPW; s0 < NS; ++s0)
 #pragma unroll
           for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wop[p][s0], hb[s0], acc[p]);
-        // dW += S_t'^T D_t' for the reverse role's previous step t' (zero
-        // A operands when it had none), then the accumulators are read here, in
-        // the block of the MFMAs: the first read of an MFMA result must not sit
-        // behind a branch, where the wait states it needs are not inserted
-        dw_mfma();
 #pragma unroll
         for (int p = 0; p < TPW; ++p) pin_vec(acc[p]);
         const Real m2omf = Real(-2) * omf;
@@ -396,22 +316,51 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
 #pragma unroll
           for (int r = 0; r < 4; ++r) dqp = fma_r(h[p][r], u[r], dqp);
         }
-        sm.rq[jp][li][wr * 4 + g] = dqp;
-      } else {
-        dw_mfma();
+        // this wave's columns of dq_t, summed over the four lane groups
+        dqp = cross_row_sum(dqp);
+        if (g == 0) sm.rq[jp][li][wr] = dqp;
       }
-      // dW operands of the step the reverse role takes in this phase: S_t
-      // transposed, or zeros when it takes none
-      {
-        const bool ract = j >= S + 1 && j <= nch * S + S;
-        const int pos = (int)((nch * S + S - j) & (M - 1));
+      // dq of the previous phase's step: the per-wave sums, added by wave 0
+      if (wr == 0 && g == 0 && row_ok && j >= 1 && j <= nch * S) {
+        const int tf = I > 0 ? cF * S + I - 1 : cF * S + 2 * S - 1;
+        if (tf < T32) {
+          Real sq = 0;
 #pragma unroll
-        for (int p = 0; p < TPW; ++p)
+          for (int i = 0; i < NW; ++i) sq += sm.rq[jp ^ 1][li][i];
+          dq_row[(int64_t)tf * NK] = sq;
+        }
+      }
+      // dv_t' = D^T k over this slab's rows (+ w_r (.) u when the slab is the
+      // whole head) for the reverse role's step t' = (cF + 2) S - I + 1 of
+      // phase j - 1: this wave's D tiles, reduced over the 16 rows with DPP
+      if (ractive(j - 1)) {
+        const int tp = (cF + 2) * S - I + 1;
+        if (tp < T32) {
+          constexpr int tq = (1 - I + S) % S;
+          const Real* stq = &sm.st[S == 1 ? slotC : (I <= 1 ? slotB : slotA)][tq * E];
+          const Real kq = stq[li];
+          Real* dvp = dv_tok + (int64_t)tp * NV;
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const Real x = ((const Real*)&sm.hr[ract ? pos : 0][wr * TPW + p][0])[tidx(kk)];
-            aop[p][kk] = ract ? x : Real(0);
+          for (int p = 0; p < TPW; ++p) {
+            const R4 Dt = sm.xd[jp ^ 1][wr * TPW + p][lane];
+            R4 sv = row16_sum_x4(Dt, kq);
+            if (li == 0) {
+              if (nslab == 1) {
+                const R4 u = cols4(stq + OFF_U + (wr * TPW + p) * 16, g);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sv[r] = fma_r(wrc[p][r], u[r], sv[r]);
+              }
+              const int col0 = col_of(p, 0);
+              if (dv_vec) {
+                if (col0 < V) *(R4*)(dvp + col0) = sv;
+              } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  if (col_of(p, r) < V) dvp[col_of(p, r)] = sv[r];
+              }
+            }
           }
+        }
       }
       // S_0 (the initial state) for the reverse role's last step
       if (j == nch * S) {
@@ -428,21 +377,378 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
       }
     };
 
-    for (int64_t k = 0; k < nper; ++k) {
-      const int64_t cF = nch - 1 - k;  // chunk recomputed in this period
+    for (int k = 0; k < nper; ++k) {
+      const int cF = nch - 1 - k;  // chunk recomputed in this period
       const bool rec = cF >= 0;
-      const int slot = rec ? (int)(cF % NSLOT) : 0;
-      const int hbase = rec ? (int)(cF & 1) * S : 0;  // ring position of S_{cF S}
-      if (rec) {
-#pragma unroll
-        for (int q = 0; q < VT; ++q) ckc[q] = ckn[q];
-        if (cF >= 1) load_start(cF - 1, ckn);
-      }
-      const bool stage = cF >= 1;
-      if (stage) stage_load(cF - 1);
+      const int slot = rec ? cF % NSLOT : 0;
+      const int hbase = rec ? (cF & 1) * S : 0;  // ring position of S_{cF S}
+      const int slotA = cF + 1 >= 0 ? (cF + 1) % NSLOT : 0;
+      const int slotB = cF + 2 >= 0 ? (cF + 2) % NSLOT : 0;
+      const int slotC = cF + 3 >= 0 ? (cF + 3) % NSLOT : 0;
       [&]<int... I>(std::integer_sequence<int, I...>) {
-        ((phase(std::integral_constant<int, I>{}, k, cF, rec, slot, hbase),
-          (I == S - 1 && stage ? stage_store(cF - 1) : void()), __syncthreads()),
+        ((phase(std::integral_constant<int, I>{}, k, cF, rec, slot, hbase, slotA, slotB, slotC),
+          __syncthreads()),
+         ...);
+      }(std::make_integer_sequence<int, S>{});
+    }
+  } else if (role == 1) {
+    // ================================================================ reverse role
+    // W as the A operand of (D W^T)^T = W D^T, rotated like the forward role's
+    Real wop[TPW][NS];
+#pragma unroll
+    for (int p = 0; p < TPW; ++p) {
+      const int col = (wr * TPW + p) * 16 + li;
+#pragma unroll
+      for (int s0 = 0; s0 < NS; ++s0) {
+        const int s = (s0 + 4 * TPW * wr) % NS;
+        const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
+        wop[p][s0] = (col < V && l < V) ? Wp[((int64_t)n * V + col) * V + l] : Real(0);
+      }
+    }
+    R4 fR[TPW], Dp[TPW], rcn[TPW];
+#pragma unroll
+    for (int p = 0; p < TPW; ++p) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int col = col_of(p, r);
+        fR[p][r] = (a.dHT && row_ok && col < V) ? ((const Real*)a.dHT)[state_base + col] : Real(0);
+      }
+      Dp[p] = R4{0, 0, 0, 0};
+      rcn[p] = R4{0, 0, 0, 0};
+    }
+    // complete the loads made before the loop here (see the forward role)
+#pragma unroll
+    for (int p = 0; p < TPW; ++p) {
+#pragma unroll
+      for (int s0 = 0; s0 < NS; s0 += 4) pin_values(wop[p][s0], wop[p][s0 + 1], wop[p][s0 + 2], wop[p][s0 + 3]);
+      pin_vec(fR[p]);
+    }
+    // transposed D: element (row li, column c) of a tile at [c][4 (li % 4) + li / 4]
+    const int trow = 4 * (li & 3) + (li >> 2);
+
+    __syncthreads();  // prologue staging by the side role
+
+    auto phase = [&](auto Ic, int k, int slotA, int slotB, int par) {
+      constexpr int I = decltype(Ic)::value;
+      const int j = k * S + I;
+      const int jp = j & 1;
+      const int t = rstep(j);  // step reversed in this phase
+      const bool act = ractive(j);
+      const bool fin = j == jlast;
+      if (act || fin) {
+        // C = f R + D W^T of step t + 1 (other waves' D tiles from phase j - 1)
+        Real db[NS];
+#pragma unroll
+        for (int q0 = 0; q0 < VT; ++q0) {
+          const R4 t4 = q0 < TPW ? Dp[q0] : sm.xd[jp ^ 1][(q0 + TPW * wr) % VT][lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) db[4 * q0 + r] = t4[r];
+        }
+        R4 acc[TPW];
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) acc[p] = fR[p];
+#pragma unroll
+        for (int s0 = 0; s0 < NS; ++s0)
+#pragma unroll
+          for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wop[p][s0], db[s0], acc[p]);
+        // read the accumulators before the branch below
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) pin_vec(acc[p]);
+        if (fin) {
+          if (a.dH0 && row_ok) {
+#pragma unroll
+            for (int p = 0; p < TPW; ++p)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int col = col_of(p, r);
+                if (col < V) ((Real*)a.dH0)[state_base + col] = acc[p][r];
+              }
+          }
+        } else {
+          // phase I >= 1 reverses step (cF + 1) S + S - I, phase 0 step (cF + 2) S
+          constexpr int tt = I >= 1 ? S - I : 0;
+          const Real* stp = &sm.st[I >= 1 ? slotA : slotB][tt * E];
+          const Real f = stp[OFF_F];
+          const Real omf = Real(1) - f;
+          const Real qli = stp[OFF_Q + li];
+          const int pos = (par * S - I) & (M - 1);  // ring position of t
+          Real dfp = 0, dkp = 0;
+#pragma unroll
+          for (int p = 0; p < TPW; ++p) {
+            const R4 hp = sm.hr[pos][wr * TPW + p][lane];
+            const R4 u = cols4(stp + OFF_U + (wr * TPW + p) * 16, g);
+            const R4 vv = cols4(stp + OFF_V + (wr * TPW + p) * 16, g);
+            R4 D;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const Real rc = rcn[p][r];
+              const Real z = fma_r(Real(-2), rc, Real(1));
+              const Real sech2 = Real(4) * rc * (Real(1) - rc);
+              const Real Rm = fma_r(qli, u[r], acc[p][r]);
+              D[r] = omf * Rm * sech2;
+              fR[p][r] = f * Rm;
+              dfp = fma_r(Rm, hp[r] - z, dfp);
+              dkp = fma_r(D[r], vv[r], dkp);
+            }
+            Dp[p] = D;
+            sm.xd[jp][wr * TPW + p][lane] = D;
+            if constexpr (Tr::kXdt) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) sm.xdT[jp][wr * TPW + p][acc_m<Real>(g, r)][trow] = D[r];
+            }
+          }
+          sm.rk[jp][li][wr * 4 + g] = dkp;
+          dfp = row16_sum(dfp);
+          if (li == 0) sm.rf[jp][wr * 4 + g] = dfp;
+          // rc of step t - 1, for the next phase
+          if (t >= 1) {
+#pragma unroll
+            for (int p = 0; p < TPW; ++p) rcn[p] = sm.zr[(pos - 1) & (M - 1)][wr * TPW + p][lane];
+          }
+        }
+      }
+      if (j == S) {  // rc of the first reversed step
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) rcn[p] = sm.zr[(nch * S - 1) & (M - 1)][wr * TPW + p][lane];
+      }
+    };
+
+    for (int k = 0; k < nper; ++k) {
+      const int cF = nch - 1 - k;  // chunk the forward role recomputes
+      const int cA = cF + 1, cB = cF + 2;
+      const int slotA = cA >= 0 ? cA % NSLOT : 0;
+      const int slotB = cB >= 0 ? cB % NSLOT : 0;
+      // step (cF + 1) S + S - I sits at ring position ((cF + 2) S - I) mod 2 S
+      const int par = cB & 1;
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        ((phase(std::integral_constant<int, I>{}, k, slotA, slotB, par), __syncthreads()), ...);
+      }(std::make_integer_sequence<int, S>{});
+    }
+  } else {
+    // ================================================================ side role
+    const int xt = tid - 2 * 64 * NW;  // thread index within the role
+    const InT* __restrict__ kp = (const InT*)a.k;
+    const InT* __restrict__ vp = (const InT*)a.v;
+    const InT* __restrict__ qp = (const InT*)a.q;
+    const Real* __restrict__ fp = (const Real*)a.f;
+    const Real* __restrict__ dyp = (const Real*)a.dy;
+    Real* __restrict__ ws = (Real*)a.ws;
+
+    // ---- staging of one chunk's inputs.  Side thread xt owns the staged
+    // values e = xt + m NX of a chunk (step e / E, field by e % E), each from
+    // an InT array (k, q, v) or a Real array (dy, f); its source addresses for
+    // chunk c are fixed pointers plus the step index times a stride, set up
+    // once.  Steps past T are padding: f = 1 and dy = 0 make them exact
+    // identities.  Raw values stay in registers until the LDS store at the
+    // period's end, so nothing waits for the loads before then.
+    const InT* ld_pin[NLD];
+    const Real* ld_pre[NLD];
+    int ld_ts[NLD], ld_tt[NLD];
+    bool ld_in[NLD], ld_ok[NLD], ld_isf[NLD], ld_st[NLD];
+#pragma unroll
+    for (int m = 0; m < NLD; ++m) {
+      const int e = xt + m * NX;
+      const int tt = e / E, r = e % E;
+      const InT* pin = kp;
+      const Real* pre = fp;
+      bool from_in = false, ok = false, isf = false;
+      int ts = 0;
+      if (e < S * E) {
+        if (r < 32) {  // k (r < 16) or q, slab row r mod 16
+          const int rr = slab * 16 + (r & 15);
+          ok = rr < K;
+          from_in = true;
+          pin = (r < 16 ? kp : qp) + tok0 * K + (ok ? rr : 0);
+          ts = (int)(N * K);
+        } else if (r < OFF_U) {  // v, column r - 32
+          const int jj = r - OFF_V;
+          ok = jj < V;
+          from_in = true;
+          pin = vp + tok0 * V + (ok ? jj : 0);
+          ts = (int)(N * V);
+        } else if (r < OFF_F) {  // dy, column r - 32 - VP
+          const int jj = r - OFF_U;
+          ok = jj < V;
+          pre = dyp + tok0 * V + (ok ? jj : 0);
+          ts = (int)(N * V);
+        } else if (r == OFF_F) {  // f
+          ok = true;
+          isf = true;
+          pre = fp + tok0;
+          ts = (int)N;
+        }
+      }
+      ld_pin[m] = pin;
+      ld_pre[m] = pre;
+      ld_ts[m] = ts;
+      ld_tt[m] = e < S * E ? tt : 0;
+      ld_in[m] = from_in;
+      ld_ok[m] = ok;
+      ld_isf[m] = isf;
+      ld_st[m] = e < S * E;
+    }
+    InT stx_in[NLD];
+    Real stx_re[NLD];
+    bool stx_tv[NLD];
+    auto stage_load = [&](int c) {
+#pragma unroll
+      for (int m = 0; m < NLD; ++m) {
+        const int t = c * S + ld_tt[m];
+        const bool tv = t < T32;
+        const int64_t o = (int64_t)(tv ? t : T32 - 1) * ld_ts[m];
+        stx_in[m] = ld_pin[m][ld_in[m] ? o : 0];
+        stx_re[m] = ld_pre[m][ld_in[m] ? 0 : o];
+        stx_tv[m] = tv;
+      }
+    };
+    auto stage_store = [&](int c) {
+      Real* dst = sm.st[c % NSLOT];
+#pragma unroll
+      for (int m = 0; m < NLD; ++m) {
+        const Real x = ld_in[m] ? (Real)widen(stx_in[m]) : stx_re[m];
+        const Real v = (ld_ok[m] && stx_tv[m]) ? x : (ld_isf[m] ? Real(1) : Real(0));
+        if (ld_st[m]) dst[xt + m * NX] = v;
+      }
+    };
+    // ---- start state of a chunk into register layout: element (row, col) of
+    // the slab goes to tile col / 16, lane 16 acc_g(col % 16) + row, element
+    // acc_r(col % 16).  Loads from clamped addresses; padding zeroed at the store.
+    const Real* const cks_base = (const Real*)a.cks + (int64_t)bn * a.cks_count * K * V;
+    const int64_t cks_stride = a.cks_step * K * V;
+    int ck_src[NCK], ck_dst[NCK];
+    bool ck_ok[NCK], ck_in[NCK];
+#pragma unroll
+    for (int m = 0; m < NCK; ++m) {
+      const int e = xt + m * NX;
+      const int rr = e / VP, col = e % VP, c16 = col & 15;
+      const int grow = slab * 16 + rr;
+      ck_in[m] = e < 16 * VP;
+      ck_ok[m] = ck_in[m] && grow < K && col < V;
+      ck_src[m] = ck_ok[m] ? grow * (int)V + col : 0;
+      ck_dst[m] = ((col >> 4) * 64 + 16 * acc_g<Real>(c16) + rr) * 4 + acc_r<Real>(c16);
+    }
+    Real ckx[NCK];
+    auto ck_load = [&](int c) {
+      const Real* src = cks_base + c * cks_stride;
+#pragma unroll
+      for (int m = 0; m < NCK; ++m) ckx[m] = src[ck_src[m]];
+    };
+    auto ck_store = [&](int c) {
+      Real* dst = (Real*)&sm.ck[c & 1][0][0];
+#pragma unroll
+      for (int m = 0; m < NCK; ++m)
+        if (ck_in[m]) dst[ck_dst[m]] = ck_ok[m] ? ckx[m] : Real(0);
+    };
+
+    // ---- dW accumulators: this wave's row tiles wr * TPW + p, all column tiles
+    R4 dWacc[TPW][VT];
+    Real aop[TPW][4];
+#pragma unroll
+    for (int p = 0; p < TPW; ++p) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) aop[p][kk] = Real(0);
+#pragma unroll
+      for (int jt = 0; jt < VT; ++jt) dWacc[p][jt] = R4{0, 0, 0, 0};
+    }
+    // transposed LDS element (row 4 kk + g, column li) of a state tile: lane
+    // 16 acc_g(li) + 4 kk + g, element acc_r(li)
+    auto tidx = [&](int kk) { return (16 * acc_g<Real>(li) + 4 * kk + g) * 4 + acc_r<Real>(li); };
+    // output pointers at token (b, t = 0, n); step t adds t N rows
+    Real* const dk_row = (Real*)a.dk + tok0 * K + row;
+    Real* const df_tok = ws + L.df_part + (int64_t)slab * B * T * N + tok0;
+    const int64_t NK = N * K;
+
+    // both D buffers start at zero: the reverse role's first step reads the
+    // (absent) later step's D, and dW multiplies zero A operands by the
+    // transposed copy before the first D is written
+    for (int i = xt; i < 2 * VT * 64; i += NX) (&sm.xd[0][0][0])[i] = R4{0, 0, 0, 0};
+    for (int i = xt; i < (int)(sizeof(sm.xdT) / sizeof(Real)); i += NX) (&sm.xdT[0][0][0][0])[i] = Real(0);
+    stage_load(nch - 1);
+    ck_load(nch - 1);
+    stage_store(nch - 1);
+    ck_store(nch - 1);
+    __syncthreads();
+
+    auto phase = [&](auto Ic, int k, int cF, int par) {
+      constexpr int I = decltype(Ic)::value;
+      const int j = k * S + I;
+      const int jp = j & 1;
+      // dW += S_t'^T D_t' for the reverse role's step t' of phase j - 1 (zero
+      // A operands when it had none); B from the transposed D copy
+      {
+        R4 bop[VT];
+#pragma unroll
+        for (int jt = 0; jt < VT; ++jt) {
+          if constexpr (Tr::kXdt) {
+            bop[jt] = *(const R4*)&sm.xdT[jp ^ 1][jt][li][4 * g];
+          } else {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) bop[jt][kk] = ((const Real*)&sm.xd[jp ^ 1][jt][0])[tidx(kk)];
+          }
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int jt = 0; jt < VT; ++jt)
+#pragma unroll
+            for (int p = 0; p < TPW; ++p) dWacc[p][jt] = mfma_16x16x4(aop[p][kk], bop[jt][kk], dWacc[p][jt]);
+      }
+      // A operands for the reverse role's step of this phase, (cF + 2) S - I:
+      // S_t transposed, or zeros when it takes none
+      {
+        const bool ra = ractive(j);
+        const int pos = ra ? (par * S - I) & (M - 1) : 0;
+#pragma unroll
+        for (int p = 0; p < TPW; ++p)
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const Real x = ((const Real*)&sm.hr[pos][wr * TPW + p][0])[tidx(kk)];
+            aop[p][kk] = ra ? x : Real(0);
+          }
+      }
+      // the reverse role's step of phase j - 1: tp = (cF + 2) S - I + 1
+      if (!ractive(j - 1)) return;
+      const int tp = (cF + 2) * S - I + 1;
+      if (tp >= T32) return;
+      // dk_t' and df_t' from the reverse role's partials: lane group q adds
+      // entries 4 q .. 4 q + 3, then the four groups are added across lanes
+      if (wr == 0) {
+        Real s4 = 0;
+        if (4 * g < 4 * NW) {
+          const R4 x = *(const R4*)&sm.rk[jp ^ 1][li][4 * g];
+          s4 = (x[0] + x[1]) + (x[2] + x[3]);
+        }
+        s4 = cross_row_sum(s4);
+        if (g == 0 && row_ok) dk_row[(int64_t)tp * NK] = s4;
+      }
+      if (wr == (1 % NW)) {
+        Real s4 = 0;
+        if (li == 0 && 4 * g < 4 * NW) {
+          const R4 x = *(const R4*)&sm.rf[jp ^ 1][4 * g];
+          s4 = (x[0] + x[1]) + (x[2] + x[3]);
+        }
+        s4 = cross_row_sum(s4);
+        if (lane == 0) df_tok[(int64_t)tp * N] = s4;
+      }
+    };
+    for (int k = 0; k < nper; ++k) {
+      const int cF = nch - 1 - k;  // chunk the forward role recomputes
+      const bool stage = cF >= 1;
+      if (stage) {
+        stage_load(cF - 1);
+        ck_load(cF - 1);
+      }
+      const int par = (cF + 2) & 1;
+      auto period_end = [&]() {
+        if (stage) {
+          stage_store(cF - 1);
+          ck_store(cF - 1);
+        }
+      };
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        ((phase(std::integral_constant<int, I>{}, k, cF, par),
+          (I == S - 1 ? period_end() : void()),
+          __syncthreads()),
          ...);
       }(std::make_integer_sequence<int, S>{});
     }
@@ -463,174 +769,6 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
           const int jj = jt * 16 + li;
           if (l < V && jj < V) dWp[(int64_t)l * V + jj] = dWacc[p][jt][r];
         }
-  } else {
-    // ================================================================ reverse role
-    // W as the A operand of (D W^T)^T = W D^T, rotated like the forward role's
-    Real wop[TPW][NS];
-#pragma unroll
-    for (int p = 0; p < TPW; ++p) {
-      const int col = (wr * TPW + p) * 16 + li;
-#pragma unroll
-      for (int s0 = 0; s0 < NS; ++s0) {
-        const int s = (s0 + 4 * TPW * wr) % NS;
-        const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
-        wop[p][s0] = (col < V && l < V) ? Wp[((int64_t)n * V + col) * V + l] : Real(0);
-      }
-    }
-    R4 fR[TPW], Dp[TPW], rcn[TPW];
-    Real wrc[TPW][4];
-#pragma unroll
-    for (int p = 0; p < TPW; ++p) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int col = col_of(p, r);
-        fR[p][r] = (a.dHT && row_ok && col < V) ? ((const Real*)a.dHT)[state_base + col] : Real(0);
-        wrc[p][r] = col < V ? ((const Real*)a.w_r)[(int64_t)n * V + col] : Real(0);
-      }
-      Dp[p] = R4{0, 0, 0, 0};
-      rcn[p] = R4{0, 0, 0, 0};
-    }
-    Real* __restrict__ df_part = ws + L.df_part;
-    Real* __restrict__ dv_part = ws + L.dv_part;
-
-    stage_load(nch - 1);
-    stage_store(nch - 1);
-    __syncthreads();
-
-    auto phase = [&](auto Ic, int64_t k, int slotA, int slotB, int par) {
-      constexpr int I = decltype(Ic)::value;
-      const int64_t j = k * S + I;
-      const int jp = (int)(j & 1);
-      const int64_t t = nch * S + S - j;  // step reversed in this phase
-      const bool act = j >= S + 1 && j <= nch * S + S;
-      const bool fin = j == jlast;
-      // dk and df of the previous phase's step: per-wave partials summed by wave 0
-      if (wr == 0 && j >= S + 2 && j <= jlast) {
-        const int64_t tp = t + 1;
-        if (tp < T) {
-          if (g == 0 && row_ok) {
-            Real s = 0;
-#pragma unroll
-            for (int i = 0; i < 4 * NW; ++i) s += sm.rk[jp ^ 1][li][i];
-            ((Real*)a.dk)[(tok0 + tp * N) * K + row] = s;
-          }
-          if (lane == 0) {
-            Real s = 0;
-#pragma unroll
-            for (int i = 0; i < 4 * NW; ++i) s += sm.rf[jp ^ 1][i];
-            df_part[slab * tok_stride + tok0 + tp * N] = s;
-          }
-        }
-      }
-      if (act || fin) {
-        // C = f R + D W^T of step t + 1 (other waves' D tiles from phase j - 1)
-        Real db[NS];
-#pragma unroll
-        for (int q0 = 0; q0 < VT; ++q0) {
-          const R4 t4 = q0 < TPW ? Dp[q0] : sm.xd[jp ^ 1][(q0 + TPW * wr) % VT][lane];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) db[4 * q0 + r] = t4[r];
-        }
-        R4 acc[TPW];
-#pragma unroll
-        for (int p = 0; p < TPW; ++p) acc[p] = fR[p];
-#pragma unroll
-        for (int s0 = 0; s0 < NS; ++s0)
-#pragma unroll
-          for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wop[p][s0], db[s0], acc[p]);
-        // read the accumulators before the branch below (see the forward role)
-#pragma unroll
-        for (int p = 0; p < TPW; ++p) pin_vec(acc[p]);
-        if (fin) {
-          if (a.dH0 && row_ok) {
-#pragma unroll
-            for (int p = 0; p < TPW; ++p)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int col = col_of(p, r);
-                if (col < V) ((Real*)a.dH0)[state_base + col] = acc[p][r];
-              }
-          }
-        } else {
-          // phase I >= 1 reverses step (cF + 1) S + S - I, phase 0 step (cF + 2) S
-          constexpr int tt = I >= 1 ? S - I : 0;
-          const Real* stp = &sm.st[I >= 1 ? slotA : slotB][tt * E];
-          const Real f = stp[OFF_F];
-          const Real omf = Real(1) - f;
-          const Real qli = stp[OFF_Q + li];
-          const Real kli = stp[li];
-          const int pos = (par * S - I) & (M - 1);  // ring position of t
-          Real dfp = 0, dkp = 0;
-          R4 u[TPW];
-#pragma unroll
-          for (int p = 0; p < TPW; ++p) {
-            const R4 hp = sm.hr[pos][wr * TPW + p][lane];
-            u[p] = cols4(stp + OFF_U + (wr * TPW + p) * 16, g);
-            const R4 vv = cols4(stp + OFF_V + (wr * TPW + p) * 16, g);
-            R4 D;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const Real rc = rcn[p][r];
-              const Real z = fma_r(Real(-2), rc, Real(1));
-              const Real sech2 = Real(4) * rc * (Real(1) - rc);
-              const Real Rm = fma_r(qli, u[p][r], acc[p][r]);
-              D[r] = omf * Rm * sech2;
-              fR[p][r] = f * Rm;
-              dfp = fma_r(Rm, hp[r] - z, dfp);
-              dkp = fma_r(D[r], vv[r], dkp);
-            }
-            Dp[p] = D;
-            sm.xd[jp][wr * TPW + p][lane] = D;
-          }
-          sm.rk[jp][li][wr * 4 + g] = dkp;
-          dfp = row16_sum(dfp);
-          if (li == 0) sm.rf[jp][wr * 4 + g] = dfp;
-          // dv_t = D^T k over this slab's rows (+ w_r (.) u when the slab is the whole head)
-#pragma unroll
-          for (int p = 0; p < TPW; ++p) {
-            const R4 s = row16_sum_x4(Dp[p], kli);
-            if (li == 0 && t < T) {
-              const int64_t tok = tok0 + t * N;
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int col = col_of(p, r);
-                if (col < V) {
-                  if (nslab == 1)
-                    ((Real*)a.dv)[tok * V + col] = fma_r(wrc[p][r], u[p][r], s[r]);
-                  else
-                    dv_part[slab * tok_stride * V + tok * V + col] = s[r];
-                }
-              }
-            }
-          }
-          // rc of step t - 1, for the next phase
-          if (t >= 1) {
-#pragma unroll
-            for (int p = 0; p < TPW; ++p) rcn[p] = sm.zr[(pos - 1) & (M - 1)][wr * TPW + p][lane];
-          }
-        }
-      }
-      if (j == S) {  // rc of the first reversed step
-#pragma unroll
-        for (int p = 0; p < TPW; ++p) rcn[p] = sm.zr[(nch * S - 1) & (M - 1)][wr * TPW + p][lane];
-      }
-    };
-
-    for (int64_t k = 0; k < nper; ++k) {
-      const int64_t cF = nch - 1 - k;  // chunk the forward role recomputes
-      const bool stage = cF >= 1;
-      if (stage) stage_load(cF - 1);
-      const int64_t cA = cF + 1, cB = cF + 2;
-      const int slotA = cA >= 0 ? (int)(cA % NSLOT) : 0;
-      const int slotB = cB >= 0 ? (int)(cB % NSLOT) : 0;
-      // step (cF + 1) S + S - I sits at ring position ((cF + 2) S - I) mod 2 S
-      const int par = (int)(cB & 1);
-      [&]<int... I>(std::integer_sequence<int, I...>) {
-        ((phase(std::integral_constant<int, I>{}, k, slotA, slotB, par),
-          (I == S - 1 && stage ? stage_store(cF - 1) : void()), __syncthreads()),
-         ...);
-      }(std::make_integer_sequence<int, S>{});
-    }
   }
 }
 

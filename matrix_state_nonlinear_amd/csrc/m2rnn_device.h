@@ -170,12 +170,30 @@ __device__ __forceinline__ f64x4 row16_sum_x4(f64x4 h, double q) {
   return y;
 }
 
-// Sum over the four 16-lane rows (lanes l, l^16, l^32, l^48), via ds_swizzle-free
-// cross-row permutes.  Result valid in every lane.
-template <typename Real>
-__device__ __forceinline__ Real cross_row_sum(Real x) {
-  x += __shfl_xor(x, 16, 64);
+// Sum over the four 16-lane rows (lanes l, l^16, l^32, l^48); every lane gets
+// the same value.  fp32: the gfx950 lane-swap instructions (v_permlane32_swap
+// exchanges the two halves of the wave between two registers, v_permlane16_swap
+// the odd and even rows), written as asm with explicit copies, two wait states
+// around each swap.  fp64: cross-lane shuffles.
+__device__ __forceinline__ float cross_row_sum(float x) {
+  float y;
+  asm volatile(
+      "v_mov_b32 %1, %0\n"
+      "s_nop 1\n"
+      "v_permlane32_swap_b32 %0, %1\n"
+      "s_nop 1\n"
+      "v_add_f32 %0, %0, %1\n"
+      "v_mov_b32 %1, %0\n"
+      "s_nop 1\n"
+      "v_permlane16_swap_b32 %0, %1\n"
+      "s_nop 1\n"
+      "v_add_f32 %0, %0, %1\n"
+      : "+v"(x), "=&v"(y));
+  return x;
+}
+__device__ __forceinline__ double cross_row_sum(double x) {
   x += __shfl_xor(x, 32, 64);
+  x += __shfl_xor(x, 16, 64);
   return x;
 }
 
@@ -194,6 +212,11 @@ __device__ __forceinline__ float load_in(const uint16_t* p) {
   return __builtin_bit_cast(float, (uint32_t)(*p) << 16);
 }
 __device__ __forceinline__ double load_in(const double* p) { return *p; }
+
+// The same conversions for a value already in a register.
+__device__ __forceinline__ float widen(float x) { return x; }
+__device__ __forceinline__ float widen(uint16_t x) { return __builtin_bit_cast(float, (uint32_t)x << 16); }
+__device__ __forceinline__ double widen(double x) { return x; }
 
 template <typename Real, typename InT>
 __device__ __forceinline__ Real load_as(const InT* p) {

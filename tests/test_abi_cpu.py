@@ -53,15 +53,15 @@ def test_workspace_sizes(L):
     # unsupported sizes report 0
     assert ws(0, 1, 10, 1, 300, 16, 1, _lib.M2RNN_F32) == 0
     assert ws(1, 1, 10, 1, 16, 16, 0, _lib.M2RNN_F32) == 0
-    # backward: for V = 64 in fp32 the reverse sweep walks 8-step chunks; a
-    # checkpoint interval dividing 8 provides every chunk start, any other adds
-    # a [B, N, ceil(T / 8), K, V] region of recomputed chunk starts
-    base = ws(1, 2, 64, 2, 32, 64, 8, _lib.M2RNN_F32)
+    # backward: for V = 64 in fp32 the reverse sweep walks 4-step chunks; a
+    # checkpoint interval dividing 4 provides every chunk start, any other adds
+    # a [B, N, ceil(T / 4), K, V] region of recomputed chunk starts
+    base = ws(1, 2, 64, 2, 32, 64, 4, _lib.M2RNN_F32)
     assert base > 0
-    for C in (1, 2, 4):
+    for C in (1, 2):
         assert ws(1, 2, 64, 2, 32, 64, C, _lib.M2RNN_F32) == base
-    for C in (3, 16, 64):
-        assert ws(1, 2, 64, 2, 32, 64, C, _lib.M2RNN_F32) == base + 2 * 2 * 8 * 32 * 64 * 4
+    for C in (3, 8, 64):
+        assert ws(1, 2, 64, 2, 32, 64, C, _lib.M2RNN_F32) == base + 2 * 2 * 16 * 32 * 64 * 4
 
 
 def fwd(L, **kw):

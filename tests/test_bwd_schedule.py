@@ -1,12 +1,17 @@
 """Host-side check of the backward kernel's phase schedule (no GPU).
 
-m2rnn_bwd runs two wave roles in lock step, one barrier per phase: the forward
-role recomputes chunk cF = nch - 1 - k of S steps in period k and writes each
-step's state and tanh term into LDS rings of 2 S entries; the reverse role
-walks the previously recomputed chunk backwards one phase behind, reading
-those rings, a staging ring of input chunks and a parity-buffered D exchange.
-This test replays, phase by phase, the ring positions and slots exactly as the
-kernel computes them (same expressions as m2rnn_bwd.hip) and checks that
+m2rnn_bwd runs three wave roles in lock step, one barrier per phase:
+* forward role: recomputes chunk cF = nch - 1 - k (S steps) in period k, reads
+  its start state from the chunk-start buffer (phase 0) or the state ring,
+  writes each step's state and tanh term into LDS rings of 2 S entries, and
+  forms dv of the reverse role's previous step from the D buffer;
+* reverse role: walks the previously recomputed chunk backwards one phase
+  behind, reading the rings and the staging slots, publishing D;
+* side role: dW from the previous phase's D and the A operands read in the
+  same phase as the reverse role's state read; stages the next chunk's inputs
+  and start state at the period's last phase.
+This test replays, phase by phase, every buffer position and slot exactly as
+the kernel computes them (same expressions as m2rnn_bwd.hip) and checks that
 
 * every read finds the item it needs, written in an earlier phase;
 * no location is read and written in the same phase (no barrier between);
@@ -16,26 +21,34 @@ kernel computes them (same expressions as m2rnn_bwd.hip) and checks that
 import pytest
 
 
-def replay(S, nch):
+def slots(S):
+    """Staging slots of the kernel for chunk length S."""
+    return 3 if S >= 4 else (4 if S == 2 else 5)
+
+
+def replay(S, nch, nslot=None):
     M = 2 * S
-    NSLOT = 3 if S >= 2 else 4
+    NSLOT = nslot or slots(S)
     jlast = nch * S + S + 1
     nper = jlast // S + 1
     store = {}          # (buffer, position) -> (item, phase written)
     errors = []
     fwd_steps, rev_steps = [], []
+    rstep = lambda j: nch * S + S - j            # noqa: E731
+    ractive = lambda j: S + 1 <= j <= nch * S + S  # noqa: E731
 
-    # prologue: staging of the last chunk, before the first barrier
+    # prologue (side role): staging and start state of the last chunk
     store[("st", (nch - 1) % NSLOT)] = (("chunk", nch - 1), -1)
+    store[("ck", (nch - 1) & 1)] = (("start", nch - 1), -1)
     for k in range(nper):
         cF = nch - 1 - k
         rec = cF >= 0
         slot = cF % NSLOT if rec else 0
         hbase = (cF & 1) * S if rec else 0
-        cA, cB = cF + 1, cF + 2
-        slotA = cA % NSLOT if cA >= 0 else 0
-        slotB = cB % NSLOT if cB >= 0 else 0
-        par = cB & 1
+        slotA = (cF + 1) % NSLOT if cF + 1 >= 0 else 0
+        slotB = (cF + 2) % NSLOT if cF + 2 >= 0 else 0
+        slotC = (cF + 3) % NSLOT if cF + 3 >= 0 else 0
+        par = (cF + 2) & 1
         for I in range(S):
             j = k * S + I
             jp = j & 1
@@ -45,19 +58,27 @@ def replay(S, nch):
                 t = cF * S + I
                 fwd_steps.append(t)
                 reads.append(("st", slot, ("chunk", t // S)))
-                if I > 0:
+                if I == 0:
+                    reads.append(("ck", cF & 1, ("start", cF)))
+                else:
                     reads.append(("hr", hbase + I, ("S", t)))
                 writes.append(("hr", (hbase + I + 1) & (M - 1), ("S", t + 1)))
                 writes.append(("zr", hbase + I, ("Z", t)))
-            if S + 2 <= j <= jlast:      # dW from the reverse role's previous step
-                reads.append(("xd", jp ^ 1, ("D", nch * S + S - (j - 1))))
-            if S + 1 <= j <= nch * S + S:   # dW A-operands of this phase's reverse step
-                reads.append(("hr", (nch * S + S - j) & (M - 1), ("S", nch * S + S - j)))
             if j == nch * S:
                 writes.append(("hr", 0, ("S", 0)))
+            if ractive(j - 1):   # dv of the reverse role's previous step
+                tp = (cF + 2) * S - I + 1
+                if tp != rstep(j - 1):
+                    errors.append(f"j={j}: previous reverse step {tp} != {rstep(j - 1)}")
+                tq = (1 - I + S) % S
+                sl = slotC if S == 1 else (slotB if I <= 1 else slotA)
+                if tq != tp % S:
+                    errors.append(f"j={j}: staged index {tq} != {tp % S}")
+                reads.append(("st", sl, ("chunk", tp // S)))
+                reads.append(("xd", jp ^ 1, ("D", tp)))
             # ---------------- reverse role
-            t = nch * S + S - j
-            act = S + 1 <= j <= nch * S + S
+            t = rstep(j)
+            act = ractive(j)
             fin = j == jlast
             if act or fin:
                 reads.append(("xd", jp ^ 1, ("D", t + 1) if j > S + 1 else ("D", "zero")))
@@ -77,9 +98,14 @@ def replay(S, nch):
                     reads.append(("zr", (pos - 1) & (M - 1), ("Z", t - 1)))
             if j == S:
                 reads.append(("zr", (nch * S - 1) & (M - 1), ("Z", nch * S - 1)))
-            # ---------------- staging of chunk cF - 1 at the period's last phase
+            # ---------------- side role
+            if ractive(j - 1):   # dW B operands: the previous step's D
+                reads.append(("xd", jp ^ 1, ("D", rstep(j - 1))))
+            if act:              # dW A operands: this phase's reverse step's state
+                reads.append(("hr", (par * S - I) & (M - 1), ("S", t)))
             if I == S - 1 and cF >= 1:
                 writes.append(("st", (cF - 1) % NSLOT, ("chunk", cF - 1)))
+                writes.append(("ck", (cF - 1) & 1, ("start", cF - 1)))
             # ---------------- checks
             wpos = {(b, p) for b, p, _ in writes}
             for b, p, item in reads:
@@ -109,6 +135,13 @@ def test_backward_phase_schedule(S, nch):
     assert rev == list(range(Tp - 1, -1, -1))
 
 
+@pytest.mark.parametrize("S", [1, 2])
+def test_schedule_replay_detects_too_few_slots(S):
+    """With one staging slot fewer than the kernel uses, the replay must fail
+    (the side role's store would meet a read of the same slot)."""
+    assert any(replay(S, n, nslot=slots(S) - 1)[0] for n in range(2, 9))
+
+
 def test_schedule_replay_detects_short_rings():
     """The replay must catch rings one chunk long (too short) and pass 2 S."""
     for S in (2, 4, 8):
@@ -117,7 +150,7 @@ def test_schedule_replay_detects_short_rings():
 
 
 def replay_with_ring(S, nch, ring):
-    """Like replay(), but with every ring position taken mod `ring`."""
+    """The state and tanh-term rings alone, with positions taken mod `ring`."""
     errors = []
     store = {}
     jlast = nch * S + S + 1
