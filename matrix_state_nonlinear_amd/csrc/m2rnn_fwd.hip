@@ -352,28 +352,37 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
   // the barrier of step TC - 2 orders it before step TC - 1 reads its first
   // slot.  Inputs alternate between two StepIn buffers by step parity.
   StepIn ins[2];
-  auto full_chunk = [&](int base, bool store_next, int64_t ch) {
+  // With a checkpoint interval C that divides TC (a power of two below TC),
+  // the checkpoints inside the chunk are written after steps I with
+  // (I + 1) mod C = 0; ck_in is then C - 1, else -1 (none inside chunks).
+  auto full_chunk = [&](int base, bool store_next, int64_t ch, int ck_in) {
     const int nbase = base ^ TC;
+    Real* const ckc = ck0 ? ck0 + (ch * TC / (ck_in + 1)) * K * V : nullptr;
     [&]<int... I>(std::integer_sequence<int, I...>) {
       ((step(std::integral_constant<int, I & 1>{}, base + I, ins[I & 1], ins[(I + 1) & 1],
              I + 1 < TC ? base + I + 1 : nbase),
-        (I == TC - 3 && store_next ? store_chunk(ch + 1) : void())),
+        (I == TC - 3 && store_next ? store_chunk(ch + 1) : void()),
+        (I + 1 < TC && ck_in >= 0 && ((I + 1) & ck_in) == 0
+             ? write_state(ckc + ((I + 1) / (ck_in + 1)) * K * V)
+             : void())),
        ...);
     }(std::make_integer_sequence<int, TC>{});
   };
 
   ins[0] = read_in(0);
 
-  // Checkpoints need a chunk boundary at every multiple of C; with C a
-  // multiple of TC they all fall between chunks.
-  const bool ck_at_chunks = !a.ckpt || (a.C % TC) == 0;
+  // Checkpoints fall between chunks when C is a multiple of TC; inside the
+  // unrolled chunk when C divides TC (C a power of two); else per step.
+  const bool ck_pow2_in = a.ckpt && a.C < TC && (TC % a.C) == 0;
+  const bool ck_at_chunks = !a.ckpt || (a.C % TC) == 0 || ck_pow2_in;
+  const int ck_in = ck_pow2_in ? (int)a.C - 1 : -1;
   int64_t ch = 0;
   for (; ch < nchunks; ++ch) {
     const int64_t t0 = ch * TC;
     const int base = (int)(ch & 1) * TC;
     const bool last = ch + 1 == nchunks;
     if (!last && ck_at_chunks) {
-      full_chunk(base, true, ch);
+      full_chunk(base, true, ch, ck_in);
     } else {
       // generic path: the partial last chunk, or checkpoints inside chunks
       const int tn = (int)((T - t0) < TC ? (T - t0) : TC);
@@ -385,13 +394,14 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
           step(std::integral_constant<int, 1>{}, base + tt, ins[1], ins[0], nslot);
         if (tt == TC - 3 && !last) store_chunk(ch + 1);
         const int64_t t = t0 + tt;
-        if (a.ckpt && !ck_at_chunks && (t + 1) % a.C == 0 && t + 1 < T)
+        if (a.ckpt && (!ck_at_chunks || ck_pow2_in) && (t + 1) % a.C == 0 && t + 1 < T)
           write_state(ck0 + ((t + 1) / a.C) * K * V);
       }
     }
     // ---- between chunks: checkpoint, write-back of this chunk, prefetch
     const int64_t tend = t0 + TC;   // steps done after this chunk (if not last)
     if (!last && a.ckpt && ck_at_chunks && tend % a.C == 0) write_state(ck0 + (tend / a.C) * K * V);
+    // (the generic path below writes its own checkpoints per step)
     __syncthreads();                             // the chunk's last readout stores
     flush(ch);                                   // readouts of chunk ch are complete
     if (ch + 2 < nchunks) load_chunk(ch + 2);    // into registers; stored during chunk ch + 1
