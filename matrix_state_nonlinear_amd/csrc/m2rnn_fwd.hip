@@ -30,8 +30,11 @@
 // reduction over the 16 rows -- placed where the wave would otherwise wait for
 // its exchange write to land -- then the barrier and the exchange reads.
 // Inputs come from an LDS staging ring laid out so that each step needs only
-// immediate-offset reads; each staging chunk of TC steps is unrolled, and all
-// global traffic (prefetch, write-back, checkpoints) happens between chunks.
+// immediate-offset reads; each staging chunk of TC steps is unrolled, and the
+// global traffic of inputs and readouts (prefetch, write-back) happens between
+// chunks, from pointers that step forward one chunk at a time (no index
+// arithmetic in the loop).  Checkpoints are written after the steps they
+// follow, counted down on the scalar unit.
 
 #include <type_traits>
 
@@ -123,18 +126,44 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
       hown[p][r] = (a.H0 && row_ok && col < V) ? ((const Real*)a.H0)[state_base + col] : Real(0);
     }
   const int64_t nck = a.ckpt ? (T + a.C - 1) / a.C : 0;
+  // where a lane's four columns are consecutive (fp32), one 16-byte store
+  const bool st_vec = sizeof(Real) == 4 && (V & 3) == 0;
   auto write_state = [&](Real* dst) {
     if (!row_ok) return;
 #pragma unroll
-    for (int p = 0; p < TPW; ++p)
+    for (int p = 0; p < TPW; ++p) {
+      if (st_vec) {
+        if (col_of(p, 0) < V) *(R4*)(dst + col_of(p, 0)) = hown[p];
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int col = col_of(p, r);
-        if (col < V) dst[col] = hown[p][r];
+        for (int r = 0; r < 4; ++r) {
+          const int col = col_of(p, r);
+          if (col < V) dst[col] = hown[p][r];
+        }
       }
+    }
   };
-  Real* const ck0 = a.ckpt ? (Real*)a.ckpt + (((int64_t)b * N + n) * nck * K + row) * V : nullptr;
-  if (a.ckpt) write_state(ck0);
+  // checkpoints H_{cC}, c = 0 .. nck - 1, are written in order: ckp is the
+  // next one's slot, and ck_left counts the steps until it is due
+  Real* ckp = a.ckpt ? (Real*)a.ckpt + (((int64_t)b * N + n) * nck * K + row) * V : nullptr;
+  const int64_t KV = K * V;
+  const int C32 = a.ckpt ? (int)a.C : 0;
+  int ck_left = C32;
+  if (a.ckpt) {
+    write_state(ckp);
+    ckp += KV;
+  }
+  // after step t (t + 1 steps done): write H_{t+1} when it is due and not H_T
+  auto ck_step = [&](int t) {
+    if (C32 == 0) return;
+    if (--ck_left == 0) {
+      ck_left = C32;
+      if (t + 1 < (int)T) {
+        write_state(ckp);
+        ckp += KV;
+      }
+    }
+  };
 
   // ---- staging of one chunk of TC steps.  Each thread owns a fixed set of
   // (step-in-chunk, index) elements, so its global addresses for chunk ch are
@@ -143,7 +172,15 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
   // the last chunk the step index is clamped to T - 1 and the value masked.
   const int64_t NV = N * V, NK = N * K;
   const int64_t tok0 = (int64_t)b * T * N + n;       // token index of (b, t = 0, n)
-  int64_t r1_vofs[Tr::NR1_PER], r1_kofs[Tr::NR1_PER], q_ofs[Tr::NQ_PER];
+  const int T32 = (int)T;                             // T < 2^30
+  // Each thread owns a fixed set of (step-in-chunk, index) elements.  Chunks
+  // are loaded in order, so each element's source pointer steps forward by
+  // one chunk (TC tokens) per load; the last, partial chunk clamps its steps
+  // to T - 1 and masks them.  Loads are unconditional (all of a chunk's loads
+  // are in flight at once).
+  const InT* r1_vp[Tr::NR1_PER];
+  const InT* r1_kp[Tr::NR1_PER];
+  const InT* q_p[Tr::NQ_PER];
   int r1_tt[Tr::NR1_PER], q_tt[Tr::NQ_PER];
   bool r1_vok[Tr::NR1_PER], r1_kok[Tr::NR1_PER], q_ok[Tr::NQ_PER];
 #pragma unroll
@@ -151,50 +188,64 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
     const int e = tid + m * NT;                      // [tt][c][i]
     const int tt = e / VP, c = (e / 16) % VT, i = e % 16;
     const int j = c * 16 + i, rr = slab * 16 + i;
-    r1_tt[m] = tt < TC ? tt : TC;                    // TC marks a padding element
+    r1_tt[m] = tt < TC ? tt : 0;
     r1_vok[m] = tt < TC && j < V;
     r1_kok[m] = tt < TC && rr < K;
-    r1_vofs[m] = tok0 * V + (j < V ? j : V - 1);
-    r1_kofs[m] = tok0 * K + (rr < K ? rr : K - 1);
+    r1_vp[m] = vp + tok0 * V + (j < V ? j : V - 1) + (int64_t)r1_tt[m] * NV;
+    r1_kp[m] = kp + tok0 * K + (rr < K ? rr : K - 1) + (int64_t)r1_tt[m] * NK;
   }
 #pragma unroll
   for (int m = 0; m < Tr::NQ_PER; ++m) {
     const int e = tid + m * NT;                      // [tt][i]
     const int tt = e / 16, i = e % 16, rr = slab * 16 + i;
-    q_tt[m] = tt < TC ? tt : TC;
+    q_tt[m] = tt < TC ? tt : 0;
     q_ok[m] = tt < TC && rr < K;
-    q_ofs[m] = tok0 * K + (rr < K ? rr : K - 1);
+    q_p[m] = qp + tok0 * K + (rr < K ? rr : K - 1) + (int64_t)q_tt[m] * NK;
   }
+  const int f_tt = tid < TC ? tid : 0;
+  const Real* f_p = fp + tok0 + (int64_t)f_tt * N;
   R2 st_r1[Tr::NR1_PER];
   Real st_q[Tr::NQ_PER], st_f;
-  auto load_chunk = [&](int64_t ch) {
-    const int64_t t0 = ch * TC;
-    const bool full = t0 + TC <= T;
-    auto tok = [&](int tt) {   // token offset (in tokens) of step t0 + tt, clamped
-      const int64_t t = t0 + (tt < TC ? tt : 0);
-      return full ? t : (t < T ? t : T - 1);
-    };
+  // load chunk ch (chunks in order: the pointers are at chunk ch on entry)
+  auto load_chunk = [&](int ch) {
+    const int t0 = ch * TC;
+    if (t0 + TC <= T32) {
+#pragma unroll
+      for (int m = 0; m < Tr::NR1_PER; ++m) {
+        st_r1[m][0] = load_sel<Real>(r1_vp[m], 0, r1_vok[m]);
+        st_r1[m][1] = load_sel<Real>(r1_kp[m], 0, r1_kok[m]);
+      }
+#pragma unroll
+      for (int m = 0; m < Tr::NQ_PER; ++m) st_q[m] = load_sel<Real>(q_p[m], 0, q_ok[m]);
+      st_f = load_sel<Real>(f_p, 0, tid < TC);
+    } else {  // the last chunk: steps past T read step T - 1 and are masked
+      const int64_t lim = T32 - 1 - t0;  // last step of the chunk within T, relative
+#pragma unroll
+      for (int m = 0; m < Tr::NR1_PER; ++m) {
+        const int64_t back = r1_tt[m] > lim ? r1_tt[m] - lim : 0;
+        const bool in = r1_tt[m] <= lim;
+        st_r1[m][0] = load_sel<Real>(r1_vp[m], -back * NV, r1_vok[m] && in);
+        st_r1[m][1] = load_sel<Real>(r1_kp[m], -back * NK, r1_kok[m] && in);
+      }
+#pragma unroll
+      for (int m = 0; m < Tr::NQ_PER; ++m) {
+        const int64_t back = q_tt[m] > lim ? q_tt[m] - lim : 0;
+        st_q[m] = load_sel<Real>(q_p[m], -back * NK, q_ok[m] && q_tt[m] <= lim);
+      }
+      const int64_t back = f_tt > lim ? f_tt - lim : 0;
+      st_f = load_sel<Real>(f_p, -back * N, tid < TC && f_tt <= lim);
+    }
 #pragma unroll
     for (int m = 0; m < Tr::NR1_PER; ++m) {
-      const int64_t t = tok(r1_tt[m]);
-      const bool in = full || t0 + r1_tt[m] < T;
-      st_r1[m][0] = load_sel<Real>(vp, r1_vofs[m] + t * NV, r1_vok[m] && in);
-      st_r1[m][1] = load_sel<Real>(kp, r1_kofs[m] + t * NK, r1_kok[m] && in);
+      r1_vp[m] += TC * NV;
+      r1_kp[m] += TC * NK;
     }
 #pragma unroll
-    for (int m = 0; m < Tr::NQ_PER; ++m) {
-      const int64_t t = tok(q_tt[m]);
-      const bool in = full || t0 + q_tt[m] < T;
-      st_q[m] = load_sel<Real>(qp, q_ofs[m] + t * NK, q_ok[m] && in);
-    }
-    {
-      const int tt = tid < TC ? tid : 0;
-      const int64_t t = tok(tt);
-      st_f = load_sel<Real>(fp, (tok0 + t * N), tid < TC && (full || t0 + tt < T));
-    }
+    for (int m = 0; m < Tr::NQ_PER; ++m) q_p[m] += TC * NK;
+    f_p += TC * N;
   };
-  auto store_chunk = [&](int64_t ch) {
-    const int base = (int)(ch & 1) * TC;
+  auto store_chunk = [&](int ch) {
+    const int base = (ch & 1) * TC;
 #pragma unroll
     for (int m = 0; m < Tr::NR1_PER; ++m) {
       const int e = tid + m * NT;
@@ -227,13 +278,14 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
     y_ofs[k] = (tok0 + (int64_t)y_tt[k] * N) * V + (j < V ? j : 0);
     y_wr[k] = j < V ? wrp[(int64_t)n * V + j] : Real(0);
   }
-  auto flush = [&](int64_t ch) {
-    const int64_t t0 = ch * TC;
-    const int base = (int)(ch & 1) * TC;
-    const int64_t cofs = t0 * NV;
+  // readouts of chunk ch; cofs = ch TC N V (the chunk's token offset), stepped per chunk
+  int64_t cofs = 0;
+  auto flush = [&](int ch) {
+    const int t0 = ch * TC;
+    const int base = (ch & 1) * TC;
 #pragma unroll
     for (int k = 0; k < NY_PER; ++k) {
-      if (y_ok[k] && t0 + y_tt[k] < T) {
+      if (y_ok[k] && t0 + y_tt[k] < T32) {
         const int slot = base + y_tt[k];
         const Real val = sm.y[slot][y_c[k]][y_g[k]][y_r[k]];
         if (nslab == 1) {
@@ -244,9 +296,10 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
         }
       }
     }
+    cofs += TC * NV;
   };
 
-  const int64_t nchunks = (T + TC - 1) / TC;
+  const int nchunks = (T32 + TC - 1) / TC;
   load_chunk(0);
   store_chunk(0);
   if (nchunks > 1) load_chunk(1);
@@ -351,57 +404,40 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
   // A whole chunk, unrolled.  Chunk ch + 1 is staged after step TC - 3, so
   // the barrier of step TC - 2 orders it before step TC - 1 reads its first
   // slot.  Inputs alternate between two StepIn buffers by step parity.
+  // Checkpoints are checked after every step (a countdown, on the scalar unit).
   StepIn ins[2];
-  // With a checkpoint interval C that divides TC (a power of two below TC),
-  // the checkpoints inside the chunk are written after steps I with
-  // (I + 1) mod C = 0; ck_in is then C - 1, else -1 (none inside chunks).
-  auto full_chunk = [&](int base, bool store_next, int64_t ch, int ck_in) {
+  auto full_chunk = [&](int base, int ch) {
     const int nbase = base ^ TC;
-    Real* const ckc = ck0 ? ck0 + (ch * TC / (ck_in + 1)) * K * V : nullptr;
+    const int t0 = ch * TC;
     [&]<int... I>(std::integer_sequence<int, I...>) {
       ((step(std::integral_constant<int, I & 1>{}, base + I, ins[I & 1], ins[(I + 1) & 1],
              I + 1 < TC ? base + I + 1 : nbase),
-        (I == TC - 3 && store_next ? store_chunk(ch + 1) : void()),
-        (I + 1 < TC && ck_in >= 0 && ((I + 1) & ck_in) == 0
-             ? write_state(ckc + ((I + 1) / (ck_in + 1)) * K * V)
-             : void())),
+        (I == TC - 3 ? store_chunk(ch + 1) : void()), ck_step(t0 + I)),
        ...);
     }(std::make_integer_sequence<int, TC>{});
   };
 
   ins[0] = read_in(0);
 
-  // Checkpoints fall between chunks when C is a multiple of TC; inside the
-  // unrolled chunk when C divides TC (C a power of two); else per step.
-  const bool ck_pow2_in = a.ckpt && a.C < TC && (TC % a.C) == 0;
-  const bool ck_at_chunks = !a.ckpt || (a.C % TC) == 0 || ck_pow2_in;
-  const int ck_in = ck_pow2_in ? (int)a.C - 1 : -1;
-  int64_t ch = 0;
-  for (; ch < nchunks; ++ch) {
-    const int64_t t0 = ch * TC;
-    const int base = (int)(ch & 1) * TC;
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int t0 = ch * TC;
+    const int base = (ch & 1) * TC;
     const bool last = ch + 1 == nchunks;
-    if (!last && ck_at_chunks) {
-      full_chunk(base, true, ch, ck_in);
+    if (!last) {
+      full_chunk(base, ch);
     } else {
-      // generic path: the partial last chunk, or checkpoints inside chunks
-      const int tn = (int)((T - t0) < TC ? (T - t0) : TC);
+      // the last chunk, possibly partial
+      const int tn = T32 - t0 < TC ? T32 - t0 : TC;
       for (int tt = 0; tt < tn; ++tt) {
         const int nslot = tt + 1 < TC ? base + tt + 1 : (base ^ TC);
         if ((tt & 1) == 0)
           step(std::integral_constant<int, 0>{}, base + tt, ins[0], ins[1], nslot);
         else
           step(std::integral_constant<int, 1>{}, base + tt, ins[1], ins[0], nslot);
-        if (tt == TC - 3 && !last) store_chunk(ch + 1);
-        const int64_t t = t0 + tt;
-        if (a.ckpt && (!ck_at_chunks || ck_pow2_in) && (t + 1) % a.C == 0 && t + 1 < T)
-          write_state(ck0 + ((t + 1) / a.C) * K * V);
+        ck_step(t0 + tt);
       }
     }
-    // ---- between chunks: checkpoint, write-back of this chunk, prefetch
-    const int64_t tend = t0 + TC;   // steps done after this chunk (if not last)
-    if (!last && a.ckpt && ck_at_chunks && tend % a.C == 0) write_state(ck0 + (tend / a.C) * K * V);
-    // (the generic path below writes its own checkpoints per step)
+    // ---- between chunks: write-back of this chunk, prefetch
     __syncthreads();                             // the chunk's last readout stores
     flush(ch);                                   // readouts of chunk ch are complete
     if (ch + 2 < nchunks) load_chunk(ch + 2);    // into registers; stored during chunk ch + 1
