@@ -204,36 +204,47 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
   }
   const int f_tt = tid < TC ? tid : 0;
   const Real* f_p = fp + tok0 + (int64_t)f_tt * N;
-  R2 st_r1[Tr::NR1_PER];
-  Real st_q[Tr::NQ_PER], st_f;
+  // Raw loaded values stay in registers until the LDS store during the next
+  // chunk (conversion and masking happen there), so nothing waits for the
+  // loads at the chunk boundary.
+  InT st_v[Tr::NR1_PER], st_k[Tr::NR1_PER], st_q[Tr::NQ_PER];
+  Real st_f;
+  bool st_in[Tr::NR1_PER], st_qin[Tr::NQ_PER], st_fin;  // step within T
   // load chunk ch (chunks in order: the pointers are at chunk ch on entry)
   auto load_chunk = [&](int ch) {
     const int t0 = ch * TC;
     if (t0 + TC <= T32) {
 #pragma unroll
       for (int m = 0; m < Tr::NR1_PER; ++m) {
-        st_r1[m][0] = load_sel<Real>(r1_vp[m], 0, r1_vok[m]);
-        st_r1[m][1] = load_sel<Real>(r1_kp[m], 0, r1_kok[m]);
+        st_v[m] = *r1_vp[m];
+        st_k[m] = *r1_kp[m];
+        st_in[m] = true;
       }
 #pragma unroll
-      for (int m = 0; m < Tr::NQ_PER; ++m) st_q[m] = load_sel<Real>(q_p[m], 0, q_ok[m]);
-      st_f = load_sel<Real>(f_p, 0, tid < TC);
+      for (int m = 0; m < Tr::NQ_PER; ++m) {
+        st_q[m] = *q_p[m];
+        st_qin[m] = true;
+      }
+      st_f = *f_p;
+      st_fin = true;
     } else {  // the last chunk: steps past T read step T - 1 and are masked
-      const int64_t lim = T32 - 1 - t0;  // last step of the chunk within T, relative
+      const int lim = T32 - 1 - t0;  // last step of the chunk within T, relative
 #pragma unroll
       for (int m = 0; m < Tr::NR1_PER; ++m) {
         const int64_t back = r1_tt[m] > lim ? r1_tt[m] - lim : 0;
-        const bool in = r1_tt[m] <= lim;
-        st_r1[m][0] = load_sel<Real>(r1_vp[m], -back * NV, r1_vok[m] && in);
-        st_r1[m][1] = load_sel<Real>(r1_kp[m], -back * NK, r1_kok[m] && in);
+        st_v[m] = r1_vp[m][-back * NV];
+        st_k[m] = r1_kp[m][-back * NK];
+        st_in[m] = r1_tt[m] <= lim;
       }
 #pragma unroll
       for (int m = 0; m < Tr::NQ_PER; ++m) {
         const int64_t back = q_tt[m] > lim ? q_tt[m] - lim : 0;
-        st_q[m] = load_sel<Real>(q_p[m], -back * NK, q_ok[m] && q_tt[m] <= lim);
+        st_q[m] = q_p[m][-back * NK];
+        st_qin[m] = q_tt[m] <= lim;
       }
       const int64_t back = f_tt > lim ? f_tt - lim : 0;
-      st_f = load_sel<Real>(f_p, -back * N, tid < TC && f_tt <= lim);
+      st_f = f_p[-back * N];
+      st_fin = f_tt <= lim;
     }
 #pragma unroll
     for (int m = 0; m < Tr::NR1_PER; ++m) {
@@ -244,19 +255,34 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
     for (int m = 0; m < Tr::NQ_PER; ++m) q_p[m] += TC * NK;
     f_p += TC * N;
   };
+  // a raw value, converted in a register (a select between a loaded value and
+  // zero is otherwise turned into a load from a select of addresses)
+  auto held = [&](auto x) -> Real {
+    Real y = (Real)widen(x);
+    asm volatile("" : "+v"(y));
+    return y;
+  };
   auto store_chunk = [&](int ch) {
     const int base = (ch & 1) * TC;
 #pragma unroll
     for (int m = 0; m < Tr::NR1_PER; ++m) {
       const int e = tid + m * NT;
-      if (e < TC * VP) sm.r1[base + e / VP][(e / 16) % VT][e % 16] = st_r1[m];
+      const Real vv = held(st_v[m]), kk = held(st_k[m]);
+      if (e < TC * VP)
+        sm.r1[base + e / VP][(e / 16) % VT][e % 16] =
+            R2{r1_vok[m] && st_in[m] ? vv : Real(0), r1_kok[m] && st_in[m] ? kk : Real(0)};
     }
 #pragma unroll
     for (int m = 0; m < Tr::NQ_PER; ++m) {
       const int e = tid + m * NT;
-      if (e < TC * 16) sm.q[base + e / 16][e % 16] = st_q[m];
+      const Real qq = held(st_q[m]);
+      if (e < TC * 16) sm.q[base + e / 16][e % 16] = q_ok[m] && st_qin[m] ? qq : Real(0);
     }
-    if (tid < TC) sm.fg[base + tid] = R2{st_f, Real(1) - st_f};
+    if (tid < TC) {
+      const Real ff = held(st_f);
+      const Real fv = st_fin ? ff : Real(0);
+      sm.fg[base + tid] = R2{fv, Real(1) - fv};
+    }
   };
   // write back one chunk of readouts (staged in lane order); element e of the
   // chunk is (step e / VP, lane-order column e % VP)
