@@ -43,7 +43,55 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the MFMA fraction of every workload")
     return ap.parse_args()
+
+
+def per_config_fractions(reps=3):
+    """Achieved fraction of the fp32 MFMA peak of every workload: the forward
+    call alone (no checkpoints) and, for the workload that defines a
+    checkpoint interval, the backward call from checkpoints at that interval.
+    Flops are the algorithmic ones (forward 2 K V^2, backward 4 K V^2 per token
+    and head)."""
+    import torch
+
+    from m2rnn_inputs import WORKLOADS, make_inputs, to_device
+    from matrix_state_nonlinear_amd import m2rnn_bwd, m2rnn_fwd, m2rnn_gates
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    rows = []
+    for wl in WORKLOADS.values():
+        inp = make_inputs(wl, with_dy=wl.C > 0)
+        d = to_device(inp, "float32")
+        f = m2rnn_gates(d["logit"], wl.gate, d["alpha"], d["beta"])
+        th = wl.B * wl.T * wl.N
+        ms = timed(lambda: m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"], None, 0))
+        tf = 2.0 * th * wl.K * wl.V * wl.V / (ms * 1e-3) / 1e12
+        row = {"workload": wl.name, "B": wl.B, "T": wl.T, "n_heads": wl.N, "K": wl.K, "V": wl.V,
+               "fwd_ms": ms, "fwd_tflops": tf, "fwd_mfma_frac": tf / MFMA_F32_PEAK_TFLOPS}
+        if wl.C > 0:
+            _, _, ck = m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"], None, wl.C)
+            ms = timed(lambda: m2rnn_bwd(d["k"], d["v"], d["q"], wl.gate, d["logit"], d["alpha"],
+                                         d["beta"], f, d["W"], d["w_r"], None, ck, wl.C, d["dy"]))
+            tf = 4.0 * th * wl.K * wl.V * wl.V / (ms * 1e-3) / 1e12
+            row.update({"C": wl.C, "bwd_ms": ms, "bwd_tflops": tf,
+                        "bwd_mfma_frac": tf / MFMA_F32_PEAK_TFLOPS})
+        rows.append(row)
+        del d, f, inp
+        torch.cuda.empty_cache()
+    return rows
 
 
 def oracle_baseline(wl, target_s):
@@ -189,11 +237,14 @@ def main():
         "roofline": {"bound": "mfma", "kernel": f"m2rnn_{dom} (whole call)", "achieved": dom_tf,
                      "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": dom_tf / MFMA_F32_PEAK_TFLOPS, "traffic": None},
-        "fwd_only": {"tokens_heads_per_s": kernels["fwd"]["tokens_heads_per_s"],
+        "fwd_only": {"checkpoint_interval": C,
+                     "tokens_heads_per_s": kernels["fwd"]["tokens_heads_per_s"],
                      "ms": avg_ms["fwd"], "mfma_frac": kernels["fwd"]["frac"],
                      "achieved_tflops": kernels["fwd"]["achieved_tflops"]},
         "kernels": kernels,
     }
+    if not args.no_per_config:
+        out["per_config"] = per_config_fractions()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = oracle_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
