@@ -16,20 +16,24 @@
 // kernels afterwards.
 //
 // Three wave roles per workgroup, one wave of each role on every SIMD, so the
-// three MFMA streams of a step share each SIMD's matrix unit and one role's
-// VALU and LDS work runs while another's MFMAs execute:
+// three MFMA streams of a step share each SIMD's matrix unit.  On gfx950 a
+// SIMD does not run fp32 MFMA and VALU work at the same time, not even for
+// different waves, so the roles do not buy overlap of VALU with MFMA: they
+// give the SIMD three independent dependency chains per step, which hide each
+// other's latencies (LDS round trips, dependent MFMA chains, the barrier).
 //  * forward role: reruns the recurrence chunk by chunk (S steps per chunk,
 //    chunks from last to first), each chunk from its stored start state, with
 //    exactly the forward kernel's arithmetic.  Every step's state S_{t+1} and
 //    rc_t = 1 / (1 + e^{2 A_t}) (tanh(A_t) = 1 - 2 rc_t) go into LDS rings;
-//    it also forms the lane partials of dq_t = S_{t+1} u_t.
+//    it forms the per-wave sums of dq_t = S_{t+1} u_t, and it finishes dq and
+//    dv (D^T k over the slab rows, by DPP) of the previous phase's steps.
 //  * reverse role: walks the chunk recomputed in the previous period from its
 //    last step to its first, one phase behind, carrying C through the MFMA
 //    product (D W^T)^T = W D^T; it publishes D (plain and transposed) and the
 //    lane partials of dk and df.
 //  * side role: accumulates dW += S_t^T D_t on MFMA one phase behind the
-//    reverse role, finishes dq, dk, dv and df and stores them, and stages the
-//    next chunk's inputs and start state from HBM into LDS.
+//    reverse role, finishes dk and df, and stages the next chunk's inputs and
+//    start state from HBM into LDS.
 // All roles finish one step per phase (one barrier per phase).  The rings hold
 // 2 S entries; no ring entry, staging slot or buffer is read and written in
 // the same phase (the schedule is replayed step by step on the host in the
