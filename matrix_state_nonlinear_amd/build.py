@@ -16,9 +16,12 @@ LIB = os.path.join(HERE, "libm2rnn.so")
 SOURCES = ["m2rnn_api.hip", "m2rnn_gates.hip", "m2rnn_fwd.hip", "m2rnn_bwd.hip"]
 ARCH = "gfx950"
 
-# Packed fp32 VALU instructions are switched off for every kernel.
+# Packed fp32 VALU instructions are switched off for every kernel.  MFMA
+# accumulators live in ordinary VGPRs (the step's VALU work reads them right
+# after the chain; AGPR accumulators would add a copy per element).
 HIP_FLAGS = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form",
              "-fno-gpu-rdc", "-Wall", "-Wno-unused-function"]
 
 

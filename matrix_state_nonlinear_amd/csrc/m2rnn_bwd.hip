@@ -159,14 +159,6 @@ BwdWorkspace bwd_workspace_layout(int64_t B, int64_t T, int64_t N, int64_t K, in
   return L;
 }
 
-// Four values of columns 16 c + m(g, r), r = 0..3, from a row of staged values
-// starting at column 16 c.
-__device__ __forceinline__ f32x4 cols4(const float* p, int g) {
-  return *(const f32x4*)(p + 4 * g);
-}
-__device__ __forceinline__ f64x4 cols4(const double* p, int g) {
-  return f64x4{p[g], p[4 + g], p[8 + g], p[12 + g]};
-}
 
 template <typename InT, typename Real, int VT>
 __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
@@ -207,7 +199,8 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
 
   if (role == 0) {
     // ================================================================ forward role
-    // W^T as the A operand, rotated so this wave's own tiles come first
+    // W^T as the A operand, rotated so this wave's own tiles come first and
+    // scaled by 2 / ln 2, exactly as in the forward kernel
     Real wop[TPW][NS];
 #pragma unroll
     for (int p = 0; p < TPW; ++p) {
@@ -216,7 +209,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
       for (int s0 = 0; s0 < NS; ++s0) {
         const int s = (s0 + 4 * TPW * wr) % NS;
         const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
-        wop[p][s0] = (col < V && l < V) ? Wp[((int64_t)n * V + l) * V + col] : Real(0);
+        wop[p][s0] = (col < V && l < V) ? kTanhScale<Real> * Wp[((int64_t)n * V + l) * V + col] : Real(0);
       }
     }
     // wait for these loads before the loop (a wait left for inside the loop
@@ -229,7 +222,6 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
     Real hb[NS];
 #pragma unroll
     for (int p = 0; p < TPW; ++p) h[p] = R4{0, 0, 0, 0};
-    const Real a_mask = g == 0 ? Real(1) : Real(0);
     // w_r of this lane's dv columns (completed here, see above); where a lane's
     // four columns are consecutive (fp32) dv is written with one 16-byte store
     Real wrc[TPW][4];
@@ -285,21 +277,17 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
         }
         const Real f = stp[OFF_F];
         const Real omf = Real(1) - f;
-        const Real kli = stp[li];
-        Real vli[TPW];
-#pragma unroll
-        for (int p = 0; p < TPW; ++p) vli[p] = stp[OFF_V + (wr * TPW + p) * 16 + li];
+        // the scaled rank-1 write k v^T starts the accumulators, as in the forward
+        const Real ks = kTanhScale<Real> * stp[li];
         R4 acc[TPW];
 #pragma unroll
-        for (int p = 0; p < TPW; ++p) acc[p] = R4{0, 0, 0, 0};
+        for (int p = 0; p < TPW; ++p) {
+          const R4 vv = cols4(stp + OFF_V + (wr * TPW + p) * 16, g);
 #pragma unroll
-        for (int s0 = 0; s0 < 4 * TPW; ++s0)
+          for (int r = 0; r < 4; ++r) acc[p][r] = ks * vv[r];
+        }
 #pragma unroll
-          for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wop[p][s0], hb[s0], acc[p]);
-#pragma unroll
-        for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(vli[p] * a_mask, kli, acc[p]);
-#pragma unroll
-        for (int s0 = 4 * TPW; s0 < NS; ++s0)
+        for (int s0 = 0; s0 < NS; ++s0)
 #pragma unroll
           for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wop[p][s0], hb[s0], acc[p]);
 #pragma unroll
@@ -311,7 +299,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
           R4 rc;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            rc[r] = sigmoid_neg2x(acc[p][r]);
+            rc[r] = tanh_rc_scaled(acc[p][r]);
             h[p][r] = fma_r(m2omf, rc[r], fma_r(f, h[p][r], omf));
           }
           sm.hr[(hbase + I + 1) & (M - 1)][wr * TPW + p][lane] = h[p];
@@ -824,7 +812,7 @@ __global__ void __launch_bounds__((BwdShape<Real, VT>::NW * 64))
     for (int s0 = 0; s0 < NS; ++s0) {
       const int s = (s0 + 4 * TPW * w) % NS;
       const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
-      wa[p][s0] = (col < V && l < V) ? Wp[((int64_t)n * V + l) * V + col] : Real(0);
+      wa[p][s0] = (col < V && l < V) ? kTanhScale<Real> * Wp[((int64_t)n * V + l) * V + col] : Real(0);
     }
   }
   const Real* ck = (const Real*)a.ckpt + (((int64_t)bn * nck + c) * K + (row_ok ? row : 0)) * V;
@@ -855,26 +843,22 @@ __global__ void __launch_bounds__((BwdShape<Real, VT>::NW * 64))
       }
   };
   if ((t0 & (S - 1)) == 0) write_start(t0);
-  const Real a_mask = g == 0 ? Real(1) : Real(0);
   for (int64_t t = t0; t < tend; ++t) {
     const int64_t tok = tok0 + t * N;
     const Real f = fp[tok];
     const Real kli = load_sel<Real>(kp, tok * K + (row_ok ? row : 0), row_ok);
+    // the scaled rank-1 write k v^T starts the accumulators, as in the forward
+    const Real ks = kTanhScale<Real> * kli;
     R4 acc[TPW];
 #pragma unroll
-    for (int p = 0; p < TPW; ++p) acc[p] = R4{0, 0, 0, 0};
+    for (int p = 0; p < TPW; ++p)
 #pragma unroll
-    for (int s0 = 0; s0 < 4 * TPW; ++s0)
+      for (int r = 0; r < 4; ++r) {
+        const int col = (w * TPW + p) * 16 + acc_m<Real>(g, r);
+        acc[p][r] = ks * load_sel<Real>(vp, tok * V + (col < V ? col : 0), col < V);
+      }
 #pragma unroll
-      for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wa[p][s0], hb[s0], acc[p]);
-#pragma unroll
-    for (int p = 0; p < TPW; ++p) {
-      const int col = (w * TPW + p) * 16 + li;
-      const Real vv = load_sel<Real>(vp, tok * V + (col < V ? col : 0), col < V);
-      acc[p] = mfma_16x16x4(vv * a_mask, kli, acc[p]);
-    }
-#pragma unroll
-    for (int s0 = 4 * TPW; s0 < NS; ++s0)
+    for (int s0 = 0; s0 < NS; ++s0)
 #pragma unroll
       for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wa[p][s0], hb[s0], acc[p]);
     const Real omf = Real(1) - f;
@@ -884,7 +868,7 @@ __global__ void __launch_bounds__((BwdShape<Real, VT>::NW * 64))
     for (int p = 0; p < TPW; ++p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        h[p][r] = fma_r(m2omf, sigmoid_neg2x(acc[p][r]), fma_r(f, h[p][r], omf));
+        h[p][r] = fma_r(m2omf, tanh_rc_scaled(acc[p][r]), fma_r(f, h[p][r], omf));
       xb[P][w * TPW + p][lane] = h[p];
     }
     __syncthreads();

@@ -67,22 +67,28 @@ __device__ __forceinline__ constexpr int acc_r(int m) {
 // e lies in (0, 1], so neither term overflows; 1 - e is exact for e near 1
 // (Sterbenz), which keeps the absolute error near 1e-7 over the whole line.
 // Uses the hardware base-2 exponential and reciprocal (about 1 ulp each).
-__device__ __forceinline__ float tanh_fast(float x) {
-  const float two_log2e = 2.885390081777926814f;  // 2 / ln 2
-  const float e = __builtin_amdgcn_exp2f(-two_log2e * __builtin_fabsf(x));
-  const float t = (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e);
-  return __builtin_copysignf(t, x);
-}
-__device__ __forceinline__ double tanh_fast(double x) { return ::tanh(x); }
+// The recurrence step works with the pre-activation scaled by 2 / ln 2,
+// A' = (2 / ln 2) A: W and the rank-1 term are scaled once (W when it is
+// loaded, k per step), so that the step's exponential needs no extra multiply.
+template <typename Real>
+constexpr Real kTanhScale = Real(2.8853900817779268147198493620037843);  // 2 / ln 2
 
-// 1 / (1 + e^{2x}), so that tanh(x) = 1 - 2 / (1 + e^{2x}).  For large |x| the
-// exponential saturates to inf or 0 and the result to 0 or 1, so the identity
-// still gives +-1.  fp32: hardware base-2 exponential and reciprocal.
-__device__ __forceinline__ float sigmoid_neg2x(float x) {
-  const float two_log2e = 2.885390081777926814f;  // 2 / ln 2
-  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(two_log2e * x));
+// rc = 1 / (1 + e^{2A}) from A' = (2 / ln 2) A, so that tanh(A) = 1 - 2 rc.  For
+// large |A| the exponential saturates to inf or 0 and rc to 0 or 1, so the
+// identity still gives +-1.  fp32: hardware base-2 exponential and reciprocal.
+__device__ __forceinline__ float tanh_rc_scaled(float xs) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(xs));
 }
-__device__ __forceinline__ double sigmoid_neg2x(double x) { return 1.0 / (1.0 + ::exp(2.0 * x)); }
+__device__ __forceinline__ double tanh_rc_scaled(double xs) { return 1.0 / (1.0 + ::exp2(xs)); }
+
+// Four values of columns 16 c + m(g, r), r = 0..3 (m the MFMA accumulator row
+// map), from a row of values starting at column 16 c.
+__device__ __forceinline__ f32x4 cols4(const float* p, int g) {
+  return *(const f32x4*)(p + 4 * g);
+}
+__device__ __forceinline__ f64x4 cols4(const double* p, int g) {
+  return f64x4{p[g], p[4 + g], p[8 + g], p[12 + g]};
+}
 
 // Forces `x` to be computed at this point of the program (an empty volatile
 // asm that reads and writes it cannot move across other volatile operations

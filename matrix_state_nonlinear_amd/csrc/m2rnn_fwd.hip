@@ -20,11 +20,13 @@
 // pi(s, g) = 16 (s / 4) + m(g, s % 4).  So a wave's own 16-column tiles never
 // leave registers, and the other tiles of the slab arrive through one 16-byte
 // LDS write and (VT / TPW - 1) 16-byte LDS reads per lane per step.  The
-// rank-1 write k v^T is one more MFMA whose contraction has a single non-zero
-// slice (A = v in lane group 0, zero elsewhere; B = k).
+// rank-1 write k v^T initialises the accumulators (one multiply per element).
+// The step works with the pre-activation scaled by 2 / ln 2 (W^T is scaled
+// when loaded, k per step), which the base-2 exponential of tanh takes as is.
 //
-// Step schedule.  On gfx950 a wave issues nothing else while its MFMA chain
-// runs, so every VALU instruction of a step adds to the step time.  The step
+// Step schedule.  On gfx950 fp32 MFMA and VALU work of a SIMD do not overlap
+// (not even for different waves), so every VALU instruction of a step adds to
+// the step time.  The step
 // is therefore: MFMAs (own tiles first: no LDS wait), tanh and the gate
 // interpolation, the exchange write, then the readout y_t = H_t^T q_t as a DPP
 // reduction over the 16 rows -- placed where the wave would otherwise wait for
@@ -52,9 +54,9 @@ struct FwdTraits {
   static constexpr int NS = 4 * VT;                  // MFMAs per tile per step (H W)
   static constexpr int TC = sizeof(Real) == 4 ? 16 : 8;   // steps per staging chunk (unrolled)
   static constexpr int RING = 2 * TC;                     // staging ring: two chunks
-  // per chunk: v and k as rank-1 operands [TC][VT][16], q [TC][16], f [TC]
-  static constexpr int NR1_PER = (TC * VT * 16 + NT - 1) / NT;   // (v, k) pairs per thread
-  static constexpr int NQ_PER = (TC * 16 + NT - 1) / NT;
+  // per chunk: v [TC][VP], k and q [TC][16], f [TC]
+  static constexpr int NV_PER = (TC * VP + NT - 1) / NT;   // v values per thread
+  static constexpr int NQ_PER = (TC * 16 + NT - 1) / NT;   // (k, q) pairs per thread
 };
 
 template <typename Real, int VT, int NW, int RING>
@@ -64,7 +66,8 @@ struct FwdSmem {
   R4 xb[2][VT][64];           // state exchange, double-buffered by step parity
   R4 y[RING][VT][4];          // readouts (this slab's rows), lane order [tile][g][r]
   R4 ydump[NW * 64];          // sink for readout stores of lanes that hold no result
-  R2 r1[RING][VT][16];        // rank-1 operands of a step: (v_{16 c + i}, k_i)
+  Real v[RING][16 * VT];      // v_j of a step
+  Real k[RING][16];           // k_i of a step (this slab's rows)
   R2 fg[RING];                // (f, 1 - f) of a step
   Real q[RING][16];           // q_i of a step
 };
@@ -103,7 +106,8 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
   const int64_t slab_stride = B * T * N * V;
   auto col_of = [&](int p, int r) { return (w * TPW + p) * 16 + acc_m<Real>(g, r); };
 
-  // ---- W^T as the MFMA A operand, rotated so this wave's own tiles come first.
+  // ---- W^T as the MFMA A operand, rotated so this wave's own tiles come first,
+  // scaled by 2 / ln 2 (the step works with the scaled pre-activation).
   Real wa[TPW][NS];
 #pragma unroll
   for (int p = 0; p < TPW; ++p) {
@@ -112,7 +116,7 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
     for (int s0 = 0; s0 < NS; ++s0) {
       const int s = (s0 + 4 * TPW * w) % NS;
       const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
-      wa[p][s0] = (col < V && l < V) ? Wp[((int64_t)n * V + l) * V + col] : Real(0);
+      wa[p][s0] = (col < V && l < V) ? kTanhScale<Real> * Wp[((int64_t)n * V + l) * V + col] : Real(0);
     }
   }
 
@@ -178,21 +182,18 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
   // one chunk (TC tokens) per load; the last, partial chunk clamps its steps
   // to T - 1 and masks them.  Loads are unconditional (all of a chunk's loads
   // are in flight at once).
-  const InT* r1_vp[Tr::NR1_PER];
-  const InT* r1_kp[Tr::NR1_PER];
+  const InT* v_p[Tr::NV_PER];
+  const InT* k_p[Tr::NQ_PER];
   const InT* q_p[Tr::NQ_PER];
-  int r1_tt[Tr::NR1_PER], q_tt[Tr::NQ_PER];
-  bool r1_vok[Tr::NR1_PER], r1_kok[Tr::NR1_PER], q_ok[Tr::NQ_PER];
+  int v_tt[Tr::NV_PER], q_tt[Tr::NQ_PER];
+  bool v_ok[Tr::NV_PER], q_ok[Tr::NQ_PER];
 #pragma unroll
-  for (int m = 0; m < Tr::NR1_PER; ++m) {
-    const int e = tid + m * NT;                      // [tt][c][i]
-    const int tt = e / VP, c = (e / 16) % VT, i = e % 16;
-    const int j = c * 16 + i, rr = slab * 16 + i;
-    r1_tt[m] = tt < TC ? tt : 0;
-    r1_vok[m] = tt < TC && j < V;
-    r1_kok[m] = tt < TC && rr < K;
-    r1_vp[m] = vp + tok0 * V + (j < V ? j : V - 1) + (int64_t)r1_tt[m] * NV;
-    r1_kp[m] = kp + tok0 * K + (rr < K ? rr : K - 1) + (int64_t)r1_tt[m] * NK;
+  for (int m = 0; m < Tr::NV_PER; ++m) {
+    const int e = tid + m * NT;                      // [tt][j]
+    const int tt = e / VP, j = e % VP;
+    v_tt[m] = tt < TC ? tt : 0;
+    v_ok[m] = tt < TC && j < V;
+    v_p[m] = vp + tok0 * V + (j < V ? j : V - 1) + (int64_t)v_tt[m] * NV;
   }
 #pragma unroll
   for (int m = 0; m < Tr::NQ_PER; ++m) {
@@ -200,6 +201,7 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
     const int tt = e / 16, i = e % 16, rr = slab * 16 + i;
     q_tt[m] = tt < TC ? tt : 0;
     q_ok[m] = tt < TC && rr < K;
+    k_p[m] = kp + tok0 * K + (rr < K ? rr : K - 1) + (int64_t)q_tt[m] * NK;
     q_p[m] = qp + tok0 * K + (rr < K ? rr : K - 1) + (int64_t)q_tt[m] * NK;
   }
   const int f_tt = tid < TC ? tid : 0;
@@ -207,21 +209,21 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
   // Raw loaded values stay in registers until the LDS store during the next
   // chunk (conversion and masking happen there), so nothing waits for the
   // loads at the chunk boundary.
-  InT st_v[Tr::NR1_PER], st_k[Tr::NR1_PER], st_q[Tr::NQ_PER];
+  InT st_v[Tr::NV_PER], st_k[Tr::NQ_PER], st_q[Tr::NQ_PER];
   Real st_f;
-  bool st_in[Tr::NR1_PER], st_qin[Tr::NQ_PER], st_fin;  // step within T
+  bool st_in[Tr::NV_PER], st_qin[Tr::NQ_PER], st_fin;  // step within T
   // load chunk ch (chunks in order: the pointers are at chunk ch on entry)
   auto load_chunk = [&](int ch) {
     const int t0 = ch * TC;
     if (t0 + TC <= T32) {
 #pragma unroll
-      for (int m = 0; m < Tr::NR1_PER; ++m) {
-        st_v[m] = *r1_vp[m];
-        st_k[m] = *r1_kp[m];
+      for (int m = 0; m < Tr::NV_PER; ++m) {
+        st_v[m] = *v_p[m];
         st_in[m] = true;
       }
 #pragma unroll
       for (int m = 0; m < Tr::NQ_PER; ++m) {
+        st_k[m] = *k_p[m];
         st_q[m] = *q_p[m];
         st_qin[m] = true;
       }
@@ -230,15 +232,15 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
     } else {  // the last chunk: steps past T read step T - 1 and are masked
       const int lim = T32 - 1 - t0;  // last step of the chunk within T, relative
 #pragma unroll
-      for (int m = 0; m < Tr::NR1_PER; ++m) {
-        const int64_t back = r1_tt[m] > lim ? r1_tt[m] - lim : 0;
-        st_v[m] = r1_vp[m][-back * NV];
-        st_k[m] = r1_kp[m][-back * NK];
-        st_in[m] = r1_tt[m] <= lim;
+      for (int m = 0; m < Tr::NV_PER; ++m) {
+        const int64_t back = v_tt[m] > lim ? v_tt[m] - lim : 0;
+        st_v[m] = v_p[m][-back * NV];
+        st_in[m] = v_tt[m] <= lim;
       }
 #pragma unroll
       for (int m = 0; m < Tr::NQ_PER; ++m) {
         const int64_t back = q_tt[m] > lim ? q_tt[m] - lim : 0;
+        st_k[m] = k_p[m][-back * NK];
         st_q[m] = q_p[m][-back * NK];
         st_qin[m] = q_tt[m] <= lim;
       }
@@ -247,12 +249,12 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
       st_fin = f_tt <= lim;
     }
 #pragma unroll
-    for (int m = 0; m < Tr::NR1_PER; ++m) {
-      r1_vp[m] += TC * NV;
-      r1_kp[m] += TC * NK;
-    }
+    for (int m = 0; m < Tr::NV_PER; ++m) v_p[m] += TC * NV;
 #pragma unroll
-    for (int m = 0; m < Tr::NQ_PER; ++m) q_p[m] += TC * NK;
+    for (int m = 0; m < Tr::NQ_PER; ++m) {
+      k_p[m] += TC * NK;
+      q_p[m] += TC * NK;
+    }
     f_p += TC * N;
   };
   // a raw value, converted in a register (a select between a loaded value and
@@ -265,18 +267,20 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
   auto store_chunk = [&](int ch) {
     const int base = (ch & 1) * TC;
 #pragma unroll
-    for (int m = 0; m < Tr::NR1_PER; ++m) {
+    for (int m = 0; m < Tr::NV_PER; ++m) {
       const int e = tid + m * NT;
-      const Real vv = held(st_v[m]), kk = held(st_k[m]);
-      if (e < TC * VP)
-        sm.r1[base + e / VP][(e / 16) % VT][e % 16] =
-            R2{r1_vok[m] && st_in[m] ? vv : Real(0), r1_kok[m] && st_in[m] ? kk : Real(0)};
+      const Real vv = held(st_v[m]);
+      if (e < TC * VP) sm.v[base + e / VP][e % VP] = v_ok[m] && st_in[m] ? vv : Real(0);
     }
 #pragma unroll
     for (int m = 0; m < Tr::NQ_PER; ++m) {
       const int e = tid + m * NT;
-      const Real qq = held(st_q[m]);
-      if (e < TC * 16) sm.q[base + e / 16][e % 16] = q_ok[m] && st_qin[m] ? qq : Real(0);
+      const Real kk = held(st_k[m]), qq = held(st_q[m]);
+      const bool ok = q_ok[m] && st_qin[m];
+      if (e < TC * 16) {
+        sm.k[base + e / 16][e % 16] = ok ? kk : Real(0);
+        sm.q[base + e / 16][e % 16] = ok ? qq : Real(0);
+      }
     }
     if (tid < TC) {
       const Real ff = held(st_f);
@@ -315,7 +319,7 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
         const int slot = base + y_tt[k];
         const Real val = sm.y[slot][y_c[k]][y_g[k]][y_r[k]];
         if (nslab == 1) {
-          const Real vv = sm.r1[slot][y_c[k]][acc_m<Real>(y_g[k], y_r[k])][0];
+          const Real vv = sm.v[slot][y_c[k] * 16 + acc_m<Real>(y_g[k], y_r[k])];
           yout[y_ofs[k] + cofs] = val + y_wr[k] * vv;
         } else {
           ypart[slab * slab_stride + y_ofs[k] + cofs] = val;
@@ -342,22 +346,21 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
     for (int r = 0; r < 4; ++r) hb[4 * q0 + r] = t4[r];
   }
 
-  // A-operand of the rank-1 MFMA: v in lane group 0, zero elsewhere (the mask
-  // is applied when the operand is formed).
-  const Real a_mask = g == 0 ? Real(1) : Real(0);
   R4* const ydump_me = &sm.ydump[tid];
 
   // Inputs of one step, read from the staging ring one step ahead of use so
   // their LDS latency is hidden behind the previous step's MFMA chain.
   struct StepIn {
-    R2 vk[TPW];   // rank-1 operands (v_{16 c + li}, k_li) of this wave's tiles
+    R4 v[TPW];    // v at this lane's columns 16 c + m(g, r) of this wave's tiles
+    Real k;       // k_li
     R2 fg;        // (f, 1 - f)
     Real q;       // q_li
   };
   auto read_in = [&](int slot) {
     StepIn in;
 #pragma unroll
-    for (int p = 0; p < TPW; ++p) in.vk[p] = sm.r1[slot][w * TPW + p][li];
+    for (int p = 0; p < TPW; ++p) in.v[p] = cols4(&sm.v[slot][(w * TPW + p) * 16], g);
+    in.k = sm.k[slot][li];
     in.fg = sm.fg[slot];
     in.q = sm.q[slot][li];
     return in;
@@ -368,24 +371,22 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
   auto step = [&](auto par, int slot, const StepIn& cur, StepIn& nxt, int nxt_slot) {
     constexpr int P = decltype(par)::value;
     nxt = read_in(nxt_slot);
+    // the rank-1 write k v^T (scaled) starts the accumulators; then the own
+    // tiles (operands in registers), then the tiles received through LDS
+    const Real ks = kTanhScale<Real> * cur.k;
     R4 acc[TPW];
 #pragma unroll
-    for (int p = 0; p < TPW; ++p) acc[p] = R4{0, 0, 0, 0};
-    // own tiles first (operands in registers), the rank-1 write, then the
-    // tiles received through LDS
-#pragma unroll
-    for (int s0 = 0; s0 < 4 * TPW; ++s0) {
-#pragma unroll
-      for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wa[p][s0], hb[s0], acc[p]);
-    }
-#pragma unroll
     for (int p = 0; p < TPW; ++p)
-      acc[p] = mfma_16x16x4(cur.vk[p][0] * a_mask, cur.vk[p][1], acc[p]);
 #pragma unroll
-    for (int s0 = 4 * TPW; s0 < NS; ++s0) {
+      for (int r = 0; r < 4; ++r) acc[p][r] = ks * cur.v[p][r];
+#pragma unroll
+    for (int s0 = 0; s0 < NS; ++s0) {
 #pragma unroll
       for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wa[p][s0], hb[s0], acc[p]);
     }
+    // the accumulators stay in VGPRs (read by the VALU right away)
+#pragma unroll
+    for (int p = 0; p < TPW; ++p) pin_vec(acc[p]);
     // H = f H + (1 - f) tanh(A), with tanh(A) = 1 - 2 / (1 + e^{2A}):
     // H = (f H + (1 - f)) - 2 (1 - f) / (1 + e^{2A}).  f = 1 gives H exactly.
     const Real m2omf = Real(-2) * cur.fg[1];
@@ -393,7 +394,7 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
     for (int p = 0; p < TPW; ++p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const Real rc = sigmoid_neg2x(acc[p][r]);
+        const Real rc = tanh_rc_scaled(acc[p][r]);
         hown[p][r] = fma_r(m2omf, rc, fma_r(cur.fg[0], hown[p][r], cur.fg[1]));
       }
       sm.xb[P][w * TPW + p][lane] = hown[p];
