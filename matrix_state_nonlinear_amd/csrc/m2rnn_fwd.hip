@@ -52,7 +52,7 @@ struct FwdTraits {
   static constexpr int TPW = VT / NW;                // 16-column tiles per wave
   static constexpr int NT = 64 * NW;                 // threads per workgroup
   static constexpr int NS = 4 * VT;                  // MFMAs per tile per step (H W)
-  static constexpr int TC = sizeof(Real) == 4 ? 16 : 8;   // steps per staging chunk (unrolled)
+  static constexpr int TC = sizeof(Real) == 4 ? (VT <= 4 ? 32 : 16) : 8;  // steps per staging chunk (unrolled)
   static constexpr int RING = 2 * TC;                     // staging ring: two chunks
   // per chunk: v [TC][VP], k and q [TC][16], f [TC]
   static constexpr int NV_PER = (TC * VP + NT - 1) / NT;   // v values per thread
