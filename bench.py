@@ -45,7 +45,36 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip the MFMA fraction of every workload")
+    ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
+                    help="first copy this many GiB twice with torch (a plain copy of known "
+                         "size, to calibrate HBM byte counters)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "m2rnn_bwd_long_t16k_k64_C4_hbm_traffic.md")
+BWD_SOURCES = ("m2rnn_bwd.hip", "m2rnn_device.h", "m2rnn_internal.h")
+
+
+def measured_bwd_traffic(workload, C):
+    """HBM bytes per m2rnn_bwd call from the committed counter summary, when it
+    applies: same workload and C, and the backward's sources unchanged since
+    the counters were taken (their sha256 is recorded with the figure)."""
+    import hashlib
+
+    if workload != "long_t16k_k64" or C != 4 or not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and line.split(":", 1)[0] in ("traffic_bytes_per_call", "source_sha256"):
+            k, v = line.split(":", 1)
+            fields[k] = v.strip()
+    h = hashlib.sha256()
+    for f in BWD_SOURCES:
+        with open(os.path.join(ROOT, "matrix_state_nonlinear_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_call" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_call"])
 
 
 def per_config_fractions(reps=3):
@@ -145,6 +174,16 @@ def main():
     from matrix_state_nonlinear_amd import m2rnn_bwd, m2rnn_fwd, m2rnn_gates
     from matrix_state_nonlinear_amd.ops import m2rnn_workspace_bytes
 
+    if args.copy_calibration_gib > 0:
+        n = int(args.copy_calibration_gib * (1 << 28))
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
+
     wl = WORKLOADS[args.workload]
     C = args.C
     B, T, N, K, V = wl.B, wl.T, wl.N, wl.K, wl.V
@@ -236,7 +275,8 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": f"m2rnn_{dom} (whole call)", "achieved": dom_tf,
                      "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": dom_tf / MFMA_F32_PEAK_TFLOPS, "traffic": None},
+                     "frac": dom_tf / MFMA_F32_PEAK_TFLOPS,
+                     "traffic": measured_bwd_traffic(wl.name, C) if dom == "bwd" else None},
         "fwd_only": {"checkpoint_interval": C,
                      "tokens_heads_per_s": kernels["fwd"]["tokens_heads_per_s"],
                      "ms": avg_ms["fwd"], "mfma_frac": kernels["fwd"]["frac"],
