@@ -929,7 +929,8 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-// dv = sum over slabs of the partials + w_r (.) dy
+// dv = sum over slabs of the partials + w_r (.) dy (64-bit indices, for sizes beyond
+// m2rnn_slab_sum_kernel's)
 template <typename Real>
 __global__ void __launch_bounds__(256)
     m2rnn_bwd_dv_kernel(int64_t total, int64_t N, int64_t V, int nslab,
@@ -958,8 +959,11 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-// Column sums over the B*T token rows, stage 1: one block per (row block, head).
-// Columns 0..V-1: dy (.) v (-> dw_r); V: -df softplus(x) f (-> dalpha); V+1: dlogit (-> dbeta).
+// Column sums over the B*T token rows, stage 1: one block per (row block of
+// 256 rows, head).  Columns 0..V-1: dy (.) v (-> dw_r); V: -df softplus(x) f
+// (-> dalpha); V+1: dlogit (-> dbeta).  The block's 256 threads are four row
+// groups (rows r0 + g, r0 + g + 4, ...) of 64 column slots; the four group
+// sums are added in a fixed order.
 template <typename InT, typename Real>
 __global__ void __launch_bounds__(256)
     m2rnn_bwd_colsum_kernel(int64_t rows, int64_t N, int64_t V, int kind,
@@ -968,20 +972,22 @@ __global__ void __launch_bounds__(256)
                             const Real* __restrict__ logit, const Real* __restrict__ alpha,
                             const Real* __restrict__ beta, const Real* __restrict__ dlogit,
                             Real* __restrict__ col_part) {
+  constexpr int kMaxCols = 16 * kMaxValueTiles + 2;
+  __shared__ Real red[4][kMaxCols];
   const int64_t rb = blockIdx.x;
   const int64_t n = blockIdx.y;
-  const int64_t ncol = V + 2;
+  const int ncol = (int)V + 2;
+  const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
   const int64_t r0 = rb * 256;
   const int64_t r1 = (r0 + 256) < rows ? (r0 + 256) : rows;
-  for (int64_t col = threadIdx.x; col < ncol; col += blockDim.x) {
+  const int64_t rstep = 4 * N * V;  // element step between rows r and r + 4
+  for (int col = lane; col < ncol; col += 64) {
     Real s = 0;
     if (col < V) {
-      for (int64_t r = r0; r < r1; ++r) {
-        const int64_t i = (r * N + n) * V + col;
-        s += dy[i] * load_as<Real>(v + i);
-      }
+      int64_t i = ((r0 + grp) * N + n) * V + col;
+      for (int64_t r = r0 + grp; r < r1; r += 4, i += rstep) s += dy[i] * load_as<Real>(v + i);
     } else if (kind == kGateExpSoftplus) {
-      for (int64_t r = r0; r < r1; ++r) {
+      for (int64_t r = r0 + grp; r < r1; r += 4) {
         const int64_t i = r * N + n;
         if (col == V) {
           s += -df[i] * softplus_(logit[i] + beta[n]) * f[i];
@@ -990,8 +996,11 @@ __global__ void __launch_bounds__(256)
         }
       }
     }
-    col_part[(rb * N + n) * ncol + col] = s;
+    red[grp][col] = s;
   }
+  __syncthreads();
+  for (int col = threadIdx.x; col < ncol; col += blockDim.x)
+    col_part[(rb * N + n) * ncol + col] = ((red[0][col] + red[1][col]) + red[2][col]) + red[3][col];
 }
 
 // stage 2: sum the row blocks in order
@@ -1061,9 +1070,15 @@ static hipError_t launch_bwd_vt(const BwdArgs& a0, hipStream_t stream) {
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (a.nslab > 1) {
     const int64_t total = tokens * a.V;
-    hipLaunchKernelGGL((m2rnn_bwd_dv_kernel<Real>), dim3(grid_for(total)), dim3(256), 0, stream,
-                       total, a.N, a.V, a.nslab, ws + L.dv_part, (const Real*)a.dy,
-                       (const Real*)a.w_r, (Real*)a.dv);
+    if (total < ((int64_t)1 << 31)) {
+      hipLaunchKernelGGL((m2rnn_slab_sum_kernel<Real, Real>), dim3(grid_for(total)), dim3(256), 0,
+                         stream, (int)tokens, (int)a.N, (int)a.V, a.nslab, total, ws + L.dv_part,
+                         (const Real*)a.dy, (const Real*)a.w_r, (Real*)a.dv);
+    } else {
+      hipLaunchKernelGGL((m2rnn_bwd_dv_kernel<Real>), dim3(grid_for(total)), dim3(256), 0, stream,
+                         total, a.N, a.V, a.nslab, ws + L.dv_part, (const Real*)a.dy,
+                         (const Real*)a.w_r, (Real*)a.dv);
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   const int64_t per = a.N * a.V * a.V;

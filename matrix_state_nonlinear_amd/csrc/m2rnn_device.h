@@ -240,4 +240,50 @@ __device__ __forceinline__ Real load_sel(const InT* p, int64_t i, bool ok) {
 }
 __device__ __forceinline__ int64_t clamp_idx(int64_t x, int64_t hi) { return x < hi ? x : hi; }
 
+// out[row][j] = sum over slabs sl of part[sl][row][j] (in slab order)
+//               + w_r[row mod N][j] * x[row][j],   rows = B T N token rows.
+// Elementwise and HBM-bound.  fp32 with V a multiple of 4: one 16-byte access
+// per array and thread; 32-bit indices (the launcher checks rows V < 2^31).
+template <typename InT, typename Real>
+__global__ void __launch_bounds__(256)
+    m2rnn_slab_sum_kernel(int rows, int N, int V, int nslab, int64_t slab_stride,
+                          const Real* __restrict__ part, const InT* __restrict__ x,
+                          const Real* __restrict__ w_r, Real* __restrict__ out) {
+  const int stride = gridDim.x * blockDim.x;
+  if (sizeof(Real) == 4 && (V & 3) == 0) {
+    const int cpr = V >> 2;  // 4-column groups per row
+    const int total = rows * cpr;
+    for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < total; c += stride) {
+      const int row = c / cpr;
+      const int j = (c - row * cpr) << 2;
+      const int n = row % N;
+      const int64_t i = (int64_t)row * V + j;
+      f32x4 acc = *(const f32x4*)((const float*)part + i);
+      for (int sl = 1; sl < nslab; ++sl) acc += *(const f32x4*)((const float*)part + sl * slab_stride + i);
+      const f32x4 w = *(const f32x4*)((const float*)w_r + (int64_t)n * V + j);
+      f32x4 xv;
+      if constexpr (sizeof(InT) == 2) {
+        const uint2 raw = *(const uint2*)(x + i);
+        xv = f32x4{__builtin_bit_cast(float, raw.x << 16), __builtin_bit_cast(float, raw.x & 0xffff0000u),
+                   __builtin_bit_cast(float, raw.y << 16), __builtin_bit_cast(float, raw.y & 0xffff0000u)};
+      } else {
+        xv = *(const f32x4*)((const float*)x + i);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(w[r], xv[r], acc[r]);
+      *(f32x4*)((float*)out + i) = acc;
+    }
+  } else {
+    const int total = rows * V;
+    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
+      const int row = e / V;
+      const int j = e - row * V;
+      const int n = row % N;
+      Real acc = part[e];
+      for (int sl = 1; sl < nslab; ++sl) acc += part[sl * slab_stride + e];
+      out[e] = fma_r(w_r[(int64_t)n * V + j], (Real)load_in(x + e), acc);
+    }
+  }
+}
+
 }  // namespace m2rnn

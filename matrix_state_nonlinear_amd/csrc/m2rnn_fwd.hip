@@ -472,7 +472,8 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
   if (a.HT) write_state((Real*)a.HT + state_base);
 }
 
-// y = sum over slabs of the partial readouts + w_r (.) v   (elementwise, HBM-bound)
+// y = sum over slabs of the partial readouts + w_r (.) v   (elementwise, HBM-bound;
+// 64-bit indices, for sizes beyond m2rnn_slab_sum_kernel's)
 template <typename InT, typename Real>
 __global__ void __launch_bounds__(256)
     m2rnn_fwd_reduce_kernel(int64_t total, int64_t N, int64_t V, int nslab,
@@ -500,9 +501,15 @@ static hipError_t launch_fwd_vt(const FwdArgs& a, hipStream_t stream) {
   const int64_t total = a.B * a.T * a.N * a.V;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL((m2rnn_fwd_reduce_kernel<InT, Real>), dim3((unsigned)blocks), dim3(256), 0,
-                     stream, total, a.N, a.V, a.nslab, (const Real*)a.ypart, (const InT*)a.v,
-                     (const Real*)a.w_r, (Real*)a.y);
+  if (total < ((int64_t)1 << 31)) {
+    hipLaunchKernelGGL((m2rnn_slab_sum_kernel<InT, Real>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, (int)(a.B * a.T * a.N), (int)a.N, (int)a.V, a.nslab, total,
+                       (const Real*)a.ypart, (const InT*)a.v, (const Real*)a.w_r, (Real*)a.y);
+  } else {
+    hipLaunchKernelGGL((m2rnn_fwd_reduce_kernel<InT, Real>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, total, a.N, a.V, a.nslab, (const Real*)a.ypart, (const InT*)a.v,
+                       (const Real*)a.w_r, (Real*)a.y);
+  }
   return hipGetLastError();
 }
 

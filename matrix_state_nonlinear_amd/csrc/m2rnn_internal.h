@@ -17,6 +17,9 @@ constexpr int kSlabRows = 16;
 
 inline int64_t num_slabs(int64_t K) { return (K + kSlabRows - 1) / kSlabRows; }
 
+// Largest value width V the kernels take, in 16-column tiles.
+constexpr int kMaxValueTiles = 8;
+
 // Value columns padded to the kernels' tile count (multiples of 16, with the
 // tile counts 5 and 7 rounded up to 6 and 8 so waves split them evenly).
 inline int value_tiles(int64_t V) {

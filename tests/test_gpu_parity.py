@@ -229,15 +229,16 @@ def test_backward_deterministic():
 
 @pytest.mark.parametrize("sd", ["float32", "float64"])
 def test_forward_checkpoints_every_c_steps_inside_chunks(sd):
-    """Checkpoint intervals that divide the forward's staging chunk are written
-    from inside the unrolled chunk: every checkpoint must equal the state the
-    per-step path (C = 1) stores, bit for bit, and the oracle's state."""
+    """Checkpoints are written after the step they follow, wherever it falls
+    in the forward's unrolled staging chunk (8, 16 or 32 steps): every
+    checkpoint must equal the state the per-step interval (C = 1) stores, bit
+    for bit, and the oracle's state.  T = 157 leaves a ragged last chunk."""
     wl = small("long_t16k_k64", T=157, B=2)
     inp = make_inputs(wl)
     _, f, y1, HT1, ck1 = gpu_forward(inp, sd, C=1)
     fo, o = oracle_forward(inp, C=1)
     assert maxerr(np_(ck1), o["ckpt"]) <= TOL_Y[sd]
-    for C in (2, 4, 8, 16):
+    for C in (2, 3, 4, 8, 16, 32, 33, 64):
         _, _, y, HT, ck = gpu_forward(inp, sd, C=C)
         assert torch.equal(y, y1) and torch.equal(HT, HT1), C
         assert torch.equal(ck, ck1[:, :, ::C].contiguous()), C
