@@ -209,15 +209,24 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
       for (int s0 = 0; s0 < NS; ++s0) {
         const int s = (s0 + 4 * TPW * wr) % NS;
         const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
-        wop[p][s0] = (col < V && l < V) ? kTanhScale<Real> * Wp[((int64_t)n * V + l) * V + col] : Real(0);
+        wop[p][s0] = Wp[((int64_t)n * V + (l < V ? l : 0)) * V + (col < V ? col : 0)];
       }
     }
     // wait for these loads before the loop (a wait left for inside the loop
-    // would also wait for the stores in flight there)
+    // would also wait for the stores in flight there), all together, then
+    // mask the padding (a guarded load would wait for itself at once)
 #pragma unroll
-    for (int p = 0; p < TPW; ++p)
+    for (int p = 0; p < TPW; ++p) {
+      const int col = (wr * TPW + p) * 16 + li;
 #pragma unroll
       for (int s0 = 0; s0 < NS; s0 += 4) pin_values(wop[p][s0], wop[p][s0 + 1], wop[p][s0 + 2], wop[p][s0 + 3]);
+#pragma unroll
+      for (int s0 = 0; s0 < NS; ++s0) {
+        const int s = (s0 + 4 * TPW * wr) % NS;
+        const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
+        wop[p][s0] = (col < V && l < V) ? kTanhScale<Real> * wop[p][s0] : Real(0);
+      }
+    }
     R4 h[TPW];
     Real hb[NS];
 #pragma unroll
@@ -394,7 +403,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
       for (int s0 = 0; s0 < NS; ++s0) {
         const int s = (s0 + 4 * TPW * wr) % NS;
         const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
-        wop[p][s0] = (col < V && l < V) ? Wp[((int64_t)n * V + col) * V + l] : Real(0);
+        wop[p][s0] = Wp[((int64_t)n * V + (col < V ? col : 0)) * V + (l < V ? l : 0)];
       }
     }
     R4 fR[TPW], Dp[TPW], rcn[TPW];
@@ -408,12 +417,20 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
       Dp[p] = R4{0, 0, 0, 0};
       rcn[p] = R4{0, 0, 0, 0};
     }
-    // complete the loads made before the loop here (see the forward role)
+    // complete the loads made before the loop here (see the forward role),
+    // then mask W's padding
 #pragma unroll
     for (int p = 0; p < TPW; ++p) {
 #pragma unroll
       for (int s0 = 0; s0 < NS; s0 += 4) pin_values(wop[p][s0], wop[p][s0 + 1], wop[p][s0 + 2], wop[p][s0 + 3]);
       pin_vec(fR[p]);
+      const int col = (wr * TPW + p) * 16 + li;
+#pragma unroll
+      for (int s0 = 0; s0 < NS; ++s0) {
+        const int s = (s0 + 4 * TPW * wr) % NS;
+        const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
+        wop[p][s0] = (col < V && l < V) ? wop[p][s0] : Real(0);
+      }
     }
     // transposed D: element (row li, column c) of a tile at [c][4 (li % 4) + li / 4]
     const int trow = 4 * (li & 3) + (li >> 2);
@@ -804,6 +821,9 @@ __global__ void __launch_bounds__((BwdShape<Real, VT>::NW * 64))
   const Real* __restrict__ fp = (const Real*)a.f;
   const Real* __restrict__ Wp = (const Real*)a.W;
 
+  // W^T (scaled) and the interval's start state: all loads from clamped
+  // addresses first, completed together, then masked (a guarded load would be
+  // a branch whose join waits for it, one load at a time)
   Real wa[TPW][NS];
 #pragma unroll
   for (int p = 0; p < TPW; ++p) {
@@ -812,7 +832,7 @@ __global__ void __launch_bounds__((BwdShape<Real, VT>::NW * 64))
     for (int s0 = 0; s0 < NS; ++s0) {
       const int s = (s0 + 4 * TPW * w) % NS;
       const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
-      wa[p][s0] = (col < V && l < V) ? kTanhScale<Real> * Wp[((int64_t)n * V + l) * V + col] : Real(0);
+      wa[p][s0] = Wp[((int64_t)n * V + (l < V ? l : 0)) * V + (col < V ? col : 0)];
     }
   }
   const Real* ck = (const Real*)a.ckpt + (((int64_t)bn * nck + c) * K + (row_ok ? row : 0)) * V;
@@ -824,7 +844,32 @@ __global__ void __launch_bounds__((BwdShape<Real, VT>::NW * 64))
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int col = 16 * q + acc_m<Real>(g, r);
-      hb[4 * q0 + r] = load_sel<Real>(ck, col < V ? col : 0, row_ok && col < V);
+      hb[4 * q0 + r] = ck[col < V ? col : 0];
+    }
+  }
+#pragma unroll
+  for (int s0 = 0; s0 < NS; s0 += 4) {
+#pragma unroll
+    for (int p = 0; p < TPW; ++p) pin_values(wa[p][s0], wa[p][s0 + 1], wa[p][s0 + 2], wa[p][s0 + 3]);
+    pin_values(hb[s0], hb[s0 + 1], hb[s0 + 2], hb[s0 + 3]);
+  }
+#pragma unroll
+  for (int p = 0; p < TPW; ++p) {
+    const int col = (w * TPW + p) * 16 + li;
+#pragma unroll
+    for (int s0 = 0; s0 < NS; ++s0) {
+      const int s = (s0 + 4 * TPW * w) % NS;
+      const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
+      wa[p][s0] = (col < V && l < V) ? kTanhScale<Real> * wa[p][s0] : Real(0);
+    }
+  }
+#pragma unroll
+  for (int q0 = 0; q0 < VT; ++q0) {
+    const int q = (q0 + TPW * w) % VT;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int col = 16 * q + acc_m<Real>(g, r);
+      hb[4 * q0 + r] = (row_ok && col < V) ? hb[4 * q0 + r] : Real(0);
     }
   }
 #pragma unroll
@@ -843,19 +888,47 @@ __global__ void __launch_bounds__((BwdShape<Real, VT>::NW * 64))
       }
   };
   if ((t0 & (S - 1)) == 0) write_start(t0);
-  for (int64_t t = t0; t < tend; ++t) {
+  // Inputs of a step, loaded raw one step ahead (from clamped addresses) so
+  // that their latency hides behind the previous step's MFMA chain.
+  InT kr, vr[TPW][4];
+  Real fr;
+  auto load_step = [&](int64_t t) {
     const int64_t tok = tok0 + t * N;
-    const Real f = fp[tok];
-    const Real kli = load_sel<Real>(kp, tok * K + (row_ok ? row : 0), row_ok);
+    fr = fp[tok];
+    kr = kp[tok * K + (row_ok ? row : 0)];
+#pragma unroll
+    for (int p = 0; p < TPW; ++p)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int col = (w * TPW + p) * 16 + acc_m<Real>(g, r);
+        vr[p][r] = vp[tok * V + (col < V ? col : 0)];
+      }
+  };
+  // a raw input converted in a register (kept there before any select)
+  auto held = [&](auto x) -> Real {
+    Real y = (Real)widen(x);
+    asm volatile("" : "+v"(y));
+    return y;
+  };
+  load_step(t0);
+  for (int64_t t = t0; t < tend; ++t) {
+    const Real f = held(fr);
+    const Real kli = held(kr);
+    Real vv[TPW][4];
+#pragma unroll
+    for (int p = 0; p < TPW; ++p)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vv[p][r] = held(vr[p][r]);
+    load_step(t + 1 < tend ? t + 1 : t);
     // the scaled rank-1 write k v^T starts the accumulators, as in the forward
-    const Real ks = kTanhScale<Real> * kli;
+    const Real ks = kTanhScale<Real> * (row_ok ? kli : Real(0));
     R4 acc[TPW];
 #pragma unroll
     for (int p = 0; p < TPW; ++p)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int col = (w * TPW + p) * 16 + acc_m<Real>(g, r);
-        acc[p][r] = ks * load_sel<Real>(vp, tok * V + (col < V ? col : 0), col < V);
+        acc[p][r] = ks * (col < V ? vv[p][r] : Real(0));
       }
 #pragma unroll
     for (int s0 = 0; s0 < NS; ++s0)

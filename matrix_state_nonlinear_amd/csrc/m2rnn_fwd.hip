@@ -116,7 +116,21 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
     for (int s0 = 0; s0 < NS; ++s0) {
       const int s = (s0 + 4 * TPW * w) % NS;
       const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
-      wa[p][s0] = (col < V && l < V) ? kTanhScale<Real> * Wp[((int64_t)n * V + l) * V + col] : Real(0);
+      wa[p][s0] = Wp[((int64_t)n * V + (l < V ? l : 0)) * V + (col < V ? col : 0)];
+    }
+  }
+  // the loads complete together, then the padding is masked (a guarded load
+  // would be a branch whose join waits for it, one load at a time)
+#pragma unroll
+  for (int p = 0; p < TPW; ++p) {
+    const int col = (w * TPW + p) * 16 + li;
+#pragma unroll
+    for (int s0 = 0; s0 < NS; s0 += 4) pin_values(wa[p][s0], wa[p][s0 + 1], wa[p][s0 + 2], wa[p][s0 + 3]);
+#pragma unroll
+    for (int s0 = 0; s0 < NS; ++s0) {
+      const int s = (s0 + 4 * TPW * w) % NS;
+      const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
+      wa[p][s0] = (col < V && l < V) ? kTanhScale<Real> * wa[p][s0] : Real(0);
     }
   }
 
