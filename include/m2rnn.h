@@ -31,9 +31,14 @@
  *   check returns its status and launches nothing.  Values on the device are
  *   not checked (f in [0, 1], alpha >= 0, finite inputs are preconditions).
  * - Launch failures are reported as M2RNN_ERR_HIP (hipGetLastError).
- * - Supported sizes: B, T, n_heads >= 1; 1 <= K <= 256; 1 <= V <= 128;
- *   B * n_heads * ceil(K / 16) <= 2^31 - 1.  Larger K or V return
- *   M2RNN_ERR_UNSUPPORTED.
+ * - Supported sizes: B, T, n_heads >= 0; 1 <= K <= 256; 1 <= V <= 128;
+ *   T < 2^30; B * n_heads * ceil(K / 16) < 2^22.  Other sizes return
+ *   M2RNN_ERR_UNSUPPORTED (negative ones, or K or V < 1,
+ *   M2RNN_ERR_INVALID_ARG).
+ * - Empty calls (B, T or n_heads = 0) are defined: nothing is recomputed, the
+ *   per-token arrays are empty (their pointers may be NULL), H_T = H_0 (zero
+ *   when H0 is NULL), dH_0 = dH_T (zero when dHT is NULL) and dW, dw_r,
+ *   dalpha, dbeta are zero (sums over no tokens).  They need no workspace.
  * - Results are bit-reproducible for the same inputs, sizes, device and build
  *   (every reduction runs in a fixed order, without atomics).
  */

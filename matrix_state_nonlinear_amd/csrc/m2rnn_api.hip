@@ -10,8 +10,10 @@ using namespace m2rnn;
 
 namespace {
 
+// B, T or n_heads may be 0 (an empty batch or sequence: nothing to recompute;
+// the per-head and state outputs still get their values); K and V may not.
 bool sizes_ok(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V) {
-  if (B < 1 || T < 1 || N < 1 || K < 1 || V < 1) return false;
+  if (B < 0 || T < 0 || N < 0 || K < 1 || V < 1) return false;
   // every element count the kernels index must stay far from int64 overflow
   const double elems = (double)B * (double)T * (double)N * (double)(K > V ? K : V);
   return elems < 4.0e18;
@@ -56,6 +58,28 @@ size_t bwd_ws_bytes(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V, int64
 
 int status_of(hipError_t e) { return e == hipSuccess ? M2RNN_OK : M2RNN_ERR_HIP; }
 
+// dst[0..n) = src[0..n), or zeros when src is NULL (outputs of empty calls)
+template <typename Real>
+__global__ void __launch_bounds__(256) fill_kernel(Real* __restrict__ dst,
+                                                   const Real* __restrict__ src, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    dst[i] = src ? src[i] : Real(0);
+}
+
+hipError_t fill(void* dst, const void* src, int64_t n, int state_dtype, hipStream_t stream) {
+  if (!dst || n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (state_dtype == M2RNN_F64)
+    hipLaunchKernelGGL(fill_kernel<double>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (double*)dst, (const double*)src, n);
+  else
+    hipLaunchKernelGGL(fill_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (float*)dst, (const float*)src, n);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" {
@@ -76,22 +100,25 @@ size_t m2rnn_workspace_bytes(int is_bwd, int64_t B, int64_t T, int64_t n_heads, 
   if (!sizes_ok(B, T, n_heads, K, V) || !sizes_supported(B, T, n_heads, K, V) ||
       !state_dtype_known(state_dtype) || (is_bwd && C < 1))
     return 0;
+  if (B * T * n_heads == 0) return 0;  // empty calls run no kernel that needs one
   return is_bwd ? bwd_ws_bytes(B, T, n_heads, K, V, C, state_dtype)
                 : fwd_ws_bytes(B, T, n_heads, K, V, state_dtype);
 }
 
 int m2rnn_gates(int64_t B, int64_t T, int64_t n_heads, int gate_kind, int dtype,
                 const void* logit, const void* alpha, const void* beta, void* f, void* stream) {
-  if (B < 1 || T < 1 || n_heads < 1) return M2RNN_ERR_INVALID_ARG;
+  if (B < 0 || T < 0 || n_heads < 0) return M2RNN_ERR_INVALID_ARG;
   if (dtype != M2RNN_F32 && dtype != M2RNN_F64) return M2RNN_ERR_INVALID_ARG;
-  if (!logit || !f) return M2RNN_ERR_INVALID_ARG;
+  const bool empty = B * T * n_heads == 0;
+  if (!empty && (!logit || !f)) return M2RNN_ERR_INVALID_ARG;
   if (gate_kind == M2RNN_GATE_SIGMOID) {
     if (alpha || beta) return M2RNN_ERR_INVALID_ARG;
   } else if (gate_kind == M2RNN_GATE_EXP_SOFTPLUS) {
-    if (!alpha || !beta) return M2RNN_ERR_INVALID_ARG;
+    if (!empty && (!alpha || !beta)) return M2RNN_ERR_INVALID_ARG;
   } else {
     return M2RNN_ERR_INVALID_ARG;
   }
+  if (empty) return M2RNN_OK;
   return status_of(launch_gates(B, T, n_heads, gate_kind, dtype, logit, alpha, beta, f,
                                 (hipStream_t)stream));
 }
@@ -102,10 +129,13 @@ int m2rnn_fwd(int64_t B, int64_t T, int64_t n_heads, int64_t K, int64_t V, int i
               int64_t C, void* workspace, size_t workspace_bytes, void* stream) {
   if (!sizes_ok(B, T, n_heads, K, V)) return M2RNN_ERR_INVALID_ARG;
   if (!in_dtype_known(in_dtype) || !state_dtype_known(state_dtype)) return M2RNN_ERR_INVALID_ARG;
-  if (!k || !v || !q || !f || !W || !w_r || !y) return M2RNN_ERR_INVALID_ARG;
+  const bool empty = B * T * n_heads == 0;
+  if (!empty && (!k || !v || !q || !f || !W || !w_r || !y)) return M2RNN_ERR_INVALID_ARG;
   if (ckpt && C < 1) return M2RNN_ERR_INVALID_ARG;
   if (!sizes_supported(B, T, n_heads, K, V) || !dtypes_ok(in_dtype, state_dtype))
     return M2RNN_ERR_UNSUPPORTED;
+  if (empty)  // no step: H_T = H_0 (zero when NULL); y and the checkpoints are empty
+    return status_of(fill(HT, H0, B * n_heads * K * V, state_dtype, (hipStream_t)stream));
   const size_t need = fwd_ws_bytes(B, T, n_heads, K, V, state_dtype);
   if (need && (!workspace || workspace_bytes < need)) return M2RNN_ERR_WORKSPACE;
   FwdArgs a{};
@@ -125,18 +155,34 @@ int m2rnn_bwd(int64_t B, int64_t T, int64_t n_heads, int64_t K, int64_t V, int i
               size_t workspace_bytes, void* stream) {
   if (!sizes_ok(B, T, n_heads, K, V)) return M2RNN_ERR_INVALID_ARG;
   if (!in_dtype_known(in_dtype) || !state_dtype_known(state_dtype)) return M2RNN_ERR_INVALID_ARG;
-  if (!k || !v || !q || !logit || !f || !W || !w_r || !ckpt || !dy) return M2RNN_ERR_INVALID_ARG;
-  if (!dk || !dv || !dq || !dlogit || !dW || !dw_r) return M2RNN_ERR_INVALID_ARG;
+  const bool empty = B * T * n_heads == 0;
+  const bool heads = n_heads > 0;  // per-head outputs exist
+  if (!empty && (!k || !v || !q || !logit || !f || !W || !w_r || !ckpt || !dy))
+    return M2RNN_ERR_INVALID_ARG;
+  if (!empty && (!dk || !dv || !dq || !dlogit)) return M2RNN_ERR_INVALID_ARG;
+  if (heads && (!dW || !dw_r)) return M2RNN_ERR_INVALID_ARG;
   if (C < 1) return M2RNN_ERR_INVALID_ARG;
   if (gate_kind == M2RNN_GATE_SIGMOID) {
     if (alpha || beta || dalpha || dbeta) return M2RNN_ERR_INVALID_ARG;
   } else if (gate_kind == M2RNN_GATE_EXP_SOFTPLUS) {
-    if (!alpha || !beta || !dalpha || !dbeta) return M2RNN_ERR_INVALID_ARG;
+    if (heads && (!dalpha || !dbeta)) return M2RNN_ERR_INVALID_ARG;
+    if (!empty && (!alpha || !beta)) return M2RNN_ERR_INVALID_ARG;
   } else {
     return M2RNN_ERR_INVALID_ARG;
   }
   if (!sizes_supported(B, T, n_heads, K, V) || !dtypes_ok(in_dtype, state_dtype))
     return M2RNN_ERR_UNSUPPORTED;
+  if (empty) {
+    // no step: dH_0 = dH_T (zero when NULL); dW, dw_r (and dalpha, dbeta) are
+    // sums over no tokens; the per-token gradients are empty
+    const hipStream_t st = (hipStream_t)stream;
+    hipError_t e = fill(dH0, dHT, B * n_heads * K * V, state_dtype, st);
+    if (e == hipSuccess) e = fill(dW, nullptr, n_heads * V * V, state_dtype, st);
+    if (e == hipSuccess) e = fill(dw_r, nullptr, n_heads * V, state_dtype, st);
+    if (e == hipSuccess) e = fill(dalpha, nullptr, n_heads, state_dtype, st);
+    if (e == hipSuccess) e = fill(dbeta, nullptr, n_heads, state_dtype, st);
+    return status_of(e);
+  }
   const size_t need = bwd_ws_bytes(B, T, n_heads, K, V, C, state_dtype);
   if (need && (!workspace || workspace_bytes < need)) return M2RNN_ERR_WORKSPACE;
   BwdArgs a{};

@@ -169,7 +169,7 @@ def backward(k, v, q, f, W, w_r, dy, H0=None, dHT=None, gate_kind=None,
     dH0 = np.empty((B, N, K, V), _f64)
     dW = np.zeros((N, V, V), _f64)
     WT = np.swapaxes(W, -1, -2)[None]
-    step = B if not b_group else b_group
+    step = max(1, B if not b_group else b_group)  # an empty batch has no groups
     for b0 in range(0, B, step):
         sl = slice(b0, min(B, b0 + step))
         st = forward(k[sl], v[sl], q[sl], f[sl], W, w_r,

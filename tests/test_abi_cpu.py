@@ -76,8 +76,10 @@ def fwd(L, **kw):
 
 def test_fwd_rejects_bad_arguments(L):
     E = _lib
-    assert fwd(L, B=0) == E.M2RNN_ERR_INVALID_ARG
+    assert fwd(L, B=-1) == E.M2RNN_ERR_INVALID_ARG
     assert fwd(L, T=-1) == E.M2RNN_ERR_INVALID_ARG
+    assert fwd(L, K=0) == E.M2RNN_ERR_INVALID_ARG
+    assert fwd(L, V=0) == E.M2RNN_ERR_INVALID_ARG
     assert fwd(L, k=None) == E.M2RNN_ERR_INVALID_ARG
     assert fwd(L, y=None) == E.M2RNN_ERR_INVALID_ARG
     assert fwd(L, ckpt=FAKE, C=0) == E.M2RNN_ERR_INVALID_ARG
@@ -90,10 +92,31 @@ def test_fwd_rejects_bad_arguments(L):
     assert fwd(L, K=64, ws=FAKE, wsb=16) == E.M2RNN_ERR_WORKSPACE
 
 
+def test_empty_calls_need_no_pointers_or_workspace(L):
+    """An empty batch or sequence is a defined call: the per-token arrays may be
+    NULL and no workspace is needed; with no state or per-head output to
+    write (HT, dH0 NULL, no heads) nothing is launched and the call succeeds
+    here, without a GPU."""
+    E = _lib
+    assert L.m2rnn_workspace_bytes(1, 0, 8, 2, 16, 16, 4, E.M2RNN_F32) == 0
+    assert L.m2rnn_workspace_bytes(0, 2, 0, 2, 64, 16, 4, E.M2RNN_F32) == 0
+    assert fwd(L, B=0, k=None, v=None, q=None, f=None, W=None, w_r=None, y=None,
+               HT=None, ckpt=None) == E.M2RNN_OK
+    assert fwd(L, T=0, K=64, HT=None, ckpt=FAKE, C=4) == E.M2RNN_OK
+    g = L.m2rnn_gates
+    assert g(2, 0, 2, E.M2RNN_GATE_SIGMOID, E.M2RNN_F32, None, None, None, None, None) == E.M2RNN_OK
+    assert g(2, 0, 2, E.M2RNN_GATE_EXP_SOFTPLUS, E.M2RNN_F32, None, None, None, None, None) == E.M2RNN_OK
+    assert bwd(L, N=0, k=None, v=None, q=None, logit=None, f=None, W=None, w_r=None, ckpt=None,
+               dy=None, dk=None, dv=None, dq=None, dlogit=None, dW=None, dw_r=None) == E.M2RNN_OK
+    # with heads, dW and dw_r are required (they are written even for no tokens)
+    assert bwd(L, T=0, dW=None) == E.M2RNN_ERR_INVALID_ARG
+    assert bwd(L, B=-1) == E.M2RNN_ERR_INVALID_ARG
+
+
 def test_gates_rejects_bad_arguments(L):
     E = _lib
     g = L.m2rnn_gates
-    assert g(0, 4, 2, E.M2RNN_GATE_SIGMOID, E.M2RNN_F32, FAKE, None, None, FAKE, None) == E.M2RNN_ERR_INVALID_ARG
+    assert g(-1, 4, 2, E.M2RNN_GATE_SIGMOID, E.M2RNN_F32, FAKE, None, None, FAKE, None) == E.M2RNN_ERR_INVALID_ARG
     assert g(1, 4, 2, E.M2RNN_GATE_SIGMOID, E.M2RNN_F32, FAKE, FAKE, None, FAKE, None) == E.M2RNN_ERR_INVALID_ARG
     assert g(1, 4, 2, E.M2RNN_GATE_EXP_SOFTPLUS, E.M2RNN_F32, FAKE, None, FAKE, FAKE, None) == E.M2RNN_ERR_INVALID_ARG
     assert g(1, 4, 2, 5, E.M2RNN_F32, FAKE, None, None, FAKE, None) == E.M2RNN_ERR_INVALID_ARG

@@ -242,3 +242,31 @@ def test_forward_checkpoints_every_c_steps_inside_chunks(sd):
         _, _, y, HT, ck = gpu_forward(inp, sd, C=C)
         assert torch.equal(y, y1) and torch.equal(HT, HT1), C
         assert torch.equal(ck, ck1[:, :, ::C].contiguous()), C
+
+
+# ---------------------------------------------------------------- empty calls
+
+@pytest.mark.parametrize("sd", ["float32", "float64"])
+@pytest.mark.parametrize("B,T,N", [(2, 0, 3), (0, 9, 3), (2, 9, 0)])
+def test_empty_batch_sequence_or_heads(B, T, N, sd):
+    """No steps or no rows: the oracle's results for zero tokens.  H_T is H_0
+    and dH_0 is dH_T (copied bit for bit), dW, dw_r, dalpha and dbeta are zero,
+    and the per-token outputs and checkpoints are empty."""
+    wl = WORKLOADS["fwd_bwd_k32_v128"].replace(B=B, T=T, N=N, K=20, V=24)
+    inp = make_inputs(wl, with_dy=True, with_h0=True, with_dht=True)
+    C = 4
+    d, f, y, HT, ckpt = gpu_forward(inp, sd, C=C)
+    _, o = oracle_forward(inp, C=C)
+    assert tuple(y.shape) == o["y"].shape and tuple(ckpt.shape) == o["ckpt"].shape
+    assert torch.equal(HT, d["H0"])
+    g = m2rnn_bwd(d["k"], d["v"], d["q"], wl.gate, d["logit"], d["alpha"], d["beta"], f,
+                  d["W"], d["w_r"], d["H0"], ckpt, C, d["dy"], d["dHT"])
+    torch.cuda.synchronize()
+    ref = oracle_backward(inp)
+    assert torch.equal(g["dH0"], d["dHT"])
+    for name, r in ref.items():
+        if name == "df" or r is None:
+            continue
+        assert tuple(g[name].shape) == r.shape, name
+        if r.size and name != "dH0":
+            assert not np.any(r) and not torch.any(g[name]), name
