@@ -226,6 +226,9 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
         const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
         wop[p][s0] = (col < V && l < V) ? kTanhScale<Real> * wop[p][s0] : Real(0);
       }
+      // the final operands are held in registers (not recomputed in the loop)
+#pragma unroll
+      for (int s0 = 0; s0 < NS; s0 += 4) pin_values(wop[p][s0], wop[p][s0 + 1], wop[p][s0 + 2], wop[p][s0 + 3]);
     }
     R4 h[TPW];
     Real hb[NS];
@@ -431,6 +434,8 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
         const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
         wop[p][s0] = (col < V && l < V) ? wop[p][s0] : Real(0);
       }
+#pragma unroll
+      for (int s0 = 0; s0 < NS; s0 += 4) pin_values(wop[p][s0], wop[p][s0 + 1], wop[p][s0 + 2], wop[p][s0 + 3]);
     }
     // transposed D: element (row li, column c) of a tile at [c][4 (li % 4) + li / 4]
     const int trow = 4 * (li & 3) + (li >> 2);
@@ -862,6 +867,8 @@ __global__ void __launch_bounds__((BwdShape<Real, VT>::NW * 64))
       const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
       wa[p][s0] = (col < V && l < V) ? kTanhScale<Real> * wa[p][s0] : Real(0);
     }
+#pragma unroll
+    for (int s0 = 0; s0 < NS; s0 += 4) pin_values(wa[p][s0], wa[p][s0 + 1], wa[p][s0 + 2], wa[p][s0 + 3]);
   }
 #pragma unroll
   for (int q0 = 0; q0 < VT; ++q0) {

@@ -132,6 +132,9 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
       const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
       wa[p][s0] = (col < V && l < V) ? kTanhScale<Real> * wa[p][s0] : Real(0);
     }
+    // the final operands are held in registers (not recomputed in the loop)
+#pragma unroll
+    for (int s0 = 0; s0 < NS; s0 += 4) pin_values(wa[p][s0], wa[p][s0 + 1], wa[p][s0 + 2], wa[p][s0 + 3]);
   }
 
   // ---- initial state: own tiles hold row `row`, columns 16 c + m(g, r).
