@@ -17,6 +17,9 @@ Sources (cited by title and section):
 
 Layouts (token-major, C-contiguous):
   k, q  [B, T, N, K]      v, dy, y  [B, T, N, V]      f, logit  [B, T, N]
+        or [B, T, NQ, K] with NQ dividing N: q and k shared by groups of
+        N / NQ consecutive value heads ([R] section 2.4 shares one q and one k
+        across all value heads, NQ = 1)
   W     [N, V, V]  with (H W)[i, j] = sum_l H[i, l] W[l, j]
   w_r   [N, V]            H0, HT, dHT  [B, N, K, V]
   ckpt  [B, N, ceil(T / C), K, V], ckpt[:, :, c] = H_{cC} (H_0 = H0)
@@ -91,6 +94,25 @@ def gate_partials(kind, logit, alpha=None, beta=None):
     return f, dfa, -softplus(x) * f, dfa
 
 
+def _expand_qk(x, N):
+    """Shared q / k ([R] section 2.4): value head n reads q/k head n // (N / NQ).
+    Returns the per-value-head array [B, T, N, K]."""
+    NQ = x.shape[2]
+    if NQ == N:
+        return x
+    assert NQ > 0 and N % NQ == 0, (NQ, N)
+    return np.repeat(x, N // NQ, axis=2)
+
+
+def _reduce_qk(g, NQ):
+    """Gradient of a shared q / k: the sum over the value heads that read it
+    (chain rule), in head order."""
+    B, T, N, K = g.shape
+    if NQ == N:
+        return g
+    return g.reshape(B, T, NQ, N // NQ, K).sum(axis=3)
+
+
 def forward(k, v, q, f, W, w_r, H0=None, C=0, keep_states=False):
     """M²RNN forward, [R] section 2.1 Eq. (10)-(12), [P] "Recurrence":
 
@@ -103,6 +125,7 @@ def forward(k, v, q, f, W, w_r, H0=None, C=0, keep_states=False):
     and Z [T, B, N, K, V].
     """
     k, v, q, f, W, w_r = map(_a, (k, v, q, f, W, w_r))
+    k, q = _expand_qk(k, v.shape[2]), _expand_qk(q, v.shape[2])
     B, T, N, K = k.shape
     V = v.shape[-1]
     H = np.zeros((B, N, K, V), _f64) if H0 is None else _a(H0).copy()
@@ -160,6 +183,8 @@ def backward(k, v, q, f, W, w_r, dy, H0=None, dHT=None, gate_kind=None,
     parameter gradients are summed across the groups).
     """
     k, v, q, f, W, w_r, dy = map(_a, (k, v, q, f, W, w_r, dy))
+    NQ = k.shape[2]
+    k, q = _expand_qk(k, v.shape[2]), _expand_qk(q, v.shape[2])
     B, T, N, K = k.shape
     V = v.shape[-1]
     dk = np.empty((B, T, N, K), _f64)
@@ -192,7 +217,7 @@ def backward(k, v, q, f, W, w_r, dy, H0=None, dHT=None, gate_kind=None,
             Cst = ft * R + np.matmul(D, WT)
         dH0[sl] = Cst
         del Hs, Zs, st
-    out = {"dk": dk, "dv": dv, "dq": dq, "df": df, "dW": dW,
+    out = {"dk": _reduce_qk(dk, NQ), "dv": dv, "dq": _reduce_qk(dq, NQ), "df": df, "dW": dW,
            "dw_r": np.sum(dy * v, axis=(0, 1)), "dH0": dH0}
     if gate_kind is not None:
         _, dfl, dfa, dfb = gate_partials(gate_kind, logit, alpha, beta)

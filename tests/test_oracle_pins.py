@@ -361,6 +361,68 @@ def test_backward_matches_torch_autograd(name):
         np.testing.assert_allclose(g[gname], ref, rtol=0, atol=1e-11 * scale, err_msg=gname)
 
 
+@pytest.mark.parametrize("NQ", [1, 2])
+def test_shared_qk_matches_torch_autograd(NQ):
+    # q and k shared by groups of N / NQ value heads ([R] section 2.4): torch
+    # repeats each shared head over its group and autograd sums the gradient
+    # over the group by itself.
+    rng = np.random.default_rng(70 + NQ)
+    B, T, N, K, V = 2, 9, 4, 3, 5
+    c = _rand_case(80 + NQ, B=B, T=T, N=N, K=K, V=V)
+    c["k"] = rng.standard_normal((B, T, NQ, K)) * 0.7
+    c["q"] = rng.standard_normal((B, T, NQ, K))
+    dy = rng.standard_normal((B, T, N, V))
+    dHT = rng.standard_normal((B, N, K, V))
+    tt = lambda a: torch.from_numpy(np.asarray(a, np.float64).copy()).requires_grad_(True)  # noqa: E731
+    k, q, v, f, W, w_r, H0 = map(tt, (c["k"], c["q"], c["v"], c["f"], c["W"], c["w_r"],
+                                     c["H0"]))
+    y, HT = _torch_forward(torch.repeat_interleave(k, N // NQ, dim=2), v,
+                           torch.repeat_interleave(q, N // NQ, dim=2), f, W, w_r, H0)
+    loss = (y * torch.from_numpy(dy)).sum() + (HT * torch.from_numpy(dHT)).sum()
+    loss.backward()
+    o = oracle.forward(c["k"], c["v"], c["q"], c["f"], c["W"], c["w_r"], c["H0"])
+    np.testing.assert_allclose(o["y"], y.detach().numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(o["HT"], HT.detach().numpy(), rtol=1e-12, atol=1e-13)
+    g = oracle.backward(c["k"], c["v"], c["q"], c["f"], c["W"], c["w_r"], dy, c["H0"], dHT)
+    assert g["dk"].shape == (B, T, NQ, K) and g["dq"].shape == (B, T, NQ, K)
+    for gname, tens in [("dk", k), ("dq", q), ("dv", v), ("df", f), ("dW", W),
+                        ("dw_r", w_r), ("dH0", H0)]:
+        ref = tens.grad.numpy()
+        np.testing.assert_allclose(g[gname], ref, rtol=0,
+                                   atol=1e-11 * max(1.0, np.abs(ref).max()), err_msg=gname)
+
+
+def test_shared_qk_central_differences():
+    # Brute force on the shared operands: every element of a q and k shared by
+    # all value heads (NQ = 1), central differences in float64.
+    rng = np.random.default_rng(91)
+    B, T, N, K, V = 1, 4, 3, 2, 3
+    c = _rand_case(92, B=B, T=T, N=N, K=K, V=V)
+    c["k"] = rng.standard_normal((B, T, 1, K)) * 0.7
+    c["q"] = rng.standard_normal((B, T, 1, K))
+    dy = rng.standard_normal((B, T, N, V))
+    dHT = rng.standard_normal((B, N, K, V))
+
+    def loss():
+        o = oracle.forward(c["k"], c["v"], c["q"], c["f"], c["W"], c["w_r"], c["H0"])
+        return float(np.sum(o["y"] * dy) + np.sum(o["HT"] * dHT))
+
+    g = oracle.backward(c["k"], c["v"], c["q"], c["f"], c["W"], c["w_r"], dy, c["H0"], dHT)
+    h = 1e-6
+    for name in ("k", "q"):
+        arr = c[name]
+        fd = np.empty(arr.shape)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + h
+            lp = loss()
+            arr[idx] = old - h
+            lm = loss()
+            arr[idx] = old
+            fd[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g["d" + name], fd, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
 # ---------------------------------------------------------------- sensitivity helper
 
 def test_tangent_growth_linear_regime_closed_form():
