@@ -79,7 +79,7 @@ def measured_bwd_traffic(workload, C):
 
 def per_config_fractions(reps=3):
     """Achieved fraction of the fp32 MFMA peak of every workload: the forward
-    call alone (no checkpoints) and, for the workload that defines a
+    call alone (no checkpoints) and, for the workloads that define a
     checkpoint interval, the backward call from checkpoints at that interval.
     Flops are the algorithmic ones (forward 2 K V^2, backward 4 K V^2 per token
     and head)."""
@@ -108,7 +108,8 @@ def per_config_fractions(reps=3):
         th = wl.B * wl.T * wl.N
         ms = timed(lambda: m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"], None, 0))
         tf = 2.0 * th * wl.K * wl.V * wl.V / (ms * 1e-3) / 1e12
-        row = {"workload": wl.name, "B": wl.B, "T": wl.T, "n_heads": wl.N, "K": wl.K, "V": wl.V,
+        row = {"workload": wl.name, "B": wl.B, "T": wl.T, "n_heads": wl.N,
+               "qk_heads": wl.qk_heads, "K": wl.K, "V": wl.V,
                "fwd_ms": ms, "fwd_tflops": tf, "fwd_mfma_frac": tf / MFMA_F32_PEAK_TFLOPS}
         if wl.C > 0:
             _, _, ck = m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"], None, wl.C)
@@ -195,10 +196,11 @@ def main():
     y = torch.empty((B, T, N, V), dtype=torch.float32, device=dev)
     HT = torch.empty((B, N, K, V), dtype=torch.float32, device=dev)
     ckpt = torch.empty((B, N, (T + C - 1) // C, K, V), dtype=torch.float32, device=dev)
-    wsf = torch.empty(max(1, m2rnn_workspace_bytes(False, B, T, N, K, V, C)), dtype=torch.uint8,
-                      device=dev)
-    wsb = torch.empty(max(1, m2rnn_workspace_bytes(True, B, T, N, K, V, C)), dtype=torch.uint8,
-                      device=dev)
+    NQ = wl.qk_heads
+    wsf = torch.empty(max(1, m2rnn_workspace_bytes(False, B, T, N, NQ, K, V, C)),
+                      dtype=torch.uint8, device=dev)
+    wsb = torch.empty(max(1, m2rnn_workspace_bytes(True, B, T, N, NQ, K, V, C)),
+                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     names = ("gates", "fwd", "bwd")
@@ -269,7 +271,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "B": B, "T": T, "n_heads": N, "K": K, "V": V,
+        "config": {"workload": wl.name, "B": B, "T": T, "n_heads": N, "qk_heads": NQ, "K": K, "V": V,
                    "C": C, "kvq_dtype": "bf16" if wl.bf16 else "f32", "state_dtype": "f32",
                    "gate": "exp_softplus" if wl.gate == 1 else "sigmoid",
                    "parallelism": "single GPU"},

@@ -31,6 +31,12 @@
  *   check returns its status and launches nothing.  Values on the device are
  *   not checked (f in [0, 1], alpha >= 0, finite inputs are preconditions).
  * - Launch failures are reported as M2RNN_ERR_HIP (hipGetLastError).
+ * - q and k have `qk_heads` heads shared by groups of n_heads / qk_heads
+ *   consecutive value heads: value head n reads q/k head n / (n_heads / qk_heads),
+ *   so dq and dk of a shared head sum over its group (the review's section 2.4
+ *   multi-value layout is qk_heads = 1; qk_heads = n_heads gives every head its
+ *   own q and k).  qk_heads must divide n_heads (1 <= qk_heads <= n_heads; both
+ *   are 0 for a call with no heads), else M2RNN_ERR_INVALID_ARG.
  * - Supported sizes: B, T, n_heads >= 0; 1 <= K <= 256; 1 <= V <= 128;
  *   T < 2^30; B * n_heads * ceil(K / 16) < 2^22.  Other sizes return
  *   M2RNN_ERR_UNSUPPORTED (negative ones, or K or V < 1,
@@ -89,13 +95,14 @@ int m2rnn_gates(int64_t B, int64_t T, int64_t n_heads, int gate_kind, int dtype,
  * used for the backward); 0 means none (workspace may be NULL).  Returns 0 as
  * well for sizes the library rejects.
  */
-size_t m2rnn_workspace_bytes(int is_bwd, int64_t B, int64_t T, int64_t n_heads, int64_t K,
-                             int64_t V, int64_t C, int state_dtype);
+size_t m2rnn_workspace_bytes(int is_bwd, int64_t B, int64_t T, int64_t n_heads,
+                             int64_t qk_heads, int64_t K, int64_t V, int64_t C,
+                             int state_dtype);
 
 /*
  * m2rnn_fwd -- the recurrence and readout of review section 2.1, Eq. (10)-(12),
  * for all B * n_heads units, from H0 (or zero), over T steps.
- *   k, q   [B, T, n_heads, K]   in, in_dtype
+ *   k, q   [B, T, qk_heads, K]  in, in_dtype
  *   v      [B, T, n_heads, V]   in, in_dtype
  *   f      [B, T, n_heads]      in, forget gate (from m2rnn_gates)
  *   W      [n_heads, V, V]      in, (H W)[i][j] = sum_l H[i][l] * W[n][l][j]
@@ -110,10 +117,10 @@ size_t m2rnn_workspace_bytes(int is_bwd, int64_t B, int64_t T, int64_t n_heads, 
  *   C      checkpoint interval, >= 1 when ckpt != NULL
  *   workspace / workspace_bytes: at least m2rnn_workspace_bytes(0, ...)
  */
-int m2rnn_fwd(int64_t B, int64_t T, int64_t n_heads, int64_t K, int64_t V, int in_dtype,
-              int state_dtype, const void* k, const void* v, const void* q, const void* f,
-              const void* W, const void* w_r, const void* H0, void* y, void* HT, void* ckpt,
-              int64_t C, void* workspace, size_t workspace_bytes, void* stream);
+int m2rnn_fwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K, int64_t V,
+              int in_dtype, int state_dtype, const void* k, const void* v, const void* q,
+              const void* f, const void* W, const void* w_r, const void* H0, void* y, void* HT,
+              void* ckpt, int64_t C, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * m2rnn_bwd -- reverse-time backward of m2rnn_fwd for a loss L with
@@ -134,7 +141,7 @@ int m2rnn_fwd(int64_t B, int64_t T, int64_t n_heads, int64_t K, int64_t V, int i
  *   ckpt   [B, n_heads, ceil(T / C), K, V]  in, from m2rnn_fwd with the same C, H0, inputs
  *   dy     [B, T, n_heads, V]   in
  *   dHT    [B, n_heads, K, V]   in, or NULL for zero
- *   dk, dq [B, T, n_heads, K]   out, state_dtype
+ *   dk, dq [B, T, qk_heads, K]  out, state_dtype (a shared head's sum over its group)
  *   dv     [B, T, n_heads, V]   out
  *   dlogit [B, T, n_heads]      out, dL/dlogit (sigmoid: g; exp-softplus: a)
  *   dW     [n_heads, V, V]      out, summed over batch and time
@@ -143,13 +150,13 @@ int m2rnn_fwd(int64_t B, int64_t T, int64_t n_heads, int64_t K, int64_t V, int i
  *   dH0    [B, n_heads, K, V]   out, or NULL to skip
  *   workspace / workspace_bytes: at least m2rnn_workspace_bytes(1, ...)
  */
-int m2rnn_bwd(int64_t B, int64_t T, int64_t n_heads, int64_t K, int64_t V, int in_dtype,
-              int state_dtype, const void* k, const void* v, const void* q, int gate_kind,
-              const void* logit, const void* alpha, const void* beta, const void* f,
-              const void* W, const void* w_r, const void* H0, const void* ckpt, int64_t C,
-              const void* dy, const void* dHT, void* dk, void* dv, void* dq, void* dlogit,
-              void* dW, void* dw_r, void* dalpha, void* dbeta, void* dH0, void* workspace,
-              size_t workspace_bytes, void* stream);
+int m2rnn_bwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K, int64_t V,
+              int in_dtype, int state_dtype, const void* k, const void* v, const void* q,
+              int gate_kind, const void* logit, const void* alpha, const void* beta,
+              const void* f, const void* W, const void* w_r, const void* H0, const void* ckpt,
+              int64_t C, const void* dy, const void* dHT, void* dk, void* dv, void* dq,
+              void* dlogit, void* dW, void* dw_r, void* dalpha, void* dbeta, void* dH0,
+              void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

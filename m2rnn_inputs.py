@@ -5,11 +5,12 @@ kernels read (bf16 round-to-nearest-even).  It holds none of the recurrence's
 arithmetic: both the float64 oracle and the HIP path consume what it returns,
 so the two sides always see bit-identical inputs.
 
-The five named workloads follow the shapes and distributions of the M²RNN
+The named workloads follow the shapes and distributions of the M²RNN
 layer described in the review of "M²RNN: Non-Linear RNNs with Matrix-Valued
 States for Scalable Language Modeling" (section 2.1, Eq. 10-12; section 2.2,
 Eq. 13/17 for the exp-softplus gate; section 2.4 for the paper's own K=64,
-V=16 head shape).  "N(0, s)" is read as standard deviation s.
+V=16 head shape with one q and one k shared by all value heads).  "N(0, s)"
+is read as standard deviation s.
 
 Draw order inside one workload is fixed: k, v, q, gate logit, alpha, beta,
 W, w_r, dy.  Every array is drawn at its full shape, so a workload with the
@@ -44,17 +45,25 @@ class Workload:
     w_scale: float
     C: int = 0            # checkpoint interval for the backward workload (0: forward only)
     seed: int = 1
+    NQ: int = 0           # heads of q and k, dividing N (0: one per value head)
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
+
+    @property
+    def qk_heads(self) -> int:
+        return self.NQ if self.NQ else self.N
 
     @property
     def tokens_heads(self) -> int:
         return self.B * self.T * self.N
 
 
-# The five workloads.  Sizes are the full ones; tests shrink B/T through
-# Workload.replace while keeping the recipe.
+# The workloads.  Sizes are the full ones; tests shrink B/T through
+# Workload.replace while keeping the recipe.  The first five are the
+# benchmark's configurations; the last is the paper's multi-value layout
+# (K=64, V=16, q and k shared by all heads) at the same state size per
+# sequence as the long-context one (64 heads x 64 x 16).
 WORKLOADS = {
     "tiny_fp32": Workload("tiny_fp32", B=2, T=64, N=1, K=8, V=8, bf16=False,
                           gate=GATE_SIGMOID, kq_scale=1 / math.sqrt(8),
@@ -79,6 +88,10 @@ WORKLOADS = {
                                  v_scale=1 / math.sqrt(128), g_mean=0.0,
                                  w_kind="ident", w_eps=0.05,
                                  w_scale=1 / math.sqrt(128), C=64, seed=5),
+    "multi_value_k64_v16": Workload("multi_value_k64_v16", B=4, T=16384, N=64, K=64, V=16,
+                                    bf16=True, gate=GATE_EXP_SOFTPLUS, kq_scale=1 / 8,
+                                    v_scale=1 / 4, g_mean=0.0, w_kind="ident", w_eps=0.05,
+                                    w_scale=1 / 4, C=8, seed=6, NQ=1),
 }
 WORKLOAD_ORDER = ["tiny_fp32", "fp32_k64", "long_t16k_k64", "big_state_k128",
                   "fwd_bwd_k32_v128"]
@@ -102,7 +115,7 @@ class Inputs:
 
     k, v, q are float32 arrays holding exactly the values the kernels read
     (already bf16-rounded when ``wl.bf16``); ``*_bits`` hold the bf16 bit
-    patterns in that case.  Layouts: k, q [B,T,N,K]; v [B,T,N,V];
+    patterns in that case.  Layouts: k, q [B,T,NQ,K] (NQ = wl.qk_heads); v [B,T,N,V];
     logit [B,T,N]; alpha, beta [N]; W [N,V,V] with (H W)[i,j] = sum_l H[i,l] W[l,j];
     w_r [N,V]; H0 [B,N,K,V] or None; dy [B,T,N,V] or None.
     """
@@ -138,11 +151,11 @@ def make_inputs(wl: Workload, seed: int | None = None, with_dy: bool | None = No
     gradient (drawn after everything else, so the other arrays do not change).
     """
     rng = np.random.Generator(np.random.PCG64(wl.seed if seed is None else seed))
-    B, T, N, K, V = wl.B, wl.T, wl.N, wl.K, wl.V
+    B, T, N, K, V, NQ = wl.B, wl.T, wl.N, wl.K, wl.V, wl.qk_heads
     f32 = np.float32
-    k = rng.standard_normal((B, T, N, K), dtype=f32) * f32(wl.kq_scale)
+    k = rng.standard_normal((B, T, NQ, K), dtype=f32) * f32(wl.kq_scale)
     v = rng.standard_normal((B, T, N, V), dtype=f32) * f32(wl.v_scale)
-    q = rng.standard_normal((B, T, N, K), dtype=f32) * f32(wl.kq_scale)
+    q = rng.standard_normal((B, T, NQ, K), dtype=f32) * f32(wl.kq_scale)
     logit = rng.standard_normal((B, T, N), dtype=f32)
     if wl.gate == GATE_SIGMOID:
         logit = logit + f32(wl.g_mean)

@@ -29,11 +29,11 @@ _i64, _int, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_s
 SIGNATURES = {
     "m2rnn_status_string": (ctypes.c_char_p, [_int]),
     "m2rnn_gates": (_int, [_i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp]),
-    "m2rnn_workspace_bytes": (_sz, [_int, _i64, _i64, _i64, _i64, _i64, _i64, _int]),
-    "m2rnn_fwd": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int,
+    "m2rnn_workspace_bytes": (_sz, [_int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _int]),
+    "m2rnn_fwd": (_int, [_i64, _i64, _i64, _i64, _i64, _i64, _int, _int,
                          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                          _i64, _vp, _sz, _vp]),
-    "m2rnn_bwd": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int,
+    "m2rnn_bwd": (_int, [_i64, _i64, _i64, _i64, _i64, _i64, _int, _int,
                          _vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                          _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                          _vp, _sz, _vp]),

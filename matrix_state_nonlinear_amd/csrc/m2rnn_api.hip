@@ -19,6 +19,12 @@ bool sizes_ok(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V) {
   return elems < 4.0e18;
 }
 
+// q and k have NQ heads shared by groups of N / NQ value heads: NQ divides N
+// (NQ = N is one q/k head per value head); with no heads both are 0.
+bool qk_heads_ok(int64_t N, int64_t NQ) {
+  return N > 0 ? (NQ >= 1 && NQ <= N && N % NQ == 0) : NQ == 0;
+}
+
 bool sizes_supported(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V) {
   if (K > 256 || V > 128) return false;
   if (T >= ((int64_t)1 << 30)) return false;  // step indices are 32-bit in the kernels
@@ -50,9 +56,9 @@ size_t fwd_ws_bytes(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V, int s
                   256);
 }
 
-size_t bwd_ws_bytes(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V, int64_t C,
-                    int state_dtype) {
-  const BwdWorkspace L = bwd_workspace_layout(B, T, N, K, V, C, state_dtype);
+size_t bwd_ws_bytes(int64_t B, int64_t T, int64_t N, int64_t NQ, int64_t K, int64_t V,
+                    int64_t C, int state_dtype) {
+  const BwdWorkspace L = bwd_workspace_layout(B, T, N, NQ, K, V, C, state_dtype);
   return align_up(L.total_elems * real_size(state_dtype), 256);
 }
 
@@ -95,13 +101,14 @@ const char* m2rnn_status_string(int status) {
   }
 }
 
-size_t m2rnn_workspace_bytes(int is_bwd, int64_t B, int64_t T, int64_t n_heads, int64_t K,
-                             int64_t V, int64_t C, int state_dtype) {
+size_t m2rnn_workspace_bytes(int is_bwd, int64_t B, int64_t T, int64_t n_heads,
+                             int64_t qk_heads, int64_t K, int64_t V, int64_t C,
+                             int state_dtype) {
   if (!sizes_ok(B, T, n_heads, K, V) || !sizes_supported(B, T, n_heads, K, V) ||
-      !state_dtype_known(state_dtype) || (is_bwd && C < 1))
+      !qk_heads_ok(n_heads, qk_heads) || !state_dtype_known(state_dtype) || (is_bwd && C < 1))
     return 0;
   if (B * T * n_heads == 0) return 0;  // empty calls run no kernel that needs one
-  return is_bwd ? bwd_ws_bytes(B, T, n_heads, K, V, C, state_dtype)
+  return is_bwd ? bwd_ws_bytes(B, T, n_heads, qk_heads, K, V, C, state_dtype)
                 : fwd_ws_bytes(B, T, n_heads, K, V, state_dtype);
 }
 
@@ -123,11 +130,12 @@ int m2rnn_gates(int64_t B, int64_t T, int64_t n_heads, int gate_kind, int dtype,
                                 (hipStream_t)stream));
 }
 
-int m2rnn_fwd(int64_t B, int64_t T, int64_t n_heads, int64_t K, int64_t V, int in_dtype,
-              int state_dtype, const void* k, const void* v, const void* q, const void* f,
-              const void* W, const void* w_r, const void* H0, void* y, void* HT, void* ckpt,
-              int64_t C, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!sizes_ok(B, T, n_heads, K, V)) return M2RNN_ERR_INVALID_ARG;
+int m2rnn_fwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K, int64_t V,
+              int in_dtype, int state_dtype, const void* k, const void* v, const void* q,
+              const void* f, const void* W, const void* w_r, const void* H0, void* y, void* HT,
+              void* ckpt, int64_t C, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!sizes_ok(B, T, n_heads, K, V) || !qk_heads_ok(n_heads, qk_heads))
+    return M2RNN_ERR_INVALID_ARG;
   if (!in_dtype_known(in_dtype) || !state_dtype_known(state_dtype)) return M2RNN_ERR_INVALID_ARG;
   const bool empty = B * T * n_heads == 0;
   if (!empty && (!k || !v || !q || !f || !W || !w_r || !y)) return M2RNN_ERR_INVALID_ARG;
@@ -142,18 +150,20 @@ int m2rnn_fwd(int64_t B, int64_t T, int64_t n_heads, int64_t K, int64_t V, int i
   a.k = k; a.v = v; a.q = q; a.f = f; a.W = W; a.w_r = w_r; a.H0 = H0;
   a.y = y; a.ypart = workspace; a.HT = HT; a.ckpt = ckpt;
   a.B = B; a.T = T; a.N = n_heads; a.K = K; a.V = V; a.C = ckpt ? C : 1;
+  a.NQ = qk_heads;
   a.nslab = (int)num_slabs(K);
   return status_of(launch_fwd(a, in_dtype, state_dtype, (hipStream_t)stream));
 }
 
-int m2rnn_bwd(int64_t B, int64_t T, int64_t n_heads, int64_t K, int64_t V, int in_dtype,
-              int state_dtype, const void* k, const void* v, const void* q, int gate_kind,
-              const void* logit, const void* alpha, const void* beta, const void* f,
-              const void* W, const void* w_r, const void* H0, const void* ckpt, int64_t C,
-              const void* dy, const void* dHT, void* dk, void* dv, void* dq, void* dlogit,
-              void* dW, void* dw_r, void* dalpha, void* dbeta, void* dH0, void* workspace,
-              size_t workspace_bytes, void* stream) {
-  if (!sizes_ok(B, T, n_heads, K, V)) return M2RNN_ERR_INVALID_ARG;
+int m2rnn_bwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K, int64_t V,
+              int in_dtype, int state_dtype, const void* k, const void* v, const void* q,
+              int gate_kind, const void* logit, const void* alpha, const void* beta,
+              const void* f, const void* W, const void* w_r, const void* H0, const void* ckpt,
+              int64_t C, const void* dy, const void* dHT, void* dk, void* dv, void* dq,
+              void* dlogit, void* dW, void* dw_r, void* dalpha, void* dbeta, void* dH0,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!sizes_ok(B, T, n_heads, K, V) || !qk_heads_ok(n_heads, qk_heads))
+    return M2RNN_ERR_INVALID_ARG;
   if (!in_dtype_known(in_dtype) || !state_dtype_known(state_dtype)) return M2RNN_ERR_INVALID_ARG;
   const bool empty = B * T * n_heads == 0;
   const bool heads = n_heads > 0;  // per-head outputs exist
@@ -183,7 +193,7 @@ int m2rnn_bwd(int64_t B, int64_t T, int64_t n_heads, int64_t K, int64_t V, int i
     if (e == hipSuccess) e = fill(dbeta, nullptr, n_heads, state_dtype, st);
     return status_of(e);
   }
-  const size_t need = bwd_ws_bytes(B, T, n_heads, K, V, C, state_dtype);
+  const size_t need = bwd_ws_bytes(B, T, n_heads, qk_heads, K, V, C, state_dtype);
   if (need && (!workspace || workspace_bytes < need)) return M2RNN_ERR_WORKSPACE;
   BwdArgs a{};
   a.k = k; a.v = v; a.q = q; a.logit = logit; a.alpha = alpha; a.beta = beta; a.f = f;
@@ -191,6 +201,7 @@ int m2rnn_bwd(int64_t B, int64_t T, int64_t n_heads, int64_t K, int64_t V, int i
   a.dk = dk; a.dv = dv; a.dq = dq; a.dlogit = dlogit; a.dW = dW; a.dw_r = dw_r;
   a.dalpha = dalpha; a.dbeta = dbeta; a.dH0 = dH0; a.ws = workspace;
   a.B = B; a.T = T; a.N = n_heads; a.K = K; a.V = V; a.C = C;
+  a.NQ = qk_heads;
   a.nslab = (int)num_slabs(K);
   a.gate_kind = gate_kind;
   return status_of(launch_bwd(a, in_dtype, state_dtype, (hipStream_t)stream));

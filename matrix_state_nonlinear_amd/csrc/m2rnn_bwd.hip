@@ -135,8 +135,8 @@ int bwd_period(int state_dtype, int64_t V) {
   }
 }
 
-BwdWorkspace bwd_workspace_layout(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V,
-                                  int64_t C, int state_dtype) {
+BwdWorkspace bwd_workspace_layout(int64_t B, int64_t T, int64_t N, int64_t NQ, int64_t K,
+                                  int64_t V, int64_t C, int state_dtype) {
   BwdWorkspace L{};
   const int64_t ns = num_slabs(K);
   L.period = bwd_period(state_dtype, V);
@@ -155,6 +155,8 @@ BwdWorkspace bwd_workspace_layout(int64_t B, int64_t T, int64_t N, int64_t K, in
   L.df_part = take((size_t)ns * B * T * N);
   L.dW_part = take((size_t)B * ns * N * V * V);
   L.col_part = take((size_t)L.row_blocks * N * (V + 2));
+  L.dk_part = take(NQ < N ? (size_t)B * T * N * K : 0);
+  L.dq_part = take(NQ < N ? (size_t)B * T * N * K : 0);
   L.total_elems = off;
   return L;
 }
@@ -190,6 +192,13 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
   const int jlast = nch * S + S + 1;  // last phase
   const int nper = jlast / S + 1;     // periods of S phases covering 0..jlast
   const int64_t tok0 = (int64_t)b * T * N + n;  // token (b, t, n) is tok0 + t N
+  // q and k rows of (b, t): tokq0 + t NQ, head n / (N / NQ) of the NQ shared heads
+  const int64_t NQ = a.NQ;
+  const int64_t tokq0 = (int64_t)b * T * NQ + n / (int)(N / NQ);
+  // dk and dq per value head: the outputs when NQ = N, else partials that
+  // are summed over each group of N / NQ heads afterwards
+  Real* const dk_base = NQ == N ? (Real*)a.dk : (Real*)a.ws + L.dk_part;
+  Real* const dq_base = NQ == N ? (Real*)a.dq : (Real*)a.ws + L.dq_part;
   const int64_t state_base = ((int64_t)bn * K + row) * V;
   const Real* __restrict__ Wp = (const Real*)a.W;
   auto col_of = [&](int p, int r) { return (wr * TPW + p) * 16 + acc_m<Real>(g, r); };
@@ -248,7 +257,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
     for (int p = 0; p < TPW; ++p) pin_values(wrc[p][0], wrc[p][1], wrc[p][2], wrc[p][3]);
     const bool dv_vec = sizeof(Real) == 4 && (V & 3) == 0;
     // output pointers at token (b, t = 0, n); step t adds t N rows
-    Real* const dq_row = (Real*)a.dq + tok0 * K + row;
+    Real* const dq_row = dq_base + tok0 * K + row;
     Real* const dv_tok = nslab == 1 ? (Real*)a.dv + tok0 * V
                                     : (Real*)a.ws + L.dv_part + ((int64_t)slab * B * T * N + tok0) * V;
     const int64_t NK = N * K, NV = N * V;
@@ -572,8 +581,8 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
           const int rr = slab * 16 + (r & 15);
           ok = rr < K;
           from_in = true;
-          pin = (r < 16 ? kp : qp) + tok0 * K + (ok ? rr : 0);
-          ts = (int)(N * K);
+          pin = (r < 16 ? kp : qp) + tokq0 * K + (ok ? rr : 0);
+          ts = (int)(NQ * K);
         } else if (r < OFF_U) {  // v, column r - 32
           const int jj = r - OFF_V;
           ok = jj < V;
@@ -668,7 +677,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
     // 16 acc_g(li) + 4 kk + g, element acc_r(li)
     auto tidx = [&](int kk) { return (16 * acc_g<Real>(li) + 4 * kk + g) * 4 + acc_r<Real>(li); };
     // output pointers at token (b, t = 0, n); step t adds t N rows
-    Real* const dk_row = (Real*)a.dk + tok0 * K + row;
+    Real* const dk_row = dk_base + tok0 * K + row;
     Real* const df_tok = ws + L.df_part + (int64_t)slab * B * T * N + tok0;
     const int64_t NK = N * K;
 
@@ -821,6 +830,7 @@ __global__ void __launch_bounds__((BwdShape<Real, VT>::NW * 64))
   if (t0 > xmax) return;               // uniform over the workgroup
   const int64_t tend = (t0 + C < T ? t0 + C : T) < xmax ? (t0 + C < T ? t0 + C : T) : xmax;
   const int64_t tok0 = (int64_t)b * T * N + n;
+  const int64_t tokq0 = (int64_t)b * T * a.NQ + n / (int)(N / a.NQ);  // shared q/k head
   const InT* __restrict__ kp = (const InT*)a.k;
   const InT* __restrict__ vp = (const InT*)a.v;
   const Real* __restrict__ fp = (const Real*)a.f;
@@ -902,7 +912,7 @@ __global__ void __launch_bounds__((BwdShape<Real, VT>::NW * 64))
   auto load_step = [&](int64_t t) {
     const int64_t tok = tok0 + t * N;
     fr = fp[tok];
-    kr = kp[tok * K + (row_ok ? row : 0)];
+    kr = kp[(tokq0 + t * a.NQ) * K + (row_ok ? row : 0)];
 #pragma unroll
     for (int p = 0; p < TPW; ++p)
 #pragma unroll
@@ -1039,6 +1049,23 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// Sum over groups of G consecutive heads (shared q and k: the gradient of a
+// shared head is the sum of its value heads' gradients): out[r][i] =
+// sum_{g < G} part[(r G + g) K + i] for the rows r of [B, T, NQ], in head order.
+template <typename Real>
+__global__ void __launch_bounds__(256)
+    m2rnn_group_sum_kernel(int64_t total, int64_t K, int G, const Real* __restrict__ part,
+                           Real* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
+    const int64_t r = e / K, i = e - r * K;
+    const Real* p = part + r * G * K + i;
+    Real s = p[0];
+    for (int g = 1; g < G; ++g) s += p[(int64_t)g * K];
+    out[e] = s;
+  }
+}
+
 // Column sums over the B*T token rows, stage 1: one block per (row block of
 // 256 rows, head).  Columns 0..V-1: dy (.) v (-> dw_r); V: -df softplus(x) f
 // (-> dalpha); V+1: dlogit (-> dbeta).  The block's 256 threads are four row
@@ -1116,7 +1143,7 @@ static hipError_t launch_bwd_vt(const BwdArgs& a0, hipStream_t stream) {
   static_assert(sizeof(BwdSmem<Real, VT>) <= kLdsBytes, "LDS budget");
   BwdArgs a = a0;
   const BwdWorkspace L =
-      bwd_workspace_layout(a.B, a.T, a.N, a.K, a.V, a.C, sizeof(Real) == 8 ? kF64 : kF32);
+      bwd_workspace_layout(a.B, a.T, a.N, a.NQ, a.K, a.V, a.C, sizeof(Real) == 8 ? kF64 : kF32);
   Real* ws = (Real*)a.ws;
   const int64_t units = a.B * a.N * a.nslab;
   const int64_t nck = (a.T + a.C - 1) / a.C;
@@ -1159,6 +1186,16 @@ static hipError_t launch_bwd_vt(const BwdArgs& a0, hipStream_t stream) {
                          total, a.N, a.V, a.nslab, ws + L.dv_part, (const Real*)a.dy,
                          (const Real*)a.w_r, (Real*)a.dv);
     }
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (a.NQ < a.N) {
+    // shared q and k: dk and dq of a shared head are the sums over its group
+    const int64_t out = a.B * a.T * a.NQ * a.K;
+    hipLaunchKernelGGL((m2rnn_group_sum_kernel<Real>), dim3(grid_for(out)), dim3(256), 0, stream,
+                       out, a.K, (int)(a.N / a.NQ), ws + L.dk_part, (Real*)a.dk);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL((m2rnn_group_sum_kernel<Real>), dim3(grid_for(out)), dim3(256), 0, stream,
+                       out, a.K, (int)(a.N / a.NQ), ws + L.dq_part, (Real*)a.dq);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   const int64_t per = a.N * a.V * a.V;

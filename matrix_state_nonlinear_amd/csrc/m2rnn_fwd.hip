@@ -191,8 +191,10 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
   // fixed offsets plus ch * TC * (elements per step); they are computed once.
   // Loads are unconditional (a chunk's loads are all in flight at once); in
   // the last chunk the step index is clamped to T - 1 and the value masked.
-  const int64_t NV = N * V, NK = N * K;
+  const int64_t NV = N * V, NK = a.NQ * K;
   const int64_t tok0 = (int64_t)b * T * N + n;       // token index of (b, t = 0, n)
+  // q and k rows of (b, t = 0): head n / (N / NQ) of the NQ shared heads
+  const int64_t tokq0 = (int64_t)b * T * a.NQ + n / (int)(N / a.NQ);
   const int T32 = (int)T;                             // T < 2^30
   // Each thread owns a fixed set of (step-in-chunk, index) elements.  Chunks
   // are loaded in order, so each element's source pointer steps forward by
@@ -218,8 +220,8 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
     const int tt = e / 16, i = e % 16, rr = slab * 16 + i;
     q_tt[m] = tt < TC ? tt : 0;
     q_ok[m] = tt < TC && rr < K;
-    k_p[m] = kp + tok0 * K + (rr < K ? rr : K - 1) + (int64_t)q_tt[m] * NK;
-    q_p[m] = qp + tok0 * K + (rr < K ? rr : K - 1) + (int64_t)q_tt[m] * NK;
+    k_p[m] = kp + tokq0 * K + (rr < K ? rr : K - 1) + (int64_t)q_tt[m] * NK;
+    q_p[m] = qp + tokq0 * K + (rr < K ? rr : K - 1) + (int64_t)q_tt[m] * NK;
   }
   const int f_tt = tid < TC ? tid : 0;
   const Real* f_p = fp + tok0 + (int64_t)f_tt * N;

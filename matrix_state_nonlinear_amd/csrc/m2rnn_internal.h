@@ -44,6 +44,7 @@ struct FwdArgs {
   void* HT;          // may be null
   void* ckpt;        // may be null
   int64_t B, T, N, K, V, C;
+  int64_t NQ;        // heads of q and k; value head n reads q/k head n / (N / NQ)
   int nslab;
 };
 
@@ -77,6 +78,7 @@ struct BwdArgs {
   const void* cks;
   int64_t cks_count, cks_step;
   int64_t B, T, N, K, V, C;
+  int64_t NQ;        // heads of q and k; value head n reads q/k head n / (N / NQ)
   int nslab;
   int gate_kind;
 };
@@ -92,11 +94,13 @@ struct BwdWorkspace {
   size_t df_part;     // [nslab, B, T, N]
   size_t dW_part;     // [B * nslab, N, V, V]
   size_t col_part;    // [row_blocks, N, V + 2] column-sum partials (dw_r, dalpha, dbeta)
+  size_t dk_part;     // [B, T, N, K] per-value-head dk (NQ < N only; summed over groups)
+  size_t dq_part;     // [B, T, N, K] per-value-head dq (NQ < N only)
   int64_t row_blocks;
   size_t total_elems;
 };
-BwdWorkspace bwd_workspace_layout(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V,
-                                  int64_t C, int state_dtype);
+BwdWorkspace bwd_workspace_layout(int64_t B, int64_t T, int64_t N, int64_t NQ, int64_t K,
+                                  int64_t V, int64_t C, int state_dtype);
 
 hipError_t launch_gates(int64_t B, int64_t T, int64_t N, int gate_kind, int dtype,
                         const void* logit, const void* alpha, const void* beta, void* f,

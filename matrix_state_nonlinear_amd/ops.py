@@ -53,10 +53,21 @@ def m2rnn_status_string(status: int) -> str:
     return _lib.status_string(status)
 
 
-def m2rnn_workspace_bytes(is_bwd: bool, B: int, T: int, n_heads: int, K: int, V: int, C: int,
-                          state_dtype=torch.float32) -> int:
-    return int(_lib.lib().m2rnn_workspace_bytes(int(bool(is_bwd)), B, T, n_heads, K, V, C,
-                                                _DT[state_dtype]))
+def m2rnn_workspace_bytes(is_bwd: bool, B: int, T: int, n_heads: int, qk_heads: int, K: int,
+                          V: int, C: int, state_dtype=torch.float32) -> int:
+    return int(_lib.lib().m2rnn_workspace_bytes(int(bool(is_bwd)), B, T, n_heads, qk_heads, K,
+                                                V, C, _DT[state_dtype]))
+
+
+def _heads(k, v):
+    """(N, NQ): value heads from v, q/k heads from k (NQ divides N; value head
+    n reads q/k head n // (N // NQ))."""
+    if k.dim() != 4 or v.dim() != 4:
+        raise ValueError("k, q must be [B, T, qk_heads, K] and v [B, T, n_heads, V]")
+    N, NQ = v.shape[2], k.shape[2]
+    if (NQ < 1 or NQ > N or N % NQ) if N > 0 else NQ != 0:
+        raise ValueError(f"qk_heads = {NQ} must divide n_heads = {N}")
+    return N, NQ
 
 
 def _workspace(nbytes: int, device, given=None):
@@ -92,17 +103,19 @@ def m2rnn_fwd(k, v, q, f, W, w_r, H0=None, C: int = 0, want_ht: bool = True,
               out=None, workspace=None):
     """Forward recurrence.  Returns (y, HT or None, ckpt or None).
 
-    k, q [B, T, N, K] and v [B, T, N, V] in float32 / bfloat16 (float32 state)
-    or float64 / bfloat16 (float64 state); f [B, T, N], W [N, V, V], w_r [N, V],
+    k, q [B, T, NQ, K] and v [B, T, N, V] in float32 / bfloat16 (float32 state)
+    or float64 / bfloat16 (float64 state), where NQ divides N and value head n
+    reads q/k head n // (N // NQ); f [B, T, N], W [N, V, V], w_r [N, V],
     H0 [B, N, K, V] in the state dtype (taken from f).  C > 0 also writes the
     checkpoints ckpt[B, N, ceil(T / C), K, V] with ckpt[:, :, c] = H_{cC}.
     ``out`` may hold preallocated (y, HT, ckpt).
     """
-    B, T, N, K = k.shape
+    N, NQ = _heads(k, v)
+    B, T, _, K = k.shape
     V = v.shape[-1]
     sd = f.dtype
     _need(v, (B, T, N, V), k.dtype, "v")
-    _need(q, (B, T, N, K), k.dtype, "q")
+    _need(q, (B, T, NQ, K), k.dtype, "q")
     _need(f, (B, T, N), sd, "f")
     _need(W, (N, V, V), sd, "W")
     _need(w_r, (N, V), sd, "w_r")
@@ -115,9 +128,9 @@ def m2rnn_fwd(k, v, q, f, W, w_r, H0=None, C: int = 0, want_ht: bool = True,
         HT = torch.empty((B, N, K, V), dtype=sd, device=dev) if want_ht else None
         ckpt = (torch.empty((B, N, math.ceil(T / C), K, V), dtype=sd, device=dev)
                 if C and C > 0 else None)
-    ws, wsb = _workspace(m2rnn_workspace_bytes(False, B, T, N, K, V, max(C, 1), sd), dev,
+    ws, wsb = _workspace(m2rnn_workspace_bytes(False, B, T, N, NQ, K, V, max(C, 1), sd), dev,
                          workspace)
-    st = _lib.lib().m2rnn_fwd(B, T, N, K, V, _DT[k.dtype], _DT[sd], _ptr(k), _ptr(v), _ptr(q),
+    st = _lib.lib().m2rnn_fwd(B, T, N, NQ, K, V, _DT[k.dtype], _DT[sd], _ptr(k), _ptr(v), _ptr(q),
                               _ptr(f), _ptr(W), _ptr(w_r), _ptr(H0), _ptr(y), _ptr(HT),
                               _ptr(ckpt), int(C) if ckpt is not None else 0, _ptr(ws), wsb,
                               _stream(dev))
@@ -128,12 +141,15 @@ def m2rnn_fwd(k, v, q, f, W, w_r, H0=None, C: int = 0, want_ht: bool = True,
 def m2rnn_bwd(k, v, q, gate_kind: int, logit, alpha, beta, f, W, w_r, H0, ckpt, C: int, dy,
               dHT=None, want_dh0: bool = True, workspace=None):
     """Backward of m2rnn_fwd.  Returns a dict with dk, dv, dq, dlogit, dW, dw_r,
-    dalpha and dbeta (exp-softplus gate only, else None) and dH0 (or None)."""
-    B, T, N, K = k.shape
+    dalpha and dbeta (exp-softplus gate only, else None) and dH0 (or None).
+    dk and dq have the shape of k and q: with shared heads (NQ < N) each is
+    the sum over the value heads that read it."""
+    N, NQ = _heads(k, v)
+    B, T, _, K = k.shape
     V = v.shape[-1]
     sd = f.dtype
     _need(v, (B, T, N, V), k.dtype, "v")
-    _need(q, (B, T, N, K), k.dtype, "q")
+    _need(q, (B, T, NQ, K), k.dtype, "q")
     _need(logit, (B, T, N), sd, "logit")
     _need(f, (B, T, N), sd, "f")
     _need(W, (N, V, V), sd, "W")
@@ -144,14 +160,14 @@ def m2rnn_bwd(k, v, q, gate_kind: int, logit, alpha, beta, f, W, w_r, H0, ckpt, 
     _opt(dHT, (B, N, K, V), sd, "dHT")
     dev = k.device
     e = lambda *s: torch.empty(s, dtype=sd, device=dev)  # noqa: E731
-    out = {"dk": e(B, T, N, K), "dv": e(B, T, N, V), "dq": e(B, T, N, K),
+    out = {"dk": e(B, T, NQ, K), "dv": e(B, T, N, V), "dq": e(B, T, NQ, K),
            "dlogit": e(B, T, N), "dW": e(N, V, V), "dw_r": e(N, V),
            "dalpha": e(N) if gate_kind == _lib.M2RNN_GATE_EXP_SOFTPLUS else None,
            "dbeta": e(N) if gate_kind == _lib.M2RNN_GATE_EXP_SOFTPLUS else None,
            "dH0": e(B, N, K, V) if want_dh0 else None}
-    ws, wsb = _workspace(m2rnn_workspace_bytes(True, B, T, N, K, V, C, sd), dev, workspace)
+    ws, wsb = _workspace(m2rnn_workspace_bytes(True, B, T, N, NQ, K, V, C, sd), dev, workspace)
     st = _lib.lib().m2rnn_bwd(
-        B, T, N, K, V, _DT[k.dtype], _DT[sd], _ptr(k), _ptr(v), _ptr(q), int(gate_kind),
+        B, T, N, NQ, K, V, _DT[k.dtype], _DT[sd], _ptr(k), _ptr(v), _ptr(q), int(gate_kind),
         _ptr(logit), _ptr(alpha), _ptr(beta), _ptr(f), _ptr(W), _ptr(w_r), _ptr(H0), _ptr(ckpt),
         int(C), _ptr(dy), _ptr(dHT), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dq"]),
         _ptr(out["dlogit"]), _ptr(out["dW"]), _ptr(out["dw_r"]), _ptr(out["dalpha"]),

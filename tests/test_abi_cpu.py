@@ -45,33 +45,55 @@ def test_status_strings(L):
 def test_workspace_sizes(L):
     ws = L.m2rnn_workspace_bytes
     # one slab per head: no forward workspace
-    assert ws(0, 2, 64, 1, 8, 8, 1, _lib.M2RNN_F32) == 0
+    assert ws(0, 2, 64, 1, 1, 8, 8, 1, _lib.M2RNN_F32) == 0
     # K = 64 -> 4 slabs of partial readouts
-    b = ws(0, 4, 100, 3, 64, 40, 1, _lib.M2RNN_F32)
+    b = ws(0, 4, 100, 3, 3, 64, 40, 1, _lib.M2RNN_F32)
     assert b == ((4 * 4 * 100 * 3 * 40 * 4 + 255) // 256) * 256
-    assert ws(0, 4, 100, 3, 64, 40, 1, _lib.M2RNN_F64) == ((4 * 4 * 100 * 3 * 40 * 8 + 255) // 256) * 256
+    assert ws(0, 4, 100, 3, 3, 64, 40, 1, _lib.M2RNN_F64) == ((4 * 4 * 100 * 3 * 40 * 8 + 255) // 256) * 256
     # unsupported sizes report 0
-    assert ws(0, 1, 10, 1, 300, 16, 1, _lib.M2RNN_F32) == 0
-    assert ws(1, 1, 10, 1, 16, 16, 0, _lib.M2RNN_F32) == 0
+    assert ws(0, 1, 10, 1, 1, 300, 16, 1, _lib.M2RNN_F32) == 0
+    assert ws(1, 1, 10, 1, 1, 16, 16, 0, _lib.M2RNN_F32) == 0
     # backward: for V = 64 in fp32 the reverse sweep walks 4-step chunks; a
     # checkpoint interval dividing 4 provides every chunk start, any other adds
     # a [B, N, ceil(T / 4), K, V] region of recomputed chunk starts
-    base = ws(1, 2, 64, 2, 32, 64, 4, _lib.M2RNN_F32)
+    base = ws(1, 2, 64, 2, 2, 32, 64, 4, _lib.M2RNN_F32)
     assert base > 0
     for C in (1, 2):
-        assert ws(1, 2, 64, 2, 32, 64, C, _lib.M2RNN_F32) == base
+        assert ws(1, 2, 64, 2, 2, 32, 64, C, _lib.M2RNN_F32) == base
     for C in (3, 8, 64):
-        assert ws(1, 2, 64, 2, 32, 64, C, _lib.M2RNN_F32) == base + 2 * 2 * 16 * 32 * 64 * 4
+        assert ws(1, 2, 64, 2, 2, 32, 64, C, _lib.M2RNN_F32) == base + 2 * 2 * 16 * 32 * 64 * 4
 
 
 def fwd(L, **kw):
-    a = dict(B=2, T=8, N=1, K=16, V=16, ind=_lib.M2RNN_F32, sd=_lib.M2RNN_F32, k=FAKE, v=FAKE,
-             q=FAKE, f=FAKE, W=FAKE, w_r=FAKE, H0=None, y=FAKE, HT=None, ckpt=None, C=0,
+    a = dict(B=2, T=8, N=1, NQ=None, K=16, V=16, ind=_lib.M2RNN_F32, sd=_lib.M2RNN_F32, k=FAKE,
+             v=FAKE, q=FAKE, f=FAKE, W=FAKE, w_r=FAKE, H0=None, y=FAKE, HT=None, ckpt=None, C=0,
              ws=None, wsb=0, stream=None)
     a.update(kw)
-    return L.m2rnn_fwd(a["B"], a["T"], a["N"], a["K"], a["V"], a["ind"], a["sd"], a["k"], a["v"],
+    if a["NQ"] is None:
+        a["NQ"] = a["N"]
+    return L.m2rnn_fwd(a["B"], a["T"], a["N"], a["NQ"], a["K"], a["V"], a["ind"], a["sd"], a["k"], a["v"],
                        a["q"], a["f"], a["W"], a["w_r"], a["H0"], a["y"], a["HT"], a["ckpt"],
                        a["C"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_qk_heads_must_divide_n_heads(L):
+    """q and k have qk_heads heads shared by groups of n_heads / qk_heads value
+    heads: qk_heads divides n_heads; both are 0 only when there are no heads."""
+    E = _lib
+    for N, NQ in ((4, 0), (4, 3), (4, 5), (4, -1), (0, 1), (6, 4)):
+        assert fwd(L, N=N, NQ=NQ) == E.M2RNN_ERR_INVALID_ARG, (N, NQ)
+        assert bwd(L, N=N, NQ=NQ) == E.M2RNN_ERR_INVALID_ARG, (N, NQ)
+        assert L.m2rnn_workspace_bytes(1, 2, 8, N, NQ, 16, 16, 4, E.M2RNN_F32) == 0, (N, NQ)
+    assert fwd(L, N=0, NQ=0, k=None, v=None, q=None, f=None, W=None, w_r=None,
+               y=None) == E.M2RNN_OK
+    # shared heads: the backward keeps per-value-head dk and dq partials
+    # ([B, T, n_heads, K] each) that are summed over the groups
+    for NQ in (1, 2):
+        extra = L.m2rnn_workspace_bytes(1, 2, 64, 4, NQ, 32, 64, 4, E.M2RNN_F32) - \
+            L.m2rnn_workspace_bytes(1, 2, 64, 4, 4, 32, 64, 4, E.M2RNN_F32)
+        assert extra == 2 * 2 * 64 * 4 * 32 * 4
+    assert L.m2rnn_workspace_bytes(0, 2, 64, 4, 1, 32, 64, 4, E.M2RNN_F32) == \
+        L.m2rnn_workspace_bytes(0, 2, 64, 4, 4, 32, 64, 4, E.M2RNN_F32)
 
 
 def test_fwd_rejects_bad_arguments(L):
@@ -98,8 +120,8 @@ def test_empty_calls_need_no_pointers_or_workspace(L):
     write (HT, dH0 NULL, no heads) nothing is launched and the call succeeds
     here, without a GPU."""
     E = _lib
-    assert L.m2rnn_workspace_bytes(1, 0, 8, 2, 16, 16, 4, E.M2RNN_F32) == 0
-    assert L.m2rnn_workspace_bytes(0, 2, 0, 2, 64, 16, 4, E.M2RNN_F32) == 0
+    assert L.m2rnn_workspace_bytes(1, 0, 8, 2, 2, 16, 16, 4, E.M2RNN_F32) == 0
+    assert L.m2rnn_workspace_bytes(0, 2, 0, 2, 2, 64, 16, 4, E.M2RNN_F32) == 0
     assert fwd(L, B=0, k=None, v=None, q=None, f=None, W=None, w_r=None, y=None,
                HT=None, ckpt=None) == E.M2RNN_OK
     assert fwd(L, T=0, K=64, HT=None, ckpt=FAKE, C=4) == E.M2RNN_OK
@@ -125,13 +147,15 @@ def test_gates_rejects_bad_arguments(L):
 
 
 def bwd(L, **kw):
-    a = dict(B=2, T=8, N=1, K=16, V=16, ind=_lib.M2RNN_F32, sd=_lib.M2RNN_F32, k=FAKE, v=FAKE,
+    a = dict(B=2, T=8, N=1, NQ=None, K=16, V=16, ind=_lib.M2RNN_F32, sd=_lib.M2RNN_F32, k=FAKE, v=FAKE,
              q=FAKE, gate=_lib.M2RNN_GATE_SIGMOID, logit=FAKE, alpha=None, beta=None, f=FAKE,
              W=FAKE, w_r=FAKE, H0=None, ckpt=FAKE, C=4, dy=FAKE, dHT=None, dk=FAKE, dv=FAKE,
              dq=FAKE, dlogit=FAKE, dW=FAKE, dw_r=FAKE, dalpha=None, dbeta=None, dH0=None,
              ws=None, wsb=0, stream=None)
     a.update(kw)
-    keys = ["B", "T", "N", "K", "V", "ind", "sd", "k", "v", "q", "gate", "logit", "alpha", "beta",
+    if a["NQ"] is None:
+        a["NQ"] = a["N"]
+    keys = ["B", "T", "N", "NQ", "K", "V", "ind", "sd", "k", "v", "q", "gate", "logit", "alpha", "beta",
             "f", "W", "w_r", "H0", "ckpt", "C", "dy", "dHT", "dk", "dv", "dq", "dlogit", "dW",
             "dw_r", "dalpha", "dbeta", "dH0", "ws", "wsb", "stream"]
     return L.m2rnn_bwd(*[a[k] for k in keys])

@@ -1,0 +1,142 @@
+"""GPU parity of the shared q / k layout (multi-value sharing): q and k have NQ
+heads, each read by a group of N / NQ consecutive value heads, and dq, dk of a
+shared head are sums over its group (review of "M²RNN: Non-Linear RNNs with
+Matrix-Valued States for Scalable Language Modeling", section 2.4: NQ = 1).
+
+* Small sizes against the float64 oracle, in both state precisions, with the
+  tolerances of the per-head tests (fp32: 2e-5 on y, H_T, checkpoints and
+  1e-4 relative on gradients; fp64: 1e-11 and 1e-10), over shapes that span
+  several slabs and tiles, ragged chunks and both checkpoint paths (C dividing
+  the backward's chunk length, and not).
+* Bit identity with the per-head layout: the shared call must give exactly
+  the results of the same call with q and k repeated for every value head,
+  and dq, dk must be exactly the per-head gradients summed over each group in
+  head order.  This holds at any size and is checked at the full multi-value
+  workload (B=4, T=16384, 64 heads, K=64, V=16, C=8).
+* The full workload's fp32 results against the oracle over its first WINDOW
+  steps, every head.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from m2rnn_inputs import WORKLOADS, make_inputs, to_device
+from matrix_state_nonlinear_amd import m2rnn_bwd, m2rnn_fwd, m2rnn_gates
+
+pytestmark = pytest.mark.gpu
+
+TOL_Y = {"float32": 2e-5, "float64": 1e-11}
+TAU_G = {"float32": 1e-4, "float64": 1e-10}
+WINDOW = 512
+
+
+def np_(t):
+    return None if t is None else t.detach().cpu().numpy().astype(np.float64)
+
+
+def maxerr(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
+
+
+def run(d, wl, C, k=None, q=None, H0=None, dHT=None):
+    """Forward with checkpoints every C steps, then the backward."""
+    k = d["k"] if k is None else k
+    q = d["q"] if q is None else q
+    f = m2rnn_gates(d["logit"], wl.gate, d["alpha"], d["beta"])
+    y, HT, ck = m2rnn_fwd(k, d["v"], q, f, d["W"], d["w_r"], H0, C)
+    g = m2rnn_bwd(k, d["v"], q, wl.gate, d["logit"], d["alpha"], d["beta"], f, d["W"],
+                  d["w_r"], H0, ck, C, d["dy"], dHT)
+    torch.cuda.synchronize()
+    return y, HT, ck, g
+
+
+def wl_small(NQ, K, V, T=61, N=4):
+    wl = WORKLOADS["multi_value_k64_v16"]
+    return wl.replace(B=2, T=T, N=N, NQ=NQ, K=K, V=V, kq_scale=1 / math.sqrt(K),
+                      v_scale=1 / math.sqrt(V), w_scale=1 / math.sqrt(V))
+
+
+@pytest.mark.parametrize("sd", ["float32", "float64"])
+@pytest.mark.parametrize("NQ,K,V,C", [(1, 64, 16, 8), (2, 64, 16, 5), (1, 17, 40, 4),
+                                      (2, 33, 72, 3), (1, 16, 128, 2)])
+def test_shared_qk_matches_oracle(NQ, K, V, C, sd):
+    wl = wl_small(NQ, K, V)
+    inp = make_inputs(wl, with_dy=True, with_h0=True, with_dht=True)
+    assert inp.k.shape == (2, wl.T, NQ, K)
+    d = to_device(inp, sd)
+    y, HT, ck, g = run(d, wl, C, H0=d["H0"], dHT=d["dHT"])
+    fo = oracle.gates(wl.gate, inp.logit, inp.alpha, inp.beta)
+    o = oracle.forward(inp.k, inp.v, inp.q, fo, inp.W, inp.w_r, inp.H0, C=C)
+    errs = {"y": maxerr(np_(y), o["y"]), "HT": maxerr(np_(HT), o["HT"]),
+            "ckpt": maxerr(np_(ck), o["ckpt"])}
+    ref = oracle.backward(inp.k, inp.v, inp.q, fo, inp.W, inp.w_r, inp.dy, inp.H0, inp.dHT,
+                          gate_kind=wl.gate, logit=inp.logit, alpha=inp.alpha, beta=inp.beta)
+    gerr = {}
+    for name, r in ref.items():
+        if name == "df" or r is None:
+            continue
+        assert tuple(g[name].shape) == r.shape, name
+        gerr[name] = maxerr(np_(g[name]), r) / max(1.0, float(np.max(np.abs(r))))
+    print(f"NQ={NQ} K={K} V={V} C={C} {sd}", {k_: f"{v_:.1e}" for k_, v_ in errs.items()},
+          {k_: f"{v_:.1e}" for k_, v_ in gerr.items()})
+    assert all(e <= TOL_Y[sd] for e in errs.values()), errs
+    assert all(e <= TAU_G[sd] for e in gerr.values()), gerr
+
+
+def check_equals_repeated(wl, sd, C):
+    """Shared call == per-head call on q, k repeated over each group, bit for
+    bit; dq, dk == the per-head gradients summed over the group in order."""
+    inp = make_inputs(wl, with_dy=True)
+    d = to_device(inp, sd)
+    G = wl.N // wl.qk_heads
+    y, HT, ck, g = run(d, wl, C)
+    kr = torch.repeat_interleave(d["k"], G, dim=2).contiguous()
+    qr = torch.repeat_interleave(d["q"], G, dim=2).contiguous()
+    y1, HT1, ck1, g1 = run(d, wl, C, k=kr, q=qr)
+    del kr, qr
+    assert torch.equal(y, y1) and torch.equal(HT, HT1) and torch.equal(ck, ck1)
+    for name in ("dv", "dlogit", "dW", "dw_r", "dalpha", "dbeta", "dH0"):
+        if g[name] is not None:
+            assert torch.equal(g[name], g1[name]), name
+    B, T, NQ, K = d["k"].shape
+    for name in ("dk", "dq"):
+        per = g1[name].view(B, T, NQ, G, K)
+        s = per[:, :, :, 0]
+        for j in range(1, G):
+            s = s + per[:, :, :, j]
+        assert torch.equal(g[name], s), name
+
+
+@pytest.mark.parametrize("sd", ["float32", "float64"])
+@pytest.mark.parametrize("NQ,K,V,C", [(1, 64, 16, 8), (2, 40, 24, 7)])
+def test_shared_qk_equals_repeated_heads_small(NQ, K, V, C, sd):
+    check_equals_repeated(wl_small(NQ, K, V, T=90), sd, C)
+
+
+def test_shared_qk_equals_repeated_heads_full_workload():
+    wl = WORKLOADS["multi_value_k64_v16"]
+    check_equals_repeated(wl, "float32", wl.C)
+
+
+def test_shared_qk_full_workload_window_against_oracle():
+    """Every head of the full multi-value workload, fp32, over the first WINDOW
+    steps (the shared-layout call on the full sequence, sliced), against the
+    oracle run on that prefix; bf16 inputs, tolerance 2e-2 stated for them, and
+    the fp32 recurrence over this window stays far inside it."""
+    wl = WORKLOADS["multi_value_k64_v16"]
+    inp = make_inputs(wl, with_dy=False)
+    d = to_device(inp, "float32")
+    f = m2rnn_gates(d["logit"], wl.gate, d["alpha"], d["beta"])
+    y, HT, ck = m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"], None, wl.C)
+    torch.cuda.synchronize()
+    assert float(ck.abs().max()) <= 1.0 and bool(torch.isfinite(y).all())
+    pre = lambda a: a[:, :WINDOW]  # noqa: E731
+    fo = oracle.gates(wl.gate, pre(inp.logit), inp.alpha, inp.beta)
+    o = oracle.forward(pre(inp.k), pre(inp.v), pre(inp.q), fo, inp.W, inp.w_r, C=wl.C)
+    ey = maxerr(np_(y[:, :WINDOW]), o["y"])
+    ec = maxerr(np_(ck[:, :, :WINDOW // wl.C]), o["ckpt"])
+    print(f"multi-value full workload, first {WINDOW} steps: y {ey:.2e} ckpt {ec:.2e}")
+    assert ey <= 2e-2 and ec <= 2e-2
