@@ -7,9 +7,11 @@
 //
 // Work decomposition.  W mixes value columns only, so the K rows of a head are
 // independent recurrences (they meet only in the readout sum over rows).  A
-// workgroup owns one 16-row slab of one head for all T steps; a head with K
-// rows becomes ceil(K / 16) workgroups on different compute units, and their
-// partial readouts are summed by a second, elementwise kernel.
+// unit of VT / TPW waves owns one 16-row slab of one head for all T steps; a
+// head with K rows becomes ceil(K / 16) units, and their partial readouts are
+// summed by a second, elementwise kernel.  A workgroup is one unit, except
+// that one-wave units (V <= 16) are packed four to a workgroup so that each
+// takes its own SIMD.
 //
 // MFMA formulation.  The step is computed transposed, (H W)^T = W^T H^T, on
 // the 16x16x4 MFMA: W^T is the A operand (held in registers for the whole
@@ -50,7 +52,11 @@ struct FwdTraits {
   static constexpr int VP = 16 * VT;                 // padded value width
   static constexpr int NW = VT <= 4 ? VT : VT / 2;   // waves per workgroup
   static constexpr int TPW = VT / NW;                // 16-column tiles per wave
-  static constexpr int NT = 64 * NW;                 // threads per workgroup
+  static constexpr int NT = 64 * NW;                 // threads per unit (16-row slab)
+  // Units per workgroup.  A one-wave unit (V <= 16) shares a workgroup with
+  // three others, each wave on its own SIMD of the compute unit: launched as
+  // one-wave workgroups, two of them often land on one SIMD and serialise.
+  static constexpr int PACK = NW == 1 ? 4 : 1;
   static constexpr int NS = 4 * VT;                  // MFMAs per tile per step (H W)
   static constexpr int TC = sizeof(Real) == 4 ? (VT <= 4 ? 32 : 16) : 8;  // steps per staging chunk (unrolled)
   static constexpr int RING = 2 * TC;                     // staging ring: two chunks
@@ -73,18 +79,34 @@ struct FwdSmem {
 };
 
 template <typename InT, typename Real, int VT>
-__global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
+__global__ void __launch_bounds__((FwdTraits<Real, VT>::NT * FwdTraits<Real, VT>::PACK))
     m2rnn_fwd_kernel(FwdArgs a) {
   using Tr = FwdTraits<Real, VT>;
   using R4 = typename Vec4<Real>::type;
   using R2 = typename Vec2<Real>::type;
   constexpr int VP = Tr::VP, TPW = Tr::TPW, NS = Tr::NS, TC = Tr::TC, NT = Tr::NT;
-  constexpr int RING = Tr::RING;
-  __shared__ FwdSmem<Real, VT, Tr::NW, RING> sm;
+  constexpr int RING = Tr::RING, PACK = Tr::PACK;
+  __shared__ FwdSmem<Real, VT, Tr::NW, RING> smp[PACK];
 
-  const int tid = threadIdx.x;
+  // with PACK > 1 every wave is a unit of its own: thread indices are
+  // wave-relative and the unit's LDS is the wave's own slice
+  const int wu = PACK > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
+  FwdSmem<Real, VT, Tr::NW, RING>& sm = smp[wu];
+  const int tid = PACK > 1 ? (int)threadIdx.x & 63 : (int)threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, g = lane >> 4, li = lane & 15;
-  const int unit = xcd_remap(blockIdx.x, gridDim.x);
+  const int unit = xcd_remap(blockIdx.x, gridDim.x) * PACK + wu;
+  if (PACK > 1 && unit >= a.B * a.N * a.nslab) return;  // no barrier couples the waves
+  // Orders the unit's LDS accesses.  A one-wave unit's LDS operations complete
+  // in program order, so only the compiler must not move them across.
+  auto unit_sync = [] {
+    if constexpr (PACK > 1) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+      __syncthreads();
+    }
+  };
   const int nslab = a.nslab;
   const int slab = unit % nslab;
   const int bn = unit / nslab;
@@ -357,7 +379,7 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
   Real hb[NS];
 #pragma unroll
   for (int p = 0; p < TPW; ++p) sm.xb[1][w * TPW + p][lane] = hown[p];
-  __syncthreads();
+  unit_sync();
 #pragma unroll
   for (int q0 = 0; q0 < VT; ++q0) {
     const R4 t4 = q0 < TPW ? hown[q0] : sm.xb[1][(q0 + TPW * w) % VT][lane];
@@ -416,7 +438,7 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
         const Real rc = tanh_rc_scaled(acc[p][r]);
         hown[p][r] = fma_r(m2omf, rc, fma_r(cur.fg[0], hown[p][r], cur.fg[1]));
       }
-      sm.xb[P][w * TPW + p][lane] = hown[p];
+      if constexpr (Tr::NW > 1) sm.xb[P][w * TPW + p][lane] = hown[p];
     }
     // keep the exchange write ahead of the readout, so its latency overlaps it
     __builtin_amdgcn_sched_barrier(0);
@@ -425,7 +447,7 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
     R4 ys[TPW];
 #pragma unroll
     for (int p = 0; p < TPW; ++p) ys[p] = row16_sum_x4(hown[p], cur.q);
-    __syncthreads();
+    unit_sync();
     // the readout store goes after the barrier (its latency then overlaps the
     // own-tile MFMAs of the next step); the barrier ending the chunk's last
     // step is followed by one more before the write-back reads it
@@ -484,7 +506,7 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT))
       }
     }
     // ---- between chunks: write-back of this chunk, prefetch
-    __syncthreads();                             // the chunk's last readout stores
+    unit_sync();                                 // the chunk's last readout stores
     flush(ch);                                   // readouts of chunk ch are complete
     if (ch + 2 < nchunks) load_chunk(ch + 2);    // into registers; stored during chunk ch + 1
   }
@@ -511,10 +533,12 @@ __global__ void __launch_bounds__(256)
 template <typename InT, typename Real, int VT>
 static hipError_t launch_fwd_vt(const FwdArgs& a, hipStream_t stream) {
   using Tr = FwdTraits<Real, VT>;
-  static_assert(sizeof(FwdSmem<Real, VT, Tr::NW, Tr::RING>) <= 160 * 1024, "LDS budget");
+  static_assert(Tr::PACK * sizeof(FwdSmem<Real, VT, Tr::NW, Tr::RING>) <= 160 * 1024,
+                "LDS budget");
   const int64_t units = a.B * a.N * a.nslab;
-  hipLaunchKernelGGL((m2rnn_fwd_kernel<InT, Real, VT>), dim3((unsigned)units), dim3(Tr::NT), 0,
-                     stream, a);
+  const int64_t wgs = (units + Tr::PACK - 1) / Tr::PACK;
+  hipLaunchKernelGGL((m2rnn_fwd_kernel<InT, Real, VT>), dim3((unsigned)wgs),
+                     dim3(Tr::NT * Tr::PACK), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.nslab == 1) return err;
   const int64_t total = a.B * a.T * a.N * a.V;
