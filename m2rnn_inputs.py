@@ -91,7 +91,7 @@ WORKLOADS = {
     "multi_value_k64_v16": Workload("multi_value_k64_v16", B=4, T=16384, N=64, K=64, V=16,
                                     bf16=True, gate=GATE_EXP_SOFTPLUS, kq_scale=1 / 8,
                                     v_scale=1 / 4, g_mean=0.0, w_kind="ident", w_eps=0.05,
-                                    w_scale=1 / 4, C=8, seed=6, NQ=1),
+                                    w_scale=1 / 4, C=4, seed=6, NQ=1),
 }
 WORKLOAD_ORDER = ["tiny_fp32", "fp32_k64", "long_t16k_k64", "big_state_k128",
                   "fwd_bwd_k32_v128"]

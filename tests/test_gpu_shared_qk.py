@@ -12,7 +12,7 @@ Matrix-Valued States for Scalable Language Modeling", section 2.4: NQ = 1).
   the results of the same call with q and k repeated for every value head,
   and dq, dk must be exactly the per-head gradients summed over each group in
   head order.  This holds at any size and is checked at the full multi-value
-  workload (B=4, T=16384, 64 heads, K=64, V=16, C=8).
+  workload (B=4, T=16384, 64 heads, K=64, V=16, C=4).
 * The full workload's fp32 results against the oracle over its first WINDOW
   steps, every head.
 """
