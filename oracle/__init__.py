@@ -18,6 +18,7 @@ from .m2rnn_oracle import (  # noqa: F401
     gates,
     gate_partials,
     forward,
+    decode_step,
     backward,
     step_jacobian_dense,
     tangent_growth,

@@ -158,6 +158,27 @@ def forward(k, v, q, f, W, w_r, H0=None, C=0, keep_states=False):
     return out
 
 
+def decode_step(H, k, v, q, f, W, w_r):
+    """One step of the recurrence for a batch of single tokens (decoding), the
+    sequential cell step of [P] "Reproduce (sequential)" with the readout of
+    [R] section 2.1 Eq. (10)-(12):
+
+        H_t = f H_{t-1} + (1 - f) tanh(H_{t-1} W + k v^T),   y = H_t^T q + w_r (.) v
+
+    H [B, N, K, V] is H_{t-1}; k, q [B, NQ, K] (NQ dividing N, shared as in
+    forward); v [B, N, V]; f [B, N].  Returns (H_t, y) with y [B, N, V].
+    """
+    H, k, v, q, f, W, w_r = map(_a, (H, k, v, q, f, W, w_r))
+    N = v.shape[1]
+    k = _expand_qk(k[:, None], N)[:, 0]
+    q = _expand_qk(q[:, None], N)[:, 0]
+    Z = np.tanh(np.matmul(H, W[None]) + k[:, :, :, None] * v[:, :, None, :])
+    fb = f[:, :, None, None]
+    Hn = fb * H + (1.0 - fb) * Z
+    y = np.matmul(q[:, :, None, :], Hn)[:, :, 0, :] + w_r[None] * v
+    return Hn, y
+
+
 def backward(k, v, q, f, W, w_r, dy, H0=None, dHT=None, gate_kind=None,
              logit=None, alpha=None, beta=None, b_group=None):
     """Reverse-time BPTT of the forward above for the loss L with dL/dy = dy

@@ -423,6 +423,64 @@ def test_shared_qk_central_differences():
         np.testing.assert_allclose(g["d" + name], fd, rtol=1e-6, atol=1e-8, err_msg=name)
 
 
+# ---------------------------------------------------------------- decode step
+
+def test_decode_step_gate_one_keeps_state_and_reads_it_out():
+    # f = 1: H_t = H_{t-1} exactly, and y = H^T q + w_r (.) v by brute-force sums.
+    rng = np.random.default_rng(101)
+    B, N, K, V = 2, 3, 5, 4
+    H = rng.uniform(-0.7, 0.7, (B, N, K, V))
+    k, q = rng.standard_normal((B, N, K)), rng.standard_normal((B, N, K))
+    v = rng.standard_normal((B, N, V))
+    W = rng.standard_normal((N, V, V))
+    w_r = rng.standard_normal((N, V))
+    Hn, y = oracle.decode_step(H, k, v, q, np.ones((B, N)), W, w_r)
+    assert np.array_equal(Hn, H)
+    for b in range(B):
+        for n in range(N):
+            for j in range(V):
+                ref = sum(H[b, n, i, j] * q[b, n, i] for i in range(K)) + w_r[n, j] * v[b, n, j]
+                assert abs(y[b, n, j] - ref) < 1e-12
+
+
+def test_decode_step_gate_zero_w_zero_is_tanh_outer():
+    rng = np.random.default_rng(102)
+    B, N, K, V = 2, 2, 3, 6
+    H = rng.uniform(-0.7, 0.7, (B, N, K, V))
+    k, q = rng.standard_normal((B, N, K)), rng.standard_normal((B, N, K))
+    v = rng.standard_normal((B, N, V))
+    Hn, _ = oracle.decode_step(H, k, v, q, np.zeros((B, N)), np.zeros((N, V, V)),
+                               np.zeros((N, V)))
+    for b in range(B):
+        for n in range(N):
+            np.testing.assert_allclose(Hn[b, n], np.tanh(np.outer(k[b, n], v[b, n])),
+                                       rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("NQ", [1, 3])
+def test_decode_steps_chain_to_the_torch_recurrence(NQ):
+    # T decode steps from H_0 reproduce a direct torch transcription of
+    # Eq. (10)-(12) over the same T tokens (y at every step and H_T).
+    rng = np.random.default_rng(103 + NQ)
+    B, T, N, K, V = 2, 6, 3, 4, 5
+    c = _rand_case(104, B=B, T=T, N=N, K=K, V=V)
+    k = rng.standard_normal((B, T, NQ, K)) * 0.7
+    q = rng.standard_normal((B, T, NQ, K))
+    H = c["H0"]
+    ys = []
+    for t in range(T):
+        H, y = oracle.decode_step(H, k[:, t], c["v"][:, t], q[:, t], c["f"][:, t], c["W"],
+                                  c["w_r"])
+        ys.append(y)
+    tt = lambda a: torch.from_numpy(np.asarray(a, np.float64))  # noqa: E731
+    G = N // NQ
+    yr, HT = _torch_forward(torch.repeat_interleave(tt(k), G, dim=2), tt(c["v"]),
+                            torch.repeat_interleave(tt(q), G, dim=2), tt(c["f"]), tt(c["W"]),
+                            tt(c["w_r"]), tt(c["H0"]))
+    np.testing.assert_allclose(np.stack(ys, 1), yr.numpy(), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(H, HT.numpy(), rtol=0, atol=1e-13)
+
+
 # ---------------------------------------------------------------- sensitivity helper
 
 def test_tangent_growth_linear_regime_closed_form():
