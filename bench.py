@@ -44,7 +44,10 @@ def parse():
                     help="target duration of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true",
-                    help="skip the MFMA fraction of every workload")
+                    help="skip the MFMA fraction of every workload and the decode-step rates")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only time the single-token step on the decoding workloads and "
+                         "print those rates")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="first copy this many GiB twice with torch (a plain copy of known "
                          "size, to calibrate HBM byte counters)")
@@ -124,6 +127,51 @@ def per_config_fractions(reps=3):
     return rows
 
 
+def decode_rates(reps=50):
+    """The single-token step (m2rnn_step) on the decoding workloads: one token
+    for each of B sequences, the state updated in place.  HBM-bound by design:
+    the algorithmic bytes per (sequence, head) are the state read and written
+    (2 K V 4 B) plus v, f, y and the shared k, q; the rate is priced against
+    the 8 TB/s HBM peak."""
+    import torch
+
+    from m2rnn_inputs import DECODE_WORKLOADS, make_inputs, to_device
+    from matrix_state_nonlinear_amd import m2rnn_gates, m2rnn_step
+
+    rows = []
+    for wl in DECODE_WORKLOADS.values():
+        inp = make_inputs(wl)
+        d = to_device(inp, "float32")
+        f = m2rnn_gates(d["logit"], wl.gate, d["alpha"], d["beta"])[:, 0].contiguous()
+        H = torch.empty((wl.B, wl.N, wl.K, wl.V), device="cuda").uniform_(-0.5, 0.5)
+        k, v, q = (d[x][:, 0].contiguous() for x in ("k", "v", "q"))
+        y = torch.empty((wl.B, wl.N, wl.V), device="cuda")
+        stream = torch.cuda.current_stream()
+        for _ in range(3):
+            m2rnn_step(H, k, v, q, f, d["W"], d["w_r"], out=y)
+        stream.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            m2rnn_step(H, k, v, q, f, d["W"], d["w_r"], out=y)
+        e1.record(stream)
+        stream.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        th = wl.B * wl.N
+        in_b = 2 if wl.bf16 else 4
+        nbytes = (th * (2 * wl.K * wl.V * 4 + wl.V * in_b + 4 + wl.V * 4)
+                  + wl.B * wl.qk_heads * 2 * wl.K * in_b)
+        gbs = nbytes / us / 1e3
+        rows.append({"workload": wl.name, "B": wl.B, "n_heads": wl.N, "qk_heads": wl.qk_heads,
+                     "K": wl.K, "V": wl.V, "us_per_step": us,
+                     "tokens_heads_per_s": th / us * 1e6, "bytes_per_step": nbytes,
+                     "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                     "mfma_frac": 2.0 * th * wl.K * wl.V * wl.V / us / 1e6 / MFMA_F32_PEAK_TFLOPS})
+        del d, f, H, k, v, q, y, inp
+        torch.cuda.empty_cache()
+    return rows
+
+
 def oracle_baseline(wl, target_s):
     """float64 oracle (forward + backward) on the first Ts steps of every unit."""
     import numpy as np
@@ -174,6 +222,11 @@ def main():
     from m2rnn_inputs import WORKLOADS, make_inputs, to_device
     from matrix_state_nonlinear_amd import m2rnn_bwd, m2rnn_fwd, m2rnn_gates
     from matrix_state_nonlinear_amd.ops import m2rnn_workspace_bytes
+
+    if args.decode_only:
+        torch.cuda.set_device(0)
+        print(json.dumps({"decode": decode_rates()}), flush=True)
+        return
 
     if args.copy_calibration_gib > 0:
         n = int(args.copy_calibration_gib * (1 << 28))
@@ -287,6 +340,7 @@ def main():
     }
     if not args.no_per_config:
         out["per_config"] = per_config_fractions()
+        out["decode"] = decode_rates()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = oracle_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -158,6 +158,25 @@ int m2rnn_bwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K
               void* dlogit, void* dW, void* dw_r, void* dalpha, void* dbeta, void* dH0,
               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * m2rnn_step -- one token of every sequence (decoding): the state is updated in
+ * place by one step of the recurrence of review section 2.1, Eq. (10)-(12) (the
+ * sequential cell step of the pararnn-torch "ParaM2RNN" page), and read out:
+ *     H <- f H + (1 - f) tanh(H W_n + k v^T),   y = H^T q + w_r[n] (.) v.
+ * Bit-for-bit the same arithmetic as m2rnn_fwd is not promised (the H W sum
+ * runs in another order); both are within the library's stated tolerances.
+ *   k, q   [B, qk_heads, K]     in, in_dtype
+ *   v      [B, n_heads, V]      in, in_dtype
+ *   f      [B, n_heads]         in, forget gate (m2rnn_gates with T = 1)
+ *   W, w_r                      as for m2rnn_fwd
+ *   H      [B, n_heads, K, V]   in/out: H_{t-1} on entry, H_t on return
+ *   y      [B, n_heads, V]      out
+ * No workspace.  B * n_heads = 0 is a call that reads and writes nothing.
+ */
+int m2rnn_step(int64_t B, int64_t n_heads, int64_t qk_heads, int64_t K, int64_t V, int in_dtype,
+               int state_dtype, const void* k, const void* v, const void* q, const void* f,
+               const void* W, const void* w_r, void* H, void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

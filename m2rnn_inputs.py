@@ -93,6 +93,17 @@ WORKLOADS = {
                                     v_scale=1 / 4, g_mean=0.0, w_kind="ident", w_eps=0.05,
                                     w_scale=1 / 4, C=4, seed=6, NQ=1),
 }
+# Decoding: one token for each of B sequences (T = 1), the state updated in
+# place.  The recipes of the long-context workload (K = V = 64) and of the
+# multi-value one (K = 64, V = 16, shared q/k), with 512 sequences: the state
+# read and written per step is 128 MiB (512 x 16 heads x 64 x 64 fp32), so the
+# step's HBM traffic, not its launch, sets its time.
+DECODE_WORKLOADS = {
+    "decode_k64": WORKLOADS["long_t16k_k64"].replace(name="decode_k64", B=512, T=1, seed=7),
+    "decode_multi_value": WORKLOADS["multi_value_k64_v16"].replace(
+        name="decode_multi_value", B=512, T=1, C=0, seed=8),
+}
+
 WORKLOAD_ORDER = ["tiny_fp32", "fp32_k64", "long_t16k_k64", "big_state_k128",
                   "fwd_bwd_k32_v128"]
 

@@ -37,6 +37,8 @@ SIGNATURES = {
                          _vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                          _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                          _vp, _sz, _vp]),
+    "m2rnn_step": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int,
+                          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
 }
 
 _lib = None

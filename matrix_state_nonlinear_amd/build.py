@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libm2rnn.so")
-SOURCES = ["m2rnn_api.hip", "m2rnn_gates.hip", "m2rnn_fwd.hip", "m2rnn_bwd.hip"]
+SOURCES = ["m2rnn_api.hip", "m2rnn_gates.hip", "m2rnn_fwd.hip", "m2rnn_bwd.hip",
+           "m2rnn_step.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are switched off for every kernel.  MFMA

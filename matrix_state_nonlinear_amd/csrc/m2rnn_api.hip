@@ -207,4 +207,24 @@ int m2rnn_bwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K
   return status_of(launch_bwd(a, in_dtype, state_dtype, (hipStream_t)stream));
 }
 
+int m2rnn_step(int64_t B, int64_t n_heads, int64_t qk_heads, int64_t K, int64_t V, int in_dtype,
+               int state_dtype, const void* k, const void* v, const void* q, const void* f,
+               const void* W, const void* w_r, void* H, void* y, void* stream) {
+  if (!sizes_ok(B, 1, n_heads, K, V) || !qk_heads_ok(n_heads, qk_heads))
+    return M2RNN_ERR_INVALID_ARG;
+  if (!in_dtype_known(in_dtype) || !state_dtype_known(state_dtype)) return M2RNN_ERR_INVALID_ARG;
+  const bool empty = B * n_heads == 0;
+  if (!empty && (!k || !v || !q || !f || !W || !w_r || !H || !y)) return M2RNN_ERR_INVALID_ARG;
+  // one workgroup per head and group of four batch rows
+  if (K > 256 || V > 128 || (double)n_heads * (double)((B + 3) / 4) >= 2147483648.0 ||
+      !dtypes_ok(in_dtype, state_dtype))
+    return M2RNN_ERR_UNSUPPORTED;
+  if (empty) return M2RNN_OK;  // no unit: nothing is read or written
+  StepArgs a{};
+  a.k = k; a.v = v; a.q = q; a.f = f; a.W = W; a.w_r = w_r; a.H = H; a.y = y;
+  a.B = B; a.N = n_heads; a.NQ = qk_heads; a.K = K; a.V = V;
+  a.vec = state_dtype == M2RNN_F32 && (V & 3) == 0 && ((uintptr_t)H & 15) == 0;
+  return status_of(launch_step(a, in_dtype, state_dtype, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -102,10 +102,25 @@ struct BwdWorkspace {
 BwdWorkspace bwd_workspace_layout(int64_t B, int64_t T, int64_t N, int64_t NQ, int64_t K,
                                   int64_t V, int64_t C, int state_dtype);
 
+struct StepArgs {
+  const void* k;     // [B, NQ, K]
+  const void* v;     // [B, N, V]
+  const void* q;     // [B, NQ, K]
+  const void* f;     // [B, N]
+  const void* W;
+  const void* w_r;
+  void* H;           // [B, N, K, V], updated in place
+  void* y;           // [B, N, V]
+  int64_t B, N, NQ, K, V;
+  int vec;           // fp32 state, V % 4 == 0 and H 16-byte aligned: 16-byte state accesses
+  int64_t upw;       // batch rows (units) per wave, set by the launcher
+};
+
 hipError_t launch_gates(int64_t B, int64_t T, int64_t N, int gate_kind, int dtype,
                         const void* logit, const void* alpha, const void* beta, void* f,
                         hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, int in_dtype, int state_dtype, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int in_dtype, int state_dtype, hipStream_t stream);
+hipError_t launch_step(const StepArgs& a, int in_dtype, int state_dtype, hipStream_t stream);
 
 }  // namespace m2rnn

@@ -174,3 +174,30 @@ def m2rnn_bwd(k, v, q, gate_kind: int, logit, alpha, beta, f, W, w_r, H0, ckpt, 
         _ptr(out["dbeta"]), _ptr(out["dH0"]), _ptr(ws), wsb, _stream(dev))
     check(st, "m2rnn_bwd")
     return out
+
+
+def m2rnn_step(H, k, v, q, f, W, w_r, out=None):
+    """One token of every sequence (decoding): H [B, N, K, V] (state dtype) is
+    updated in place from H_{t-1} to H_t, and y [B, N, V] is returned.  k, q
+    [B, NQ, K] and v [B, N, V] in the input dtype, f [B, N], W [N, V, V] and
+    w_r [N, V] in the state dtype (taken from H)."""
+    if H.dim() != 4 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("H must be [B, N, K, V], k and q [B, qk_heads, K], v [B, n_heads, V]")
+    B, N, K, V = H.shape
+    NQ = k.shape[1]
+    if (NQ < 1 or NQ > N or N % NQ) if N > 0 else NQ != 0:
+        raise ValueError(f"qk_heads = {NQ} must divide n_heads = {N}")
+    sd = H.dtype
+    _need(H, (B, N, K, V), sd, "H")
+    _need(k, (B, NQ, K), k.dtype, "k")
+    _need(q, (B, NQ, K), k.dtype, "q")
+    _need(v, (B, N, V), k.dtype, "v")
+    _need(f, (B, N), sd, "f")
+    _need(W, (N, V, V), sd, "W")
+    _need(w_r, (N, V), sd, "w_r")
+    y = torch.empty((B, N, V), dtype=sd, device=H.device) if out is None else out
+    _need(y, (B, N, V), sd, "out")
+    st = _lib.lib().m2rnn_step(B, N, NQ, K, V, _DT[k.dtype], _DT[sd], _ptr(k), _ptr(v), _ptr(q),
+                               _ptr(f), _ptr(W), _ptr(w_r), _ptr(H), _ptr(y), _stream(H.device))
+    check(st, "m2rnn_step")
+    return y

@@ -173,3 +173,31 @@ def test_bwd_rejects_bad_arguments(L):
     assert bwd(L, V=200) == E.M2RNN_ERR_UNSUPPORTED
     assert bwd(L) == E.M2RNN_ERR_WORKSPACE                             # always needs workspace
     assert bwd(L, ws=FAKE, wsb=64) == E.M2RNN_ERR_WORKSPACE
+
+
+def step(L, **kw):
+    a = dict(B=2, N=2, NQ=None, K=16, V=16, ind=_lib.M2RNN_F32, sd=_lib.M2RNN_F32, k=FAKE,
+             v=FAKE, q=FAKE, f=FAKE, W=FAKE, w_r=FAKE, H=FAKE, y=FAKE, stream=None)
+    a.update(kw)
+    NQ = a["N"] if a["NQ"] is None else a["NQ"]
+    return L.m2rnn_step(a["B"], a["N"], NQ, a["K"], a["V"], a["ind"], a["sd"], a["k"], a["v"],
+                        a["q"], a["f"], a["W"], a["w_r"], a["H"], a["y"], a["stream"])
+
+
+def test_step_rejects_bad_arguments(L):
+    E = _lib
+    assert step(L, B=-1) == E.M2RNN_ERR_INVALID_ARG
+    assert step(L, K=0) == E.M2RNN_ERR_INVALID_ARG
+    assert step(L, V=0) == E.M2RNN_ERR_INVALID_ARG
+    assert step(L, N=4, NQ=3) == E.M2RNN_ERR_INVALID_ARG
+    assert step(L, N=4, NQ=0) == E.M2RNN_ERR_INVALID_ARG
+    assert step(L, H=None) == E.M2RNN_ERR_INVALID_ARG
+    assert step(L, y=None) == E.M2RNN_ERR_INVALID_ARG
+    assert step(L, sd=9) == E.M2RNN_ERR_INVALID_ARG
+    assert step(L, K=257) == E.M2RNN_ERR_UNSUPPORTED
+    assert step(L, V=129) == E.M2RNN_ERR_UNSUPPORTED
+    assert step(L, ind=E.M2RNN_F64) == E.M2RNN_ERR_UNSUPPORTED
+    # no (b, n) unit: nothing is read or written, nothing launched
+    none = dict(k=None, v=None, q=None, f=None, W=None, w_r=None, H=None, y=None)
+    assert step(L, B=0, **none) == E.M2RNN_OK
+    assert step(L, N=0, NQ=0, **none) == E.M2RNN_OK
