@@ -23,3 +23,12 @@ from .m2rnn_oracle import (  # noqa: F401
     step_jacobian_dense,
     tangent_growth,
 )
+from .m2rnn_block import (  # noqa: F401
+    silu,
+    silu_grad,
+    causal_conv,
+    conv_silu,
+    conv_silu_backward,
+    gate_rmsnorm,
+    gate_rmsnorm_backward,
+)
