@@ -177,6 +177,76 @@ int m2rnn_step(int64_t B, int64_t n_heads, int64_t qk_heads, int64_t K, int64_t 
                int state_dtype, const void* k, const void* v, const void* q, const void* f,
                const void* W, const void* w_r, void* H, void* y, void* stream);
 
+/*
+ * The block around the recurrence (review section 2.3, Eq. 14-23): q, k, v each
+ * pass a linear projection, a depthwise causal Conv1D of kernel size 4 and SiLU
+ * (the prologue below); the output gate g = SiLU(W_g x) multiplies the readout,
+ * which is then RMS-normalised (the epilogue).  The projections are plain GEMMs
+ * and are not part of this library.  For these entry points `io_dtype` (F32,
+ * BF16 or F64) is the storage type of x, out and g_pre; `param_dtype` (F32 or
+ * F64, paired as for m2rnn_fwd) that of w, bias, gamma, y and every gradient,
+ * and the precision of the arithmetic.  bf16 outputs are rounded to nearest
+ * even.  Parameter gradients are sums over all tokens, reduced in a fixed order.
+ *
+ * Workspace of m2rnn_conv_silu_bwd (op 0: x is [B, T, C]) or of
+ * m2rnn_gate_rmsnorm_bwd (op 1: rows = B * T, D = C); 0 = none.
+ */
+size_t m2rnn_block_workspace_bytes(int op, int64_t B, int64_t T, int64_t C, int param_dtype);
+
+/*
+ * m2rnn_conv_silu -- prologue on one projected tensor:
+ *     out_t[c] = SiLU(u_t[c]),  u_t[c] = bias[c] + sum_{i=0..3} w[c][i] x_{t-3+i}[c],
+ * with x_{t<0} = 0 (each sequence starts with no history).
+ *   x    [B, T, C]   in, io_dtype
+ *   w    [C, 4]      in, param_dtype (tap i weights the input 3 - i steps back)
+ *   bias [C]         in, param_dtype, or NULL for none
+ *   out  [B, T, C]   out, io_dtype (may feed m2rnn_fwd as k, v or q)
+ */
+int m2rnn_conv_silu(int64_t B, int64_t T, int64_t C, int io_dtype, int param_dtype,
+                    const void* x, const void* w, const void* bias, void* out, void* stream);
+
+/*
+ * m2rnn_conv_silu_bwd -- gradients of sum(dout * out):
+ *     du = dout SiLU'(u),  dx_s = sum_i w[i] du_{s+3-i},
+ *     dw[c][i] = sum_{b,t} du_t[c] x_{t-3+i}[c],  dbias[c] = sum_{b,t} du_t[c].
+ *   x, w, bias  as for m2rnn_conv_silu (u is recomputed)
+ *   dout [B, T, C]   in, param_dtype (e.g. dk, dv or dq from m2rnn_bwd)
+ *   dx   [B, T, C]   out, param_dtype
+ *   dw   [C, 4]      out;  dbias [C] out, non-NULL exactly when bias is
+ *   workspace / workspace_bytes: at least m2rnn_block_workspace_bytes(0, B, T, C, param_dtype)
+ */
+int m2rnn_conv_silu_bwd(int64_t B, int64_t T, int64_t C, int io_dtype, int param_dtype,
+                        const void* x, const void* w, const void* bias, const void* dout, void* dx,
+                        void* dw, void* dbias, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
+ * m2rnn_gate_rmsnorm -- epilogue on the readout of each token:
+ *     z = y (.) SiLU(g_pre),  out = gamma (.) z / sqrt(mean_D(z^2) + eps)
+ * (gate first, then RMSNorm over the D = n_heads * V channels of the token).
+ *   y      [rows, D]   in, param_dtype (m2rnn_fwd's y, rows = B * T)
+ *   g_pre  [rows, D]   in, io_dtype (the gate projection W_g x)
+ *   gamma  [D]         in, param_dtype
+ *   eps    >= 0
+ *   out    [rows, D]   out, io_dtype
+ */
+int m2rnn_gate_rmsnorm(int64_t rows, int64_t D, int io_dtype, int param_dtype, double eps,
+                       const void* y, const void* g_pre, const void* gamma, void* out,
+                       void* stream);
+
+/*
+ * m2rnn_gate_rmsnorm_bwd -- gradients of sum(dout * out): with r = 1 / sqrt(mean(z^2) + eps),
+ * zh = z r and dzh = dout gamma:  dz = r (dzh - zh mean_D(dzh zh)),
+ * dy = dz SiLU(g_pre),  dg_pre = dz y SiLU'(g_pre),  dgamma = sum_rows dout zh.
+ *   y, g_pre, gamma, eps   as for m2rnn_gate_rmsnorm
+ *   dout [rows, D]  in, param_dtype;  dy, dg_pre [rows, D] out, param_dtype;  dgamma [D] out
+ *   workspace / workspace_bytes: at least m2rnn_block_workspace_bytes(1, rows, 1, D, param_dtype)
+ */
+int m2rnn_gate_rmsnorm_bwd(int64_t rows, int64_t D, int io_dtype, int param_dtype, double eps,
+                           const void* y, const void* g_pre, const void* gamma, const void* dout,
+                           void* dy, void* dg_pre, void* dgamma, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

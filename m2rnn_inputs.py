@@ -228,3 +228,53 @@ def to_device(inp: Inputs, state_dtype="float32", device="cuda:0") -> dict:
     for name in ("logit", "alpha", "beta", "W", "w_r", "H0", "dy", "dHT"):
         out[name] = t(getattr(inp, name))
     return out
+
+
+# ---------------------------------------------------------------- block around the recurrence
+
+@dataclasses.dataclass
+class ConvInputs:
+    """Prologue inputs: x [B, T, C] (exact bf16 values when bf16; x_bits the
+    patterns), w [C, 4], bias [C], dout [B, T, C]."""
+    x: np.ndarray
+    w: np.ndarray
+    bias: np.ndarray
+    dout: np.ndarray
+    x_bits: np.ndarray | None = None
+
+
+def make_conv_inputs(B: int, T: int, C: int, seed: int = 11, bf16: bool = True) -> ConvInputs:
+    """x ~ N(0, 1) (a projection output), w ~ N(0, 1/4) per tap (fan-in 4),
+    bias ~ N(0, 0.1), dout ~ N(0, 1); draw order x, w, bias, dout."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    f32 = np.float32
+    x = rng.standard_normal((B, T, C), dtype=f32)
+    w = rng.standard_normal((C, 4), dtype=f32) * f32(0.5)
+    bias = rng.standard_normal(C, dtype=f32) * f32(0.1)
+    dout = rng.standard_normal((B, T, C), dtype=f32)
+    x, xb = _rounded(x, bf16)
+    return ConvInputs(x=x, w=w, bias=bias, dout=dout, x_bits=xb)
+
+
+@dataclasses.dataclass
+class NormInputs:
+    """Epilogue inputs: y [rows, D] (a readout), g_pre [rows, D] (exact bf16
+    values when bf16), gamma [D], dout [rows, D]."""
+    y: np.ndarray
+    g_pre: np.ndarray
+    gamma: np.ndarray
+    dout: np.ndarray
+    g_bits: np.ndarray | None = None
+
+
+def make_norm_inputs(rows: int, D: int, seed: int = 12, bf16: bool = True) -> NormInputs:
+    """y ~ N(0, 0.5), g_pre ~ N(0, 1), gamma ~ U(0.5, 1.5), dout ~ N(0, 1);
+    draw order y, g_pre, gamma, dout."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    f32 = np.float32
+    y = rng.standard_normal((rows, D), dtype=f32) * f32(0.5)
+    g = rng.standard_normal((rows, D), dtype=f32)
+    gamma = rng.uniform(0.5, 1.5, D).astype(f32)
+    dout = rng.standard_normal((rows, D), dtype=f32)
+    g, gb = _rounded(g, bf16)
+    return NormInputs(y=y, g_pre=g, gamma=gamma, dout=dout, g_bits=gb)

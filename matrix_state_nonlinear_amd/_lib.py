@@ -39,6 +39,14 @@ SIGNATURES = {
                          _vp, _sz, _vp]),
     "m2rnn_step": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int,
                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "m2rnn_block_workspace_bytes": (_sz, [_int, _i64, _i64, _i64, _int]),
+    "m2rnn_conv_silu": (_int, [_i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp]),
+    "m2rnn_conv_silu_bwd": (_int, [_i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp,
+                                   _vp, _vp, _vp, _sz, _vp]),
+    "m2rnn_gate_rmsnorm": (_int, [_i64, _i64, _int, _int, ctypes.c_double, _vp, _vp, _vp, _vp,
+                                  _vp]),
+    "m2rnn_gate_rmsnorm_bwd": (_int, [_i64, _i64, _int, _int, ctypes.c_double, _vp, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
 _lib = None

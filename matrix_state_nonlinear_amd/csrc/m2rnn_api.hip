@@ -32,6 +32,15 @@ bool sizes_supported(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V) {
   return (double)B * (double)N * (double)num_slabs(K) < (double)(1 << 22);
 }
 
+// The block kernels' one-dimensional grids: at most (tokens / 16 + B) x
+// ceil(C / 256) and tokens / 4 workgroups, below 2^31.
+bool block_grid_ok(int64_t B, int64_t T, int64_t C) {
+  const double tok = (double)B * (double)T;
+  const double cb = (double)((C + 255) / 256);
+  return (tok / 16.0 + (double)B) * cb < 2147483647.0 && tok / 4.0 < 2147483647.0 &&
+         C < ((int64_t)1 << 40);
+}
+
 size_t real_size(int state_dtype) { return state_dtype == M2RNN_F64 ? 8 : 4; }
 
 bool dtypes_ok(int in_dtype, int state_dtype) {
@@ -225,6 +234,91 @@ int m2rnn_step(int64_t B, int64_t n_heads, int64_t qk_heads, int64_t K, int64_t 
   a.B = B; a.N = n_heads; a.NQ = qk_heads; a.K = K; a.V = V;
   a.vec = state_dtype == M2RNN_F32 && (V & 3) == 0 && ((uintptr_t)H & 15) == 0;
   return status_of(launch_step(a, in_dtype, state_dtype, (hipStream_t)stream));
+}
+
+size_t m2rnn_block_workspace_bytes(int op, int64_t B, int64_t T, int64_t C, int param_dtype) {
+  if (B < 0 || T < 0 || C < 1 || !state_dtype_known(param_dtype)) return 0;
+  if (B * T == 0) return 0;
+  size_t elems;
+  if (op == 0) elems = conv_bwd_workspace_elems(B, T, C);
+  else if (op == 1) elems = rmsnorm_bwd_workspace_elems(B * T, C);
+  else return 0;
+  return align_up(elems * real_size(param_dtype), 256);
+}
+
+int m2rnn_conv_silu(int64_t B, int64_t T, int64_t C, int io_dtype, int param_dtype,
+                    const void* x, const void* w, const void* bias, void* out, void* stream) {
+  if (B < 0 || T < 0 || C < 1 || !in_dtype_known(io_dtype) || !state_dtype_known(param_dtype))
+    return M2RNN_ERR_INVALID_ARG;
+  const bool empty = B * T == 0;
+  if (!empty && (!x || !w || !out)) return M2RNN_ERR_INVALID_ARG;
+  if (!dtypes_ok(io_dtype, param_dtype) || !block_grid_ok(B, T, C)) return M2RNN_ERR_UNSUPPORTED;
+  if (empty) return M2RNN_OK;
+  BlockConvArgs a{};
+  a.B = B; a.T = T; a.C = C; a.x = x; a.w = w; a.bias = bias; a.out = out;
+  return status_of(launch_conv_silu(a, io_dtype, param_dtype, false, (hipStream_t)stream));
+}
+
+int m2rnn_conv_silu_bwd(int64_t B, int64_t T, int64_t C, int io_dtype, int param_dtype,
+                        const void* x, const void* w, const void* bias, const void* dout, void* dx,
+                        void* dw, void* dbias, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (B < 0 || T < 0 || C < 1 || !in_dtype_known(io_dtype) || !state_dtype_known(param_dtype))
+    return M2RNN_ERR_INVALID_ARG;
+  const bool empty = B * T == 0;
+  if (!w || !dw || (bias == nullptr) != (dbias == nullptr)) return M2RNN_ERR_INVALID_ARG;
+  if (!empty && (!x || !dout || !dx)) return M2RNN_ERR_INVALID_ARG;
+  if (!dtypes_ok(io_dtype, param_dtype) || !block_grid_ok(B, T, C)) return M2RNN_ERR_UNSUPPORTED;
+  const hipStream_t st = (hipStream_t)stream;
+  if (empty) {  // sums over no tokens
+    hipError_t e = fill(dw, nullptr, C * 4, param_dtype, st);
+    if (e == hipSuccess) e = fill(dbias, nullptr, C, param_dtype, st);
+    return status_of(e);
+  }
+  const size_t need = m2rnn_block_workspace_bytes(0, B, T, C, param_dtype);
+  if (!workspace || workspace_bytes < need) return M2RNN_ERR_WORKSPACE;
+  BlockConvArgs a{};
+  a.B = B; a.T = T; a.C = C; a.x = x; a.w = w; a.bias = bias; a.dout = dout; a.dx = dx;
+  a.dw = dw; a.dbias = dbias; a.ws = workspace;
+  return status_of(launch_conv_silu(a, io_dtype, param_dtype, true, st));
+}
+
+int m2rnn_gate_rmsnorm(int64_t rows, int64_t D, int io_dtype, int param_dtype, double eps,
+                       const void* y, const void* g_pre, const void* gamma, void* out,
+                       void* stream) {
+  if (rows < 0 || D < 1 || !(eps >= 0.0) || eps > 1e30 || !in_dtype_known(io_dtype) ||
+      !state_dtype_known(param_dtype))
+    return M2RNN_ERR_INVALID_ARG;
+  const bool empty = rows == 0;
+  if (!empty && (!y || !g_pre || !gamma || !out)) return M2RNN_ERR_INVALID_ARG;
+  if (!dtypes_ok(io_dtype, param_dtype) || !block_grid_ok(rows, 1, D))
+    return M2RNN_ERR_UNSUPPORTED;
+  if (empty) return M2RNN_OK;
+  BlockNormArgs a{};
+  a.rows = rows; a.D = D; a.eps = eps; a.y = y; a.g_pre = g_pre; a.gamma = gamma; a.out = out;
+  return status_of(launch_gate_rmsnorm(a, io_dtype, param_dtype, false, (hipStream_t)stream));
+}
+
+int m2rnn_gate_rmsnorm_bwd(int64_t rows, int64_t D, int io_dtype, int param_dtype, double eps,
+                           const void* y, const void* g_pre, const void* gamma, const void* dout,
+                           void* dy, void* dg_pre, void* dgamma, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (rows < 0 || D < 1 || !(eps >= 0.0) || eps > 1e30 || !in_dtype_known(io_dtype) ||
+      !state_dtype_known(param_dtype))
+    return M2RNN_ERR_INVALID_ARG;
+  const bool empty = rows == 0;
+  if (!dgamma) return M2RNN_ERR_INVALID_ARG;
+  if (!empty && (!y || !g_pre || !gamma || !dout || !dy || !dg_pre)) return M2RNN_ERR_INVALID_ARG;
+  if (!dtypes_ok(io_dtype, param_dtype) || !block_grid_ok(rows, 1, D))
+    return M2RNN_ERR_UNSUPPORTED;
+  const hipStream_t st = (hipStream_t)stream;
+  if (empty) return status_of(fill(dgamma, nullptr, D, param_dtype, st));
+  const size_t need = m2rnn_block_workspace_bytes(1, rows, 1, D, param_dtype);
+  if (!workspace || workspace_bytes < need) return M2RNN_ERR_WORKSPACE;
+  BlockNormArgs a{};
+  a.rows = rows; a.D = D; a.eps = eps; a.y = y; a.g_pre = g_pre; a.gamma = gamma;
+  a.dout = dout; a.dy = dy; a.dg_pre = dg_pre; a.dgamma = dgamma; a.ws = workspace;
+  return status_of(launch_gate_rmsnorm(a, io_dtype, param_dtype, true, st));
 }
 
 }  // extern "C"

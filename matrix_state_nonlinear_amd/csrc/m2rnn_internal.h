@@ -116,6 +116,39 @@ struct StepArgs {
   int64_t upw;       // batch rows (units) per wave, set by the launcher
 };
 
+// Block prologue (causal conv + SiLU) and epilogue (gate + RMSNorm).
+struct BlockConvArgs {
+  int64_t B, T, C;
+  const void* x;     // [B, T, C] io dtype
+  const void* w;     // [C, 4]
+  const void* bias;  // [C] or null
+  void* out;         // [B, T, C] io dtype (forward)
+  const void* dout;  // [B, T, C] (backward)
+  void* dx;          // [B, T, C] (backward)
+  void* dw;          // [C, 4] (backward)
+  void* dbias;       // [C] or null (backward)
+  void* ws;          // backward partials
+};
+struct BlockNormArgs {
+  int64_t rows, D;
+  double eps;
+  const void* y;      // [rows, D]
+  const void* g_pre;  // [rows, D] io dtype
+  const void* gamma;  // [D]
+  void* out;          // [rows, D] io dtype (forward)
+  const void* dout;   // [rows, D] (backward)
+  void* dy;           // (backward)
+  void* dg_pre;       // (backward)
+  void* dgamma;       // [D] (backward)
+  void* ws;           // backward: per-row 1/rms and dgamma partials
+};
+size_t conv_bwd_workspace_elems(int64_t B, int64_t T, int64_t C);
+size_t rmsnorm_bwd_workspace_elems(int64_t rows, int64_t D);
+hipError_t launch_conv_silu(const BlockConvArgs& a, int io_dtype, int param_dtype, bool bwd,
+                            hipStream_t stream);
+hipError_t launch_gate_rmsnorm(const BlockNormArgs& a, int io_dtype, int param_dtype, bool bwd,
+                               hipStream_t stream);
+
 hipError_t launch_gates(int64_t B, int64_t T, int64_t N, int gate_kind, int dtype,
                         const void* logit, const void* alpha, const void* beta, void* f,
                         hipStream_t stream);

@@ -201,3 +201,86 @@ def m2rnn_step(H, k, v, q, f, W, w_r, out=None):
                                _ptr(f), _ptr(W), _ptr(w_r), _ptr(H), _ptr(y), _stream(H.device))
     check(st, "m2rnn_step")
     return y
+
+
+def _io_param(x, param):
+    """(io dtype code, param dtype code) of a block call; param from the parameters."""
+    if param.dtype not in (torch.float32, torch.float64):
+        raise ValueError("parameters must be float32 or float64")
+    return _DT[x.dtype], _DT[param.dtype]
+
+
+def m2rnn_conv_silu(x, w, bias=None, out=None):
+    """Block prologue on one projected tensor x [B, T, C] (float32 / bfloat16, or
+    float64 / bfloat16): SiLU of the depthwise causal convolution with w [C, 4]
+    (+ bias [C]); returns [B, T, C] in x's dtype."""
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, C]")
+    B, T, C = x.shape
+    io, pd = _io_param(x, w)
+    _need(w, (C, 4), w.dtype, "w")
+    _opt(bias, (C,), w.dtype, "bias")
+    y = torch.empty_like(x) if out is None else out
+    _need(y, (B, T, C), x.dtype, "out")
+    st = _lib.lib().m2rnn_conv_silu(B, T, C, io, pd, _ptr(x), _ptr(w), _ptr(bias), _ptr(y),
+                                    _stream(x.device))
+    check(st, "m2rnn_conv_silu")
+    return y
+
+
+def m2rnn_conv_silu_bwd(x, w, bias, dout, workspace=None):
+    """Gradients of sum(dout * m2rnn_conv_silu(x, w, bias)): (dx, dw, dbias or None),
+    in the parameters' dtype."""
+    B, T, C = x.shape
+    io, pd = _io_param(x, w)
+    _need(w, (C, 4), w.dtype, "w")
+    _opt(bias, (C,), w.dtype, "bias")
+    _need(dout, (B, T, C), w.dtype, "dout")
+    dx = torch.empty((B, T, C), dtype=w.dtype, device=x.device)
+    dw = torch.empty((C, 4), dtype=w.dtype, device=x.device)
+    dbias = torch.empty((C,), dtype=w.dtype, device=x.device) if bias is not None else None
+    nb = int(_lib.lib().m2rnn_block_workspace_bytes(0, B, T, C, pd))
+    ws, wsb = _workspace(nb, x.device, workspace)
+    st = _lib.lib().m2rnn_conv_silu_bwd(B, T, C, io, pd, _ptr(x), _ptr(w), _ptr(bias),
+                                        _ptr(dout), _ptr(dx), _ptr(dw), _ptr(dbias), _ptr(ws),
+                                        wsb, _stream(x.device))
+    check(st, "m2rnn_conv_silu_bwd")
+    return dx, dw, dbias
+
+
+def m2rnn_gate_rmsnorm(y, g_pre, gamma, eps: float = 1e-6, out=None):
+    """Block epilogue: gamma * z / sqrt(mean(z^2) + eps), z = y * SiLU(g_pre), over the
+    last dimension D.  y [..., D] and gamma [D] in the state dtype, g_pre [..., D] in the
+    input dtype; returns [..., D] in g_pre's dtype."""
+    D = y.shape[-1]
+    rows = y.numel() // D if D else 0
+    io, pd = _io_param(g_pre, y)
+    _need(g_pre, tuple(y.shape), g_pre.dtype, "g_pre")
+    _need(gamma, (D,), y.dtype, "gamma")
+    o = torch.empty(tuple(y.shape), dtype=g_pre.dtype, device=y.device) if out is None else out
+    _need(o, tuple(y.shape), g_pre.dtype, "out")
+    st = _lib.lib().m2rnn_gate_rmsnorm(rows, D, io, pd, float(eps), _ptr(y), _ptr(g_pre),
+                                       _ptr(gamma), _ptr(o), _stream(y.device))
+    check(st, "m2rnn_gate_rmsnorm")
+    return o
+
+
+def m2rnn_gate_rmsnorm_bwd(y, g_pre, gamma, dout, eps: float = 1e-6, workspace=None):
+    """Gradients of sum(dout * m2rnn_gate_rmsnorm(y, g_pre, gamma, eps)):
+    (dy, dg_pre, dgamma) in the state dtype."""
+    D = y.shape[-1]
+    rows = y.numel() // D if D else 0
+    io, pd = _io_param(g_pre, y)
+    _need(g_pre, tuple(y.shape), g_pre.dtype, "g_pre")
+    _need(gamma, (D,), y.dtype, "gamma")
+    _need(dout, tuple(y.shape), y.dtype, "dout")
+    dy = torch.empty_like(y)
+    dg = torch.empty_like(y)
+    dgamma = torch.empty((D,), dtype=y.dtype, device=y.device)
+    nb = int(_lib.lib().m2rnn_block_workspace_bytes(1, rows, 1, D, pd))
+    ws, wsb = _workspace(nb, y.device, workspace)
+    st = _lib.lib().m2rnn_gate_rmsnorm_bwd(rows, D, io, pd, float(eps), _ptr(y), _ptr(g_pre),
+                                           _ptr(gamma), _ptr(dout), _ptr(dy), _ptr(dg),
+                                           _ptr(dgamma), _ptr(ws), wsb, _stream(y.device))
+    check(st, "m2rnn_gate_rmsnorm_bwd")
+    return dy, dg, dgamma

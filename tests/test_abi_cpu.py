@@ -201,3 +201,44 @@ def test_step_rejects_bad_arguments(L):
     none = dict(k=None, v=None, q=None, f=None, W=None, w_r=None, H=None, y=None)
     assert step(L, B=0, **none) == E.M2RNN_OK
     assert step(L, N=0, NQ=0, **none) == E.M2RNN_OK
+
+
+def test_block_entry_points_reject_bad_arguments(L):
+    E = _lib
+    F32, BF, F64 = E.M2RNN_F32, E.M2RNN_BF16, E.M2RNN_F64
+    conv = L.m2rnn_conv_silu
+    assert conv(-1, 4, 8, BF, F32, FAKE, FAKE, None, FAKE, None) == E.M2RNN_ERR_INVALID_ARG
+    assert conv(2, 4, 0, BF, F32, FAKE, FAKE, None, FAKE, None) == E.M2RNN_ERR_INVALID_ARG
+    assert conv(2, 4, 8, BF, F32, None, FAKE, None, FAKE, None) == E.M2RNN_ERR_INVALID_ARG
+    assert conv(2, 4, 8, BF, BF, FAKE, FAKE, None, FAKE, None) == E.M2RNN_ERR_INVALID_ARG
+    assert conv(2, 4, 8, F64, F32, FAKE, FAKE, None, FAKE, None) == E.M2RNN_ERR_UNSUPPORTED
+    assert conv(0, 4, 8, BF, F32, None, None, None, None, None) == E.M2RNN_OK
+    cb = L.m2rnn_conv_silu_bwd
+    # dbias must be given exactly when bias is
+    assert cb(2, 4, 8, BF, F32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20,
+              None) == E.M2RNN_ERR_INVALID_ARG
+    assert cb(2, 4, 8, BF, F32, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+              None) == E.M2RNN_ERR_INVALID_ARG
+    assert cb(2, 4, 8, BF, F32, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, 0,
+              None) == E.M2RNN_ERR_WORKSPACE
+    assert cb(2, 4, 8, BF, F32, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, 16,
+              None) == E.M2RNN_ERR_WORKSPACE
+    ws = L.m2rnn_block_workspace_bytes
+    # conv: partials [B * ceil(T / 64), C, 5]; norm: per-row 1/rms (64-aligned) and
+    # dgamma partials, max(ceil(rows / 256), min(ceil(rows / 4), 1024)) rows of D
+    assert ws(0, 2, 130, 8, F32) == ((2 * 3 * 8 * 5 * 4 + 255) // 256) * 256
+    assert ws(1, 3, 100, 24, F32) == (((320 + 75 * 24) * 4 + 255) // 256) * 256
+    assert ws(1, 3, 100, 24, F64) == (((320 + 75 * 24) * 8 + 255) // 256) * 256
+    assert ws(1, 1, 1 << 20, 8, F32) == (((1 << 20) + 4096 * 8) * 4 + 255) // 256 * 256
+    assert ws(2, 3, 100, 24, F32) == 0 and ws(0, 0, 100, 24, F32) == 0
+    rn = L.m2rnn_gate_rmsnorm
+    assert rn(4, 8, BF, F32, -1.0, FAKE, FAKE, FAKE, FAKE, None) == E.M2RNN_ERR_INVALID_ARG
+    assert rn(4, 8, BF, F32, float("nan"), FAKE, FAKE, FAKE, FAKE, None) == E.M2RNN_ERR_INVALID_ARG
+    assert rn(4, 0, BF, F32, 1e-6, FAKE, FAKE, FAKE, FAKE, None) == E.M2RNN_ERR_INVALID_ARG
+    assert rn(4, 8, BF, F32, 1e-6, FAKE, None, FAKE, FAKE, None) == E.M2RNN_ERR_INVALID_ARG
+    assert rn(0, 8, BF, F32, 1e-6, None, None, None, None, None) == E.M2RNN_OK
+    rb = L.m2rnn_gate_rmsnorm_bwd
+    assert rb(4, 8, BF, F32, 1e-6, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20,
+              None) == E.M2RNN_ERR_INVALID_ARG
+    assert rb(4, 8, BF, F32, 1e-6, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4,
+              None) == E.M2RNN_ERR_WORKSPACE
