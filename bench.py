@@ -44,10 +44,13 @@ def parse():
                     help="target duration of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true",
-                    help="skip the MFMA fraction of every workload and the decode-step rates")
+                    help="skip the MFMA fraction of every workload and the decode-step and "
+                         "block-kernel rates")
     ap.add_argument("--decode-only", action="store_true",
                     help="only time the single-token step on the decoding workloads and "
                          "print those rates")
+    ap.add_argument("--block-only", action="store_true",
+                    help="only time the block prologue / epilogue kernels and print those rates")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="first copy this many GiB twice with torch (a plain copy of known "
                          "size, to calibrate HBM byte counters)")
@@ -172,6 +175,67 @@ def decode_rates(reps=50):
     return rows
 
 
+def block_rates(reps=20):
+    """The block around the recurrence at the long-context workload's sizes:
+    the causal conv + SiLU prologue on one projected tensor [4, 16384, 1024]
+    (bf16, e.g. v of 16 heads x 64) and the gate + RMSNorm epilogue on the
+    readout [65536, 1024], forward and backward.  HBM-bound; algorithmic bytes
+    per element: conv forward 2 s_in (read x, write out), conv backward s_in + 8
+    (x, dout, dx), epilogue forward 4 + 2 s_in (y, g_pre, out), backward 16 + s_in
+    (y, g_pre, dout, dy, dg_pre); parameter partials are not counted."""
+    import numpy as np
+    import torch
+
+    from m2rnn_inputs import make_conv_inputs, make_norm_inputs
+    from matrix_state_nonlinear_amd import (m2rnn_conv_silu, m2rnn_conv_silu_bwd,
+                                            m2rnn_gate_rmsnorm, m2rnn_gate_rmsnorm_bwd)
+    from matrix_state_nonlinear_amd._lib import lib
+
+    B, T, C = 4, 16384, 1024
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        stream.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        stream.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    bf = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    f32 = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
+    ci = make_conv_inputs(B, T, C, seed=1)
+    x, w, b, dout = bf(ci.x_bits), f32(ci.w), f32(ci.bias), f32(ci.dout)
+    ws = torch.empty(int(lib().m2rnn_block_workspace_bytes(0, B, T, C, 0)), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty_like(x)
+    E = B * T * C
+    rows = []
+    us = timed(lambda: m2rnn_conv_silu(x, w, b, out=out))
+    rows.append(("conv_silu", us, E * 4))
+    us = timed(lambda: m2rnn_conv_silu_bwd(x, w, b, dout, workspace=ws))
+    rows.append(("conv_silu_bwd", us, E * 10))
+    del x, w, b, dout, ws, out, ci
+    ni = make_norm_inputs(B * T, C, seed=2)
+    y, g, gamma, nd = f32(ni.y), bf(ni.g_bits), f32(ni.gamma), f32(ni.dout)
+    ws = torch.empty(int(lib().m2rnn_block_workspace_bytes(1, B * T, 1, C, 0)),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty_like(g)
+    us = timed(lambda: m2rnn_gate_rmsnorm(y, g, gamma, 1e-6, out=o))
+    rows.append(("gate_rmsnorm", us, E * 8))
+    us = timed(lambda: m2rnn_gate_rmsnorm_bwd(y, g, gamma, nd, 1e-6, workspace=ws))
+    rows.append(("gate_rmsnorm_bwd", us, E * 18))
+    del y, g, gamma, nd, ws, o, ni
+    torch.cuda.empty_cache()
+    return [{"op": op, "shape": [B, T, C], "us": us, "bytes": nb, "hbm_gbs": nb / us / 1e3,
+             "hbm_frac": nb / us / 1e3 / HBM_PEAK_GBS} for op, us, nb in rows]
+
+
 def oracle_baseline(wl, target_s):
     """float64 oracle (forward + backward) on the first Ts steps of every unit."""
     import numpy as np
@@ -223,9 +287,10 @@ def main():
     from matrix_state_nonlinear_amd import m2rnn_bwd, m2rnn_fwd, m2rnn_gates
     from matrix_state_nonlinear_amd.ops import m2rnn_workspace_bytes
 
-    if args.decode_only:
+    if args.decode_only or args.block_only:
         torch.cuda.set_device(0)
-        print(json.dumps({"decode": decode_rates()}), flush=True)
+        print(json.dumps({"decode": decode_rates()} if args.decode_only
+                         else {"block": block_rates()}), flush=True)
         return
 
     if args.copy_calibration_gib > 0:
@@ -341,6 +406,7 @@ def main():
     if not args.no_per_config:
         out["per_config"] = per_config_fractions()
         out["decode"] = decode_rates()
+        out["block"] = block_rates()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = oracle_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
