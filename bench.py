@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip the MFMA fraction of every workload and the decode-step and "
                          "block-kernel rates")
+    ap.add_argument("--recompute", action="store_true",
+                    help="the backward recomputes the states inside each checkpoint interval "
+                         "instead of reading the per-step rc the forward stores")
     ap.add_argument("--decode-only", action="store_true",
                     help="only time the single-token step on the decoding workloads and "
                          "print those rates")
@@ -57,20 +60,25 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "m2rnn_bwd_long_t16k_k64_C4_hbm_traffic.md")
+# counter summaries of the backward call: states recomputed / stored rc read
+TRAFFIC_FILES = {
+    False: os.path.join(ROOT, "profiles", "m2rnn_bwd_long_t16k_k64_C4_hbm_traffic.md"),
+    True: os.path.join(ROOT, "profiles", "m2rnn_bwd_long_t16k_k64_C4_stored_rc_hbm_traffic.md"),
+}
 BWD_SOURCES = ("m2rnn_bwd.hip", "m2rnn_device.h", "m2rnn_internal.h")
 
 
-def measured_bwd_traffic(workload, C):
+def measured_bwd_traffic(workload, C, stored_rc):
     """HBM bytes per m2rnn_bwd call from the committed counter summary, when it
-    applies: same workload and C, and the backward's sources unchanged since
-    the counters were taken (their sha256 is recorded with the figure)."""
+    applies: same workload, C and mode, and the backward's sources unchanged
+    since the counters were taken (their sha256 is recorded with the figure)."""
     import hashlib
 
-    if workload != "long_t16k_k64" or C != 4 or not os.path.exists(TRAFFIC_FILE):
+    path = TRAFFIC_FILES[bool(stored_rc)]
+    if workload != "long_t16k_k64" or C != 4 or not os.path.exists(path):
         return None
     fields = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and line.split(":", 1)[0] in ("traffic_bytes_per_call", "source_sha256"):
             k, v = line.split(":", 1)
             fields[k] = v.strip()
@@ -320,6 +328,9 @@ def main():
     wsb = torch.empty(max(1, m2rnn_workspace_bytes(True, B, T, N, NQ, K, V, C)),
                       dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    # every step's rc = 1 / (1 + e^{2A}) from the forward, read by the backward in
+    # place of its recomputation (K V 4 bytes per token and head: 17 GB here)
+    rc = None if args.recompute else torch.empty((B, N, T, K, V), dtype=torch.float32, device=dev)
 
     names = ("gates", "fwd", "bwd")
 
@@ -330,14 +341,28 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"], None, C, out=(y, HT, ckpt),
-                  workspace=wsf)
+                  workspace=wsf, rc_out=rc)
         if ev is not None:
             ev[2].record(stream)
         g = m2rnn_bwd(d["k"], d["v"], d["q"], wl.gate, d["logit"], d["alpha"], d["beta"], f,
-                      d["W"], d["w_r"], None, ckpt, C, d["dy"], workspace=wsb)
+                      d["W"], d["w_r"], None, ckpt, C, d["dy"], workspace=wsb, rc=rc)
         if ev is not None:
             ev[3].record(stream)
         return g
+
+    def recompute_bwd_ms(reps=3):
+        # the backward that recomputes the states (no rc), on the same checkpoints
+        def run():
+            m2rnn_bwd(d["k"], d["v"], d["q"], wl.gate, d["logit"], d["alpha"], d["beta"], f,
+                      d["W"], d["w_r"], None, ckpt, C, d["dy"], workspace=wsb)
+        run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            run()
+        e1.record(stream)
+        stream.synchronize()
+        return e0.elapsed_time(e1) / reps
 
     for _ in range(args.warmup):
         step()
@@ -370,8 +395,8 @@ def main():
             gbs = th * 8 / (ms * 1e-3) / 1e9   # read logit, write f (fp32)
             entry.update({"bound": "hbm", "achieved_gbs": gbs, "frac": gbs / HBM_PEAK_GBS})
         kernels[n] = entry
-    # streamed bytes of the forward call: k, q, v, f in; y out
-    fwd_bytes = th * ((2 * K + V) * in_b + 4 + 4 * V)
+    # streamed bytes of the forward call: k, q, v, f in; y (and rc) out
+    fwd_bytes = th * ((2 * K + V) * in_b + 4 + 4 * V + (4 * K * V if rc is not None else 0))
     kernels["fwd"]["stream_gbs"] = fwd_bytes / (avg_ms["fwd"] * 1e-3) / 1e9
     dom = max(("fwd", "bwd"), key=lambda n: avg_ms[n])
     dom_tf = kernels[dom]["achieved_tflops"]
@@ -392,17 +417,23 @@ def main():
         "config": {"workload": wl.name, "B": B, "T": T, "n_heads": N, "qk_heads": NQ, "K": K, "V": V,
                    "C": C, "kvq_dtype": "bf16" if wl.bf16 else "f32", "state_dtype": "f32",
                    "gate": "exp_softplus" if wl.gate == 1 else "sigmoid",
+                   "backward_states": "recomputed" if rc is None else "stored rc",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": f"m2rnn_{dom} (whole call)", "achieved": dom_tf,
                      "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": dom_tf / MFMA_F32_PEAK_TFLOPS,
-                     "traffic": measured_bwd_traffic(wl.name, C) if dom == "bwd" else None},
+                     "traffic": (measured_bwd_traffic(wl.name, C, rc is not None)
+                                 if dom == "bwd" else None)},
         "fwd_only": {"checkpoint_interval": C,
                      "tokens_heads_per_s": kernels["fwd"]["tokens_heads_per_s"],
                      "ms": avg_ms["fwd"], "mfma_frac": kernels["fwd"]["frac"],
                      "achieved_tflops": kernels["fwd"]["achieved_tflops"]},
         "kernels": kernels,
     }
+    if rc is not None:
+        ms = recompute_bwd_ms()
+        out["bwd_recompute"] = {"ms": ms, "mfma_frac": flops["bwd"] / (ms * 1e-3) / 1e12
+                                / MFMA_F32_PEAK_TFLOPS}
     if not args.no_per_config:
         out["per_config"] = per_config_fractions()
         out["decode"] = decode_rates()

@@ -115,12 +115,18 @@ size_t m2rnn_workspace_bytes(int is_bwd, int64_t B, int64_t T, int64_t n_heads,
  *          from (the review's section 2.6 reruns the recurrence at the start of
  *          the backward; storing every C-th state bounds that rerun to C steps).
  *   C      checkpoint interval, >= 1 when ckpt != NULL
+ *   rc     [B, n_heads, T, K, V]  out, or NULL: rc_t = 1 / (1 + e^{2 A_t}) of every step
+ *          (A_t the pre-activation, tanh(A_t) = 1 - 2 rc_t).  Given to m2rnn_bwd, it
+ *          replaces the backward's recomputation of the states inside each
+ *          checkpoint interval (the states follow from rc by the interpolation
+ *          alone, bit for bit); it costs K V 4-8 bytes per token and head.
  *   workspace / workspace_bytes: at least m2rnn_workspace_bytes(0, ...)
  */
 int m2rnn_fwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K, int64_t V,
               int in_dtype, int state_dtype, const void* k, const void* v, const void* q,
               const void* f, const void* W, const void* w_r, const void* H0, void* y, void* HT,
-              void* ckpt, int64_t C, void* workspace, size_t workspace_bytes, void* stream);
+              void* ckpt, int64_t C, void* rc, void* workspace, size_t workspace_bytes,
+              void* stream);
 
 /*
  * m2rnn_bwd -- reverse-time backward of m2rnn_fwd for a loss L with
@@ -139,6 +145,8 @@ int m2rnn_fwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K
  *   k, v, q, f, W, w_r, H0     as for m2rnn_fwd (H0 NULL = zero)
  *   gate_kind, logit, alpha, beta   as for m2rnn_gates (alpha/beta NULL for sigmoid)
  *   ckpt   [B, n_heads, ceil(T / C), K, V]  in, from m2rnn_fwd with the same C, H0, inputs
+ *   rc     [B, n_heads, T, K, V]  in, from the same m2rnn_fwd call, or NULL to recompute
+ *          the states (same results either way)
  *   dy     [B, T, n_heads, V]   in
  *   dHT    [B, n_heads, K, V]   in, or NULL for zero
  *   dk, dq [B, T, qk_heads, K]  out, state_dtype (a shared head's sum over its group)
@@ -154,9 +162,9 @@ int m2rnn_bwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K
               int in_dtype, int state_dtype, const void* k, const void* v, const void* q,
               int gate_kind, const void* logit, const void* alpha, const void* beta,
               const void* f, const void* W, const void* w_r, const void* H0, const void* ckpt,
-              int64_t C, const void* dy, const void* dHT, void* dk, void* dv, void* dq,
-              void* dlogit, void* dW, void* dw_r, void* dalpha, void* dbeta, void* dH0,
-              void* workspace, size_t workspace_bytes, void* stream);
+              int64_t C, const void* rc, const void* dy, const void* dHT, void* dk, void* dv,
+              void* dq, void* dlogit, void* dW, void* dw_r, void* dalpha, void* dbeta,
+              void* dH0, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * m2rnn_step -- one token of every sequence (decoding): the state is updated in

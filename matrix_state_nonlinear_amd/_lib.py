@@ -32,10 +32,10 @@ SIGNATURES = {
     "m2rnn_workspace_bytes": (_sz, [_int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _int]),
     "m2rnn_fwd": (_int, [_i64, _i64, _i64, _i64, _i64, _i64, _int, _int,
                          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                         _i64, _vp, _sz, _vp]),
+                         _i64, _vp, _vp, _sz, _vp]),
     "m2rnn_bwd": (_int, [_i64, _i64, _i64, _i64, _i64, _i64, _int, _int,
                          _vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                         _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                         _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                          _vp, _sz, _vp]),
     "m2rnn_step": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int,
                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),

@@ -142,7 +142,8 @@ int m2rnn_gates(int64_t B, int64_t T, int64_t n_heads, int gate_kind, int dtype,
 int m2rnn_fwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K, int64_t V,
               int in_dtype, int state_dtype, const void* k, const void* v, const void* q,
               const void* f, const void* W, const void* w_r, const void* H0, void* y, void* HT,
-              void* ckpt, int64_t C, void* workspace, size_t workspace_bytes, void* stream) {
+              void* ckpt, int64_t C, void* rc, void* workspace, size_t workspace_bytes,
+              void* stream) {
   if (!sizes_ok(B, T, n_heads, K, V) || !qk_heads_ok(n_heads, qk_heads))
     return M2RNN_ERR_INVALID_ARG;
   if (!in_dtype_known(in_dtype) || !state_dtype_known(state_dtype)) return M2RNN_ERR_INVALID_ARG;
@@ -157,7 +158,7 @@ int m2rnn_fwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K
   if (need && (!workspace || workspace_bytes < need)) return M2RNN_ERR_WORKSPACE;
   FwdArgs a{};
   a.k = k; a.v = v; a.q = q; a.f = f; a.W = W; a.w_r = w_r; a.H0 = H0;
-  a.y = y; a.ypart = workspace; a.HT = HT; a.ckpt = ckpt;
+  a.y = y; a.ypart = workspace; a.HT = HT; a.ckpt = ckpt; a.rc = rc;
   a.B = B; a.T = T; a.N = n_heads; a.K = K; a.V = V; a.C = ckpt ? C : 1;
   a.NQ = qk_heads;
   a.nslab = (int)num_slabs(K);
@@ -168,7 +169,8 @@ int m2rnn_bwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K
               int in_dtype, int state_dtype, const void* k, const void* v, const void* q,
               int gate_kind, const void* logit, const void* alpha, const void* beta,
               const void* f, const void* W, const void* w_r, const void* H0, const void* ckpt,
-              int64_t C, const void* dy, const void* dHT, void* dk, void* dv, void* dq,
+              int64_t C, const void* rc, const void* dy, const void* dHT, void* dk, void* dv,
+              void* dq,
               void* dlogit, void* dW, void* dw_r, void* dalpha, void* dbeta, void* dH0,
               void* workspace, size_t workspace_bytes, void* stream) {
   if (!sizes_ok(B, T, n_heads, K, V) || !qk_heads_ok(n_heads, qk_heads))
@@ -206,7 +208,7 @@ int m2rnn_bwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K
   if (need && (!workspace || workspace_bytes < need)) return M2RNN_ERR_WORKSPACE;
   BwdArgs a{};
   a.k = k; a.v = v; a.q = q; a.logit = logit; a.alpha = alpha; a.beta = beta; a.f = f;
-  a.W = W; a.w_r = w_r; a.H0 = H0; a.ckpt = ckpt; a.dy = dy; a.dHT = dHT;
+  a.W = W; a.w_r = w_r; a.H0 = H0; a.ckpt = ckpt; a.rc = rc; a.dy = dy; a.dHT = dHT;
   a.dk = dk; a.dv = dv; a.dq = dq; a.dlogit = dlogit; a.dW = dW; a.dw_r = dw_r;
   a.dalpha = dalpha; a.dbeta = dbeta; a.dH0 = dH0; a.ws = workspace;
   a.B = B; a.T = T; a.N = n_heads; a.K = K; a.V = V; a.C = C;

@@ -165,7 +165,7 @@ BwdWorkspace bwd_workspace_layout(int64_t B, int64_t T, int64_t N, int64_t NQ, i
 }
 
 
-template <typename InT, typename Real, int VT>
+template <typename InT, typename Real, int VT, bool RC>
 __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
     m2rnn_bwd_kernel(BwdArgs a, BwdWorkspace L) {
   using Tr = BwdTraits<Real, VT>;
@@ -214,6 +214,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
     // W^T as the A operand, rotated so this wave's own tiles come first and
     // scaled by 2 / ln 2, exactly as in the forward kernel
     Real wop[TPW][NS];
+    if constexpr (!RC) {
 #pragma unroll
     for (int p = 0; p < TPW; ++p) {
       const int col = (wr * TPW + p) * 16 + li;
@@ -242,6 +243,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
 #pragma unroll
       for (int s0 = 0; s0 < NS; s0 += 4) pin_values(wop[p][s0], wop[p][s0 + 1], wop[p][s0 + 2], wop[p][s0 + 3]);
     }
+    }
     R4 h[TPW];
     Real hb[NS];
 #pragma unroll
@@ -264,6 +266,34 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
     Real* const dv_tok = nslab == 1 ? (Real*)a.dv + tok0 * V
                                     : (Real*)a.ws + L.dv_part + ((int64_t)slab * B * T * N + tok0) * V;
     const int64_t NK = N * K, NV = N * V;
+    // Stored rc (RC): this lane's values (row `row`, its tiles' columns) of the
+    // step one phase ahead; steps past T read step T - 1 (f = 1 there, so rc
+    // does not matter)
+    R4 rcn[TPW];
+    const Real* rc_lane = nullptr;
+    const int64_t KV = K * V;
+    const bool rc_vec = sizeof(Real) == 4 && (V & 3) == 0;
+    auto load_rc = [&](int t) {
+      const int tt = t < T32 ? t : T32 - 1;
+      const Real* src = rc_lane + (int64_t)tt * KV;
+#pragma unroll
+      for (int p = 0; p < TPW; ++p) {
+        if (rc_vec) {
+          const int c0 = col_of(p, 0);
+          rcn[p] = *(const R4*)(src + (c0 < V ? c0 : 0));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int col = col_of(p, r);
+            rcn[p][r] = src[col < V ? col : 0];
+          }
+        }
+      }
+    };
+    if constexpr (RC) {
+      rc_lane = (const Real*)a.rc + ((int64_t)bn * T * K + (row_ok ? row : 0)) * V;
+      if (nch > 0) load_rc((nch - 1) * S);
+    }
 
     __syncthreads();  // prologue staging by the side role
 
@@ -272,7 +302,44 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
       constexpr int I = decltype(Ic)::value;
       const int j = k * S + I;
       const int jp = j & 1;
-      if (rec) {
+      if (RC && rec) {
+        // the step t = cF S + I from state S_t, with the forward's stored rc:
+        // S_{t+1} = (f S_t + (1 - f)) - 2 (1 - f) rc, as in the forward kernel
+        const Real* stp = &sm.st[slot][I * E];
+        R4 rcc[TPW];
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) {
+          rcc[p] = rcn[p];
+          pin_vec(rcc[p]);
+        }
+        if (I + 1 < S || cF >= 1) load_rc(I + 1 < S ? cF * S + I + 1 : (cF - 1) * S);
+        if constexpr (I == 0) {
+          const int cb = (int)(cF & 1);
+#pragma unroll
+          for (int p = 0; p < TPW; ++p) h[p] = sm.ck[cb][wr * TPW + p][lane];
+        }
+        const Real f = stp[OFF_F];
+        const Real omf = Real(1) - f;
+        const Real m2omf = Real(-2) * omf;
+        Real dqp = 0;
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) {
+          R4 rc;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            // padding rows and columns keep S = 0: rc = 1/2 there, as recomputed
+            rc[r] = (row_ok && col_of(p, r) < V) ? rcc[p][r] : Real(0.5);
+            h[p][r] = fma_r(m2omf, rc[r], fma_r(f, h[p][r], omf));
+          }
+          sm.hr[(hbase + I + 1) & (M - 1)][wr * TPW + p][lane] = h[p];
+          sm.zr[hbase + I][wr * TPW + p][lane] = rc;
+          const R4 u = cols4(stp + OFF_U + (wr * TPW + p) * 16, g);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dqp = fma_r(h[p][r], u[r], dqp);
+        }
+        dqp = cross_row_sum(dqp);
+        if (g == 0) sm.rq[jp][li][wr] = dqp;
+      } else if (rec) {
         // the step t = cF S + I from state S_t
         const Real* stp = &sm.st[slot][I * E];
         if constexpr (I == 0) {
@@ -1168,8 +1235,12 @@ static hipError_t launch_bwd_vt(const BwdArgs& a0, hipStream_t stream) {
     a.cks_count = nck;
     a.cks_step = Tr::S / a.C;
   }
-  hipLaunchKernelGGL((m2rnn_bwd_kernel<InT, Real, VT>), dim3((unsigned)units), dim3(Tr::NT), 0,
-                     stream, a, L);
+  if (a.rc)  // the forward's rc replaces the recomputation inside each chunk
+    hipLaunchKernelGGL((m2rnn_bwd_kernel<InT, Real, VT, true>), dim3((unsigned)units),
+                       dim3(Tr::NT), 0, stream, a, L);
+  else
+    hipLaunchKernelGGL((m2rnn_bwd_kernel<InT, Real, VT, false>), dim3((unsigned)units),
+                       dim3(Tr::NT), 0, stream, a, L);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   const int64_t tokens = a.B * a.T * a.N;

@@ -78,7 +78,7 @@ struct FwdSmem {
   Real q[RING][16];           // q_i of a step
 };
 
-template <typename InT, typename Real, int VT>
+template <typename InT, typename Real, int VT, bool RCS>
 __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT * FwdTraits<Real, VT>::PACK))
     m2rnn_fwd_kernel(FwdArgs a) {
   using Tr = FwdTraits<Real, VT>;
@@ -171,21 +171,23 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT * FwdTraits<Real, VT>
   const int64_t nck = a.ckpt ? (T + a.C - 1) / a.C : 0;
   // where a lane's four columns are consecutive (fp32), one 16-byte store
   const bool st_vec = sizeof(Real) == 4 && (V & 3) == 0;
-  auto write_state = [&](Real* dst) {
+  // this lane's values of a [K, V] array (row `row`, its tiles' columns)
+  auto write_rows = [&](Real* dst, const R4 (&val)[TPW]) {
     if (!row_ok) return;
 #pragma unroll
     for (int p = 0; p < TPW; ++p) {
       if (st_vec) {
-        if (col_of(p, 0) < V) *(R4*)(dst + col_of(p, 0)) = hown[p];
+        if (col_of(p, 0) < V) *(R4*)(dst + col_of(p, 0)) = val[p];
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int col = col_of(p, r);
-          if (col < V) dst[col] = hown[p][r];
+          if (col < V) dst[col] = val[p][r];
         }
       }
     }
   };
+  auto write_state = [&](Real* dst) { write_rows(dst, hown); };
   // checkpoints H_{cC}, c = 0 .. nck - 1, are written in order: ckp is the
   // next one's slot, and ck_left counts the steps until it is due
   Real* ckp = a.ckpt ? (Real*)a.ckpt + (((int64_t)b * N + n) * nck * K + row) * V : nullptr;
@@ -196,6 +198,8 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT * FwdTraits<Real, VT>
     write_state(ckp);
     ckp += KV;
   }
+  // rc_t = 1 / (1 + e^{2 A_t}) of every step, [B, N, T, K, V] (RCS only)
+  Real* rcp = RCS ? (Real*)a.rc + (((int64_t)b * N + n) * T * K + row) * V : nullptr;
   // after step t (t + 1 steps done): write H_{t+1} when it is due and not H_T
   auto ck_step = [&](int t) {
     if (C32 == 0) return;
@@ -431,14 +435,19 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT * FwdTraits<Real, VT>
     // H = f H + (1 - f) tanh(A), with tanh(A) = 1 - 2 / (1 + e^{2A}):
     // H = (f H + (1 - f)) - 2 (1 - f) / (1 + e^{2A}).  f = 1 gives H exactly.
     const Real m2omf = Real(-2) * cur.fg[1];
+    R4 rcv[TPW];
 #pragma unroll
     for (int p = 0; p < TPW; ++p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const Real rc = tanh_rc_scaled(acc[p][r]);
-        hown[p][r] = fma_r(m2omf, rc, fma_r(cur.fg[0], hown[p][r], cur.fg[1]));
+        rcv[p][r] = tanh_rc_scaled(acc[p][r]);
+        hown[p][r] = fma_r(m2omf, rcv[p][r], fma_r(cur.fg[0], hown[p][r], cur.fg[1]));
       }
       if constexpr (Tr::NW > 1) sm.xb[P][w * TPW + p][lane] = hown[p];
+    }
+    if constexpr (RCS) {  // the step's rc for the backward (no recompute there)
+      write_rows(rcp, rcv);
+      rcp += KV;
     }
     // keep the exchange write ahead of the readout, so its latency overlaps it
     __builtin_amdgcn_sched_barrier(0);
@@ -537,8 +546,12 @@ static hipError_t launch_fwd_vt(const FwdArgs& a, hipStream_t stream) {
                 "LDS budget");
   const int64_t units = a.B * a.N * a.nslab;
   const int64_t wgs = (units + Tr::PACK - 1) / Tr::PACK;
-  hipLaunchKernelGGL((m2rnn_fwd_kernel<InT, Real, VT>), dim3((unsigned)wgs),
-                     dim3(Tr::NT * Tr::PACK), 0, stream, a);
+  if (a.rc)  // also store every step's rc
+    hipLaunchKernelGGL((m2rnn_fwd_kernel<InT, Real, VT, true>), dim3((unsigned)wgs),
+                       dim3(Tr::NT * Tr::PACK), 0, stream, a);
+  else
+    hipLaunchKernelGGL((m2rnn_fwd_kernel<InT, Real, VT, false>), dim3((unsigned)wgs),
+                       dim3(Tr::NT * Tr::PACK), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.nslab == 1) return err;
   const int64_t total = a.B * a.T * a.N * a.V;

@@ -43,6 +43,7 @@ struct FwdArgs {
   void* ypart;       // [nslab, B, T, N, V] partial readouts when nslab > 1
   void* HT;          // may be null
   void* ckpt;        // may be null
+  void* rc;          // [B, N, T, K, V] per-step 1 / (1 + e^{2A}), or null
   int64_t B, T, N, K, V, C;
   int64_t NQ;        // heads of q and k; value head n reads q/k head n / (N / NQ)
   int nslab;
@@ -60,6 +61,7 @@ struct BwdArgs {
   const void* w_r;
   const void* H0;    // may be null
   const void* ckpt;
+  const void* rc;    // [B, N, T, K, V] from the forward, or null (recompute)
   const void* dy;
   const void* dHT;   // may be null
   void* dk;

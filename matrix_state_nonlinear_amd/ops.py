@@ -100,7 +100,7 @@ def m2rnn_gates(logit: torch.Tensor, gate_kind: int, alpha=None, beta=None, out=
 
 
 def m2rnn_fwd(k, v, q, f, W, w_r, H0=None, C: int = 0, want_ht: bool = True,
-              out=None, workspace=None):
+              out=None, workspace=None, rc_out=None):
     """Forward recurrence.  Returns (y, HT or None, ckpt or None).
 
     k, q [B, T, NQ, K] and v [B, T, N, V] in float32 / bfloat16 (float32 state)
@@ -108,7 +108,8 @@ def m2rnn_fwd(k, v, q, f, W, w_r, H0=None, C: int = 0, want_ht: bool = True,
     reads q/k head n // (N // NQ); f [B, T, N], W [N, V, V], w_r [N, V],
     H0 [B, N, K, V] in the state dtype (taken from f).  C > 0 also writes the
     checkpoints ckpt[B, N, ceil(T / C), K, V] with ckpt[:, :, c] = H_{cC}.
-    ``out`` may hold preallocated (y, HT, ckpt).
+    ``out`` may hold preallocated (y, HT, ckpt).  ``rc_out`` [B, N, T, K, V] (state
+    dtype), when given, receives every step's rc = 1 / (1 + e^{2A}) for m2rnn_bwd.
     """
     N, NQ = _heads(k, v)
     B, T, _, K = k.shape
@@ -128,22 +129,24 @@ def m2rnn_fwd(k, v, q, f, W, w_r, H0=None, C: int = 0, want_ht: bool = True,
         HT = torch.empty((B, N, K, V), dtype=sd, device=dev) if want_ht else None
         ckpt = (torch.empty((B, N, math.ceil(T / C), K, V), dtype=sd, device=dev)
                 if C and C > 0 else None)
+    _opt(rc_out, (B, N, T, K, V), sd, "rc_out")
     ws, wsb = _workspace(m2rnn_workspace_bytes(False, B, T, N, NQ, K, V, max(C, 1), sd), dev,
                          workspace)
     st = _lib.lib().m2rnn_fwd(B, T, N, NQ, K, V, _DT[k.dtype], _DT[sd], _ptr(k), _ptr(v), _ptr(q),
                               _ptr(f), _ptr(W), _ptr(w_r), _ptr(H0), _ptr(y), _ptr(HT),
-                              _ptr(ckpt), int(C) if ckpt is not None else 0, _ptr(ws), wsb,
-                              _stream(dev))
+                              _ptr(ckpt), int(C) if ckpt is not None else 0, _ptr(rc_out),
+                              _ptr(ws), wsb, _stream(dev))
     check(st, "m2rnn_fwd")
     return y, HT, ckpt
 
 
 def m2rnn_bwd(k, v, q, gate_kind: int, logit, alpha, beta, f, W, w_r, H0, ckpt, C: int, dy,
-              dHT=None, want_dh0: bool = True, workspace=None):
+              dHT=None, want_dh0: bool = True, workspace=None, rc=None):
     """Backward of m2rnn_fwd.  Returns a dict with dk, dv, dq, dlogit, dW, dw_r,
     dalpha and dbeta (exp-softplus gate only, else None) and dH0 (or None).
     dk and dq have the shape of k and q: with shared heads (NQ < N) each is
-    the sum over the value heads that read it."""
+    the sum over the value heads that read it.  ``rc`` (from m2rnn_fwd's rc_out)
+    replaces the recomputation of the states; the results are the same."""
     N, NQ = _heads(k, v)
     B, T, _, K = k.shape
     V = v.shape[-1]
@@ -158,6 +161,7 @@ def m2rnn_bwd(k, v, q, gate_kind: int, logit, alpha, beta, f, W, w_r, H0, ckpt, 
     _need(ckpt, (B, N, math.ceil(T / C), K, V), sd, "ckpt")
     _need(dy, (B, T, N, V), sd, "dy")
     _opt(dHT, (B, N, K, V), sd, "dHT")
+    _opt(rc, (B, N, T, K, V), sd, "rc")
     dev = k.device
     e = lambda *s: torch.empty(s, dtype=sd, device=dev)  # noqa: E731
     out = {"dk": e(B, T, NQ, K), "dv": e(B, T, N, V), "dq": e(B, T, NQ, K),
@@ -169,7 +173,7 @@ def m2rnn_bwd(k, v, q, gate_kind: int, logit, alpha, beta, f, W, w_r, H0, ckpt, 
     st = _lib.lib().m2rnn_bwd(
         B, T, N, NQ, K, V, _DT[k.dtype], _DT[sd], _ptr(k), _ptr(v), _ptr(q), int(gate_kind),
         _ptr(logit), _ptr(alpha), _ptr(beta), _ptr(f), _ptr(W), _ptr(w_r), _ptr(H0), _ptr(ckpt),
-        int(C), _ptr(dy), _ptr(dHT), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dq"]),
+        int(C), _ptr(rc), _ptr(dy), _ptr(dHT), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dq"]),
         _ptr(out["dlogit"]), _ptr(out["dW"]), _ptr(out["dw_r"]), _ptr(out["dalpha"]),
         _ptr(out["dbeta"]), _ptr(out["dH0"]), _ptr(ws), wsb, _stream(dev))
     check(st, "m2rnn_bwd")

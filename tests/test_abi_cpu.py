@@ -67,13 +67,13 @@ def test_workspace_sizes(L):
 def fwd(L, **kw):
     a = dict(B=2, T=8, N=1, NQ=None, K=16, V=16, ind=_lib.M2RNN_F32, sd=_lib.M2RNN_F32, k=FAKE,
              v=FAKE, q=FAKE, f=FAKE, W=FAKE, w_r=FAKE, H0=None, y=FAKE, HT=None, ckpt=None, C=0,
-             ws=None, wsb=0, stream=None)
+             rc=None, ws=None, wsb=0, stream=None)
     a.update(kw)
     if a["NQ"] is None:
         a["NQ"] = a["N"]
     return L.m2rnn_fwd(a["B"], a["T"], a["N"], a["NQ"], a["K"], a["V"], a["ind"], a["sd"], a["k"], a["v"],
                        a["q"], a["f"], a["W"], a["w_r"], a["H0"], a["y"], a["HT"], a["ckpt"],
-                       a["C"], a["ws"], a["wsb"], a["stream"])
+                       a["C"], a["rc"], a["ws"], a["wsb"], a["stream"])
 
 
 def test_qk_heads_must_divide_n_heads(L):
@@ -149,14 +149,15 @@ def test_gates_rejects_bad_arguments(L):
 def bwd(L, **kw):
     a = dict(B=2, T=8, N=1, NQ=None, K=16, V=16, ind=_lib.M2RNN_F32, sd=_lib.M2RNN_F32, k=FAKE, v=FAKE,
              q=FAKE, gate=_lib.M2RNN_GATE_SIGMOID, logit=FAKE, alpha=None, beta=None, f=FAKE,
-             W=FAKE, w_r=FAKE, H0=None, ckpt=FAKE, C=4, dy=FAKE, dHT=None, dk=FAKE, dv=FAKE,
+             W=FAKE, w_r=FAKE, H0=None, ckpt=FAKE, C=4, rc=None, dy=FAKE, dHT=None, dk=FAKE,
+             dv=FAKE,
              dq=FAKE, dlogit=FAKE, dW=FAKE, dw_r=FAKE, dalpha=None, dbeta=None, dH0=None,
              ws=None, wsb=0, stream=None)
     a.update(kw)
     if a["NQ"] is None:
         a["NQ"] = a["N"]
     keys = ["B", "T", "N", "NQ", "K", "V", "ind", "sd", "k", "v", "q", "gate", "logit", "alpha", "beta",
-            "f", "W", "w_r", "H0", "ckpt", "C", "dy", "dHT", "dk", "dv", "dq", "dlogit", "dW",
+            "f", "W", "w_r", "H0", "ckpt", "C", "rc", "dy", "dHT", "dk", "dv", "dq", "dlogit", "dW",
             "dw_r", "dalpha", "dbeta", "dH0", "ws", "wsb", "stream"]
     return L.m2rnn_bwd(*[a[k] for k in keys])
 

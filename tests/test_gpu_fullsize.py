@@ -227,3 +227,26 @@ def test_backward_fp32_invariants_full_horizon(name):
         assert bool(torch.isfinite(v_).all()), k_
         assert torch.equal(v_, g2[k_]), k_
     print(f"{name} fp32 backward: finite and bitwise reproducible")
+
+
+@pytest.mark.parametrize("name,Cs", [("long_t16k_k64", 4), ("fwd_bwd_k32_v128", C)])
+def test_backward_stored_rc_is_the_recompute_full_size(name, Cs):
+    """At full size and in the benchmark's configurations (C dividing the
+    backward's chunk length, and C = 64 with the chunk-start pre-pass): the
+    backward reading the forward's per-step rc returns exactly what the
+    recomputing backward returns, every gradient bit for bit."""
+    wl = WORKLOADS[name]
+    inp = make_inputs(wl, with_dy=True)
+    d = to_device(inp, "float32")
+    f = m2rnn_gates(d["logit"], wl.gate, d["alpha"], d["beta"])
+    rc = torch.empty((wl.B, wl.N, wl.T, wl.K, wl.V), dtype=torch.float32, device=f.device)
+    y, HT, ck = m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"], None, Cs, rc_out=rc)
+    args = (d["k"], d["v"], d["q"], wl.gate, d["logit"], d["alpha"], d["beta"], f, d["W"],
+            d["w_r"], None, ck, Cs, d["dy"])
+    g0 = m2rnn_bwd(*args)
+    g1 = m2rnn_bwd(*args, rc=rc)
+    torch.cuda.synchronize()
+    for k_ in g0:
+        if g0[k_] is not None:
+            assert torch.equal(g0[k_], g1[k_]), k_
+    print(f"{name} C={Cs}: stored-rc backward bitwise equal to the recompute")

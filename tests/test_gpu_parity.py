@@ -270,3 +270,38 @@ def test_empty_batch_sequence_or_heads(B, T, N, sd):
         assert tuple(g[name].shape) == r.shape, name
         if r.size and name != "dH0":
             assert not np.any(r) and not torch.any(g[name]), name
+
+
+# ---------------------------------------------------------------- stored rc
+
+@pytest.mark.parametrize("sd", ["float32", "float64"])
+@pytest.mark.parametrize("K,V,C,NQ", [(64, 64, 4, 0), (17, 40, 7, 0), (33, 100, 5, 1),
+                                      (16, 16, 4, 0), (48, 128, 2, 0), (64, 16, 8, 1)])
+def test_stored_rc_forward_and_backward(K, V, C, NQ, sd):
+    """The forward's optional rc output (rc_t = 1 / (1 + e^{2 A_t}) of every step)
+    leaves y, H_T and the checkpoints bit for bit unchanged, matches the
+    oracle's (1 - Z_t) / 2, and the backward given it returns exactly the
+    results of the backward that recomputes the states (the states follow from
+    rc by the interpolation alone, with the forward's arithmetic)."""
+    wl = WORKLOADS["fwd_bwd_k32_v128"].replace(B=2, T=45, N=4 if NQ else 2, K=K, V=V, NQ=NQ,
+                                               kq_scale=1 / math.sqrt(K),
+                                               v_scale=1 / math.sqrt(V), w_scale=1 / math.sqrt(V))
+    inp = make_inputs(wl, with_dy=True, with_h0=True, with_dht=True)
+    d = to_device(inp, sd)
+    f = m2rnn_gates(d["logit"], wl.gate, d["alpha"], d["beta"])
+    y0, HT0, ck0 = m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"], d["H0"], C)
+    rc = torch.empty((wl.B, wl.N, wl.T, K, V), dtype=f.dtype, device=f.device)
+    y1, HT1, ck1 = m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"], d["H0"], C, rc_out=rc)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(HT0, HT1) and torch.equal(ck0, ck1)
+    fo, o = oracle_forward(inp, keep=True)
+    rc_ref = np.transpose((1.0 - o["Z"]) / 2.0, (1, 2, 0, 3, 4))
+    assert maxerr(np_(rc), rc_ref) <= TOL_Y[sd]
+    args = (d["k"], d["v"], d["q"], wl.gate, d["logit"], d["alpha"], d["beta"], f, d["W"],
+            d["w_r"], d["H0"], ck0, C, d["dy"], d["dHT"])
+    g0 = m2rnn_bwd(*args)
+    g1 = m2rnn_bwd(*args, rc=rc)
+    torch.cuda.synchronize()
+    for name in g0:
+        if g0[name] is not None:
+            assert torch.equal(g0[name], g1[name]), name
