@@ -94,7 +94,8 @@ def measured_bwd_traffic(workload, C, stored_rc):
 def per_config_fractions(reps=3):
     """Achieved fraction of the fp32 MFMA peak of every workload: the forward
     call alone (no checkpoints) and, for the workloads that define a
-    checkpoint interval, the backward call from checkpoints at that interval.
+    checkpoint interval, the backward call from checkpoints at that interval,
+    recomputing the states and reading the forward's stored rc.
     Flops are the algorithmic ones (forward 2 K V^2, backward 4 K V^2 per token
     and head)."""
     import torch
@@ -126,12 +127,21 @@ def per_config_fractions(reps=3):
                "qk_heads": wl.qk_heads, "K": wl.K, "V": wl.V,
                "fwd_ms": ms, "fwd_tflops": tf, "fwd_mfma_frac": tf / MFMA_F32_PEAK_TFLOPS}
         if wl.C > 0:
-            _, _, ck = m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"], None, wl.C)
-            ms = timed(lambda: m2rnn_bwd(d["k"], d["v"], d["q"], wl.gate, d["logit"], d["alpha"],
-                                         d["beta"], f, d["W"], d["w_r"], None, ck, wl.C, d["dy"]))
-            tf = 4.0 * th * wl.K * wl.V * wl.V / (ms * 1e-3) / 1e12
+            rc = torch.empty((wl.B, wl.N, wl.T, wl.K, wl.V), dtype=torch.float32, device="cuda")
+            _, _, ck = m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"], None, wl.C,
+                                 rc_out=rc)
+            bw = lambda r: m2rnn_bwd(d["k"], d["v"], d["q"], wl.gate, d["logit"],  # noqa: E731
+                                     d["alpha"], d["beta"], f, d["W"], d["w_r"], None, ck, wl.C,
+                                     d["dy"], rc=r)
+            ms = timed(lambda: bw(None))
+            ms_rc = timed(lambda: bw(rc))
+            fl = 4.0 * th * wl.K * wl.V * wl.V
+            tf = fl / (ms * 1e-3) / 1e12
             row.update({"C": wl.C, "bwd_ms": ms, "bwd_tflops": tf,
-                        "bwd_mfma_frac": tf / MFMA_F32_PEAK_TFLOPS})
+                        "bwd_mfma_frac": tf / MFMA_F32_PEAK_TFLOPS, "bwd_stored_rc_ms": ms_rc,
+                        "bwd_stored_rc_mfma_frac": fl / (ms_rc * 1e-3) / 1e12
+                        / MFMA_F32_PEAK_TFLOPS})
+            del rc, ck
         rows.append(row)
         del d, f, inp
         torch.cuda.empty_cache()
