@@ -865,6 +865,87 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
   }
 }
 
+// The same chunk-start states from the forward's stored rc: the
+// interpolation S_{t+1} = (f S_t + (1 - f)) - 2 (1 - f) rc_t acts on every
+// state element alone, so each thread carries four elements of one (b, n)
+// through one checkpoint interval with no exchange and no matrix product
+// (bit for bit the forward's arithmetic).  Workgroup id = (unit, interval,
+// block of 1024 elements); elements are K V per unit.
+template <typename Real>
+__global__ void __launch_bounds__(256)
+    m2rnn_bwd_starts_rc_kernel(BwdArgs a, int S, int64_t nch, int64_t id0,
+                               Real* __restrict__ out) {
+  const int64_t T = a.T, N = a.N, KV = a.K * a.V, C = a.C;
+  const int64_t eblocks = (KV + 1023) / 1024;
+  const int64_t nck = (T + C - 1) / C;
+  const int64_t id = id0 + blockIdx.x;
+  const int64_t eb = id % eblocks;
+  const int64_t c = (id / eblocks) % nck;  // checkpoint interval
+  const int64_t bn = id / eblocks / nck;   // (b, n) unit
+  const int64_t e0 = (eb * 256 + threadIdx.x) * 4;
+  if (e0 >= KV) return;
+  const int64_t t0 = c * C;
+  const int64_t xmax = (nch - 1) * S;  // last chunk start
+  if (t0 > xmax) return;
+  const int64_t tend = (t0 + C < T ? t0 + C : T) < xmax ? (t0 + C < T ? t0 + C : T) : xmax;
+  const int ne = KV - e0 < 4 ? (int)(KV - e0) : 4;  // elements of this thread
+  const Real* ck = (const Real*)a.ckpt + (bn * nck + c) * KV + e0;
+  const Real* rcp = (const Real*)a.rc + (bn * T + t0) * KV + e0;
+  const Real* fp = (const Real*)a.f + (bn / N) * T * N + (bn % N);  // f of (b, t = 0, n)
+  Real h[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) h[i] = i < ne ? ck[i] : Real(0);
+  auto write_start = [&](int64_t x) {
+    Real* dst = out + (bn * nch + x / S) * KV + e0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < ne) dst[i] = h[i];
+  };
+  if (t0 % S == 0) write_start(t0);
+  if (sizeof(Real) == 4 && ne == 4 && (KV & 3) == 0) {
+    // four consecutive fp32 elements: one 16-byte load per step, eight steps'
+    // loads issued ahead of their use
+    using R4 = typename Vec4<Real>::type;
+    int64_t t = t0;
+    for (; t + 8 <= tend; t += 8) {
+      R4 rv[8];
+      Real fv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        rv[u] = *(const R4*)(rcp + (t - t0 + u) * KV);
+        fv[u] = fp[(t + u) * N];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const Real omf = Real(1) - fv[u];
+        const Real m2omf = Real(-2) * omf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = fma_r(m2omf, rv[u][i], fma_r(fv[u], h[i], omf));
+        if ((t + u + 1) % S == 0) write_start(t + u + 1);
+      }
+    }
+    for (; t < tend; ++t) {
+      const R4 rv = *(const R4*)(rcp + (t - t0) * KV);
+      const Real f = fp[t * N];
+      const Real omf = Real(1) - f;
+      const Real m2omf = Real(-2) * omf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[i] = fma_r(m2omf, rv[i], fma_r(f, h[i], omf));
+      if ((t + 1) % S == 0) write_start(t + 1);
+    }
+    return;
+  }
+  for (int64_t t = t0; t < tend; ++t, rcp += KV) {
+    const Real f = fp[t * N];
+    const Real omf = Real(1) - f;
+    const Real m2omf = Real(-2) * omf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < ne) h[i] = fma_r(m2omf, rcp[i], fma_r(f, h[i], omf));
+    if ((t + 1) % S == 0) write_start(t + 1);
+  }
+}
+
 // Chunk-start states at every multiple of S, recomputed from the forward's
 // checkpoints when C does not divide S.  One workgroup per (slab, checkpoint
 // interval): the intervals are independent, so they all run at once and the
@@ -1221,11 +1302,22 @@ static hipError_t launch_bwd_vt(const BwdArgs& a0, hipStream_t stream) {
   if (L.subck_needed) {
     // one workgroup per (slab, checkpoint interval), in launches of at most 2^24 workgroups
     const int64_t total = units * nck;
-    for (int64_t id0 = 0; id0 < total; id0 += (int64_t)1 << 24) {
-      const int64_t cnt = total - id0 < ((int64_t)1 << 24) ? total - id0 : ((int64_t)1 << 24);
-      hipLaunchKernelGGL((m2rnn_bwd_starts_kernel<InT, Real, VT>), dim3((unsigned)cnt),
-                         dim3(Tr::NW * 64), 0, stream, a, L.nch, id0, ws + L.subck);
-      if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (a.rc) {
+      // from the stored rc: elementwise, one workgroup per (unit, interval, 1024 elements)
+      const int64_t tot = a.B * a.N * nck * ((a.K * a.V + 1023) / 1024);
+      for (int64_t id0 = 0; id0 < tot; id0 += (int64_t)1 << 24) {
+        const int64_t cnt = tot - id0 < ((int64_t)1 << 24) ? tot - id0 : ((int64_t)1 << 24);
+        hipLaunchKernelGGL((m2rnn_bwd_starts_rc_kernel<Real>), dim3((unsigned)cnt), dim3(256), 0,
+                           stream, a, Tr::S, L.nch, id0, ws + L.subck);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+      }
+    } else {
+      for (int64_t id0 = 0; id0 < total; id0 += (int64_t)1 << 24) {
+        const int64_t cnt = total - id0 < ((int64_t)1 << 24) ? total - id0 : ((int64_t)1 << 24);
+        hipLaunchKernelGGL((m2rnn_bwd_starts_kernel<InT, Real, VT>), dim3((unsigned)cnt),
+                           dim3(Tr::NW * 64), 0, stream, a, L.nch, id0, ws + L.subck);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+      }
     }
     a.cks = ws + L.subck;
     a.cks_count = L.nch;
