@@ -446,7 +446,16 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT * FwdTraits<Real, VT>
       if constexpr (Tr::NW > 1) sm.xb[P][w * TPW + p][lane] = hown[p];
     }
     if constexpr (RCS) {  // the step's rc for the backward (no recompute there)
-      write_rows(rcp, rcv);
+      // non-temporal: rc is read back only by the backward, long after
+      if (st_vec) {
+        if (row_ok) {
+#pragma unroll
+          for (int p = 0; p < TPW; ++p)
+            if (col_of(p, 0) < V) __builtin_nontemporal_store(rcv[p], (R4*)(rcp + col_of(p, 0)));
+        }
+      } else {
+        write_rows(rcp, rcv);
+      }
       rcp += KV;
     }
     // keep the exchange write ahead of the readout, so its latency overlaps it
