@@ -176,6 +176,41 @@ __device__ __forceinline__ f64x4 row16_sum_x4(f64x4 h, double q) {
   return y;
 }
 
+// The first two levels of row16_sum_x4 (row_ror by 8, then 4): lane i of each
+// 16-lane row ends with the sums of h[r] * q over rows i, i + 4, i + 8, i + 12
+// (lanes 0..3 hold the four distinct partials; adding them in lane order
+// finishes the row sum).
+__device__ __forceinline__ f32x4 row16_partial4_x4(f32x4 h, float q) {
+  float y0, y1, y2, y3;
+  asm volatile(
+      "v_mul_f32 %0, %4, %8\n"
+      "v_mul_f32 %1, %5, %8\n"
+      "v_mul_f32 %2, %6, %8\n"
+      "v_mul_f32 %3, %7, %8\n"
+      "v_add_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %1, %1, %1 row_ror:8 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %2, %2, %2 row_ror:8 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %3, %3, %3 row_ror:8 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %1, %1, %1 row_ror:4 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %2, %2, %2 row_ror:4 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %3, %3, %3 row_ror:4 row_mask:0xf bank_mask:0xf\n"
+      : "=&v"(y0), "=&v"(y1), "=&v"(y2), "=&v"(y3)
+      : "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "v"(q));
+  return f32x4{y0, y1, y2, y3};
+}
+__device__ __forceinline__ f64x4 row16_partial4_x4(f64x4 h, double q) {
+  f64x4 y;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    double x = h[r] * q;
+    x += dpp_move<kDppRowRor8>(x);
+    x += dpp_move<kDppRowRor4>(x);
+    y[r] = x;
+  }
+  return y;
+}
+
 // Sum over the four 16-lane rows (lanes l, l^16, l^32, l^48); every lane gets
 // the same value.  fp32: the gfx950 lane-swap instructions (v_permlane32_swap
 // exchanges the two halves of the wave between two registers, v_permlane16_swap

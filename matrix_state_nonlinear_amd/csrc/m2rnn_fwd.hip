@@ -70,7 +70,9 @@ struct FwdSmem {
   using R4 = typename Vec4<Real>::type;
   using R2 = typename Vec2<Real>::type;
   R4 xb[2][VT][64];           // state exchange, double-buffered by step parity
-  R4 y[RING][VT][4];          // readouts (this slab's rows), lane order [tile][g][r]
+  // readout partials [slot][tile][g][i]: sums over this slab's rows i, i + 4,
+  // i + 8, i + 12 of the lane group's four columns; the write-back adds the four
+  R4 y[RING][VT][4][4];
   R4 ydump[NW * 64];          // sink for readout stores of lanes that hold no result
   Real v[RING][16 * VT];      // v_j of a step
   Real k[RING][16];           // k_i of a step (this slab's rows)
@@ -362,7 +364,8 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT * FwdTraits<Real, VT>
     for (int k = 0; k < NY_PER; ++k) {
       if (y_ok[k] && t0 + y_tt[k] < T32) {
         const int slot = base + y_tt[k];
-        const Real val = sm.y[slot][y_c[k]][y_g[k]][y_r[k]];
+        const R4* yq = sm.y[slot][y_c[k]][y_g[k]];
+        const Real val = ((yq[0][y_r[k]] + yq[1][y_r[k]]) + yq[2][y_r[k]]) + yq[3][y_r[k]];
         if (nslab == 1) {
           const Real vv = sm.v[slot][y_c[k] * 16 + acc_m<Real>(y_g[k], y_r[k])];
           yout[y_ofs[k] + cofs] = val + y_wr[k] * vv;
@@ -464,14 +467,14 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT * FwdTraits<Real, VT>
     // (the reduction is volatile asm for fp32, so it also stays before the barrier)
     R4 ys[TPW];
 #pragma unroll
-    for (int p = 0; p < TPW; ++p) ys[p] = row16_sum_x4(hown[p], cur.q);
+    for (int p = 0; p < TPW; ++p) ys[p] = row16_partial4_x4(hown[p], cur.q);
     unit_sync();
     // the readout store goes after the barrier (its latency then overlaps the
     // own-tile MFMAs of the next step); the barrier ending the chunk's last
     // step is followed by one more before the write-back reads it
 #pragma unroll
     for (int p = 0; p < TPW; ++p) {
-      R4* dst = li == 0 ? &sm.y[slot][w * TPW + p][g] : ydump_me;
+      R4* dst = li < 4 ? &sm.y[slot][w * TPW + p][g][li] : ydump_me;
       *dst = ys[p];
     }
 #pragma unroll
