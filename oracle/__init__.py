@@ -32,3 +32,4 @@ from .m2rnn_block import (  # noqa: F401
     gate_rmsnorm,
     gate_rmsnorm_backward,
 )
+from .m2rnn_newton import newton_forward, newton_linearize  # noqa: F401
