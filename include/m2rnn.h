@@ -186,6 +186,46 @@ int m2rnn_step(int64_t B, int64_t n_heads, int64_t qk_heads, int64_t K, int64_t 
                const void* W, const void* w_r, void* H, void* y, void* stream);
 
 /*
+ * Parallel-in-time forward by Newton's method (pararnn-torch "ParaM2RNN" page,
+ * "Jacobian class" and "Parallel path": factorized Newton on the matrix
+ * residual; "ParaGRU" page, "Parallel path": Newton + scan from the guess
+ * X_t = F(0, x_t)).  The states X_1 .. X_T of m2rnn_fwd's recurrence are the
+ * unknowns; iteration i linearises F(X) = f X + (1 - f) tanh(X W + k v^T) at the
+ * current iterate and solves the resulting linear recurrence over time exactly
+ * (a two-level scan over chunks, each state row with its own V x V step
+ * matrix f I + (1 - f) W diag(1 - Z^2)).  After `iters` iterations the states
+ * are read out as in m2rnn_fwd.  The first i states are exact after i
+ * iterations (T iterations give the sequential result); the method converges
+ * quadratically when every step map is contractive (e.g. |W| < 1) and may
+ * diverge otherwise -- `residual` reports max_t |X_t - F(X_{t-1})| of every
+ * iterate so that the caller can check.  Its cost per iteration is about
+ * V times the sequential forward's flops, spread over all T steps: it pays
+ * when B * n_heads * ceil(K / 16) slabs leave most of the device idle.
+ *
+ * fp32 state only: in_dtype F32 or BF16 (k, v, q); f, W, w_r, H0 and every
+ * output fp32.  V must be 16, 32, 48 or 64 (else M2RNN_ERR_UNSUPPORTED); K <= 256;
+ * 0 <= iters <= 64.  H0, y, HT, states and the workspace must be 16-byte aligned.
+ *   k, q, v, f, W, w_r, H0     as for m2rnn_fwd (H0 may be NULL = zeros)
+ *   y        [B, T, n_heads, V]      out, the readout of the final iterate
+ *   HT       [B, n_heads, K, V]      out or NULL, its last state
+ *   states   [B, n_heads, T, K, V]   out or NULL, every state of the final
+ *                                    iterate (X_t at index t - 1); when NULL the
+ *                                    iterate lives in the workspace
+ *   residual [iters + 1]             out or NULL, float: entry i is the largest
+ *                                    |X_t - F(X_{t-1})| of iterate i (0 = the guess)
+ *   workspace / workspace_bytes: at least m2rnn_newton_workspace_bytes(...)
+ * Launches only on `stream`, no allocation.  B * T * n_heads = 0: H_T = H_0
+ * (zero when NULL) and residual = 0; nothing else is written.
+ */
+size_t m2rnn_newton_workspace_bytes(int64_t B, int64_t T, int64_t n_heads, int64_t K, int64_t V,
+                                    int states_given);
+int m2rnn_newton_fwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K,
+                     int64_t V, int in_dtype, const void* k, const void* v, const void* q,
+                     const void* f, const void* W, const void* w_r, const void* H0, int iters,
+                     void* y, void* HT, void* states, void* residual, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
  * The block around the recurrence (review section 2.3, Eq. 14-23): q, k, v each
  * pass a linear projection, a depthwise causal Conv1D of kernel size 4 and SiLU
  * (the prologue below); the output gate g = SiLU(W_g x) multiplies the readout,

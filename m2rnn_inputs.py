@@ -104,6 +104,16 @@ DECODE_WORKLOADS = {
         name="decode_multi_value", B=512, T=1, C=0, seed=8),
 }
 
+# The parallel-in-time Newton forward's workload: few units (one sequence of
+# four value heads with the paper's K = 64, V = 16 and shared q/k), so that the
+# sequential forward leaves most of the device idle, and a contractive
+# transition W = 0.9 Q (Q orthogonal), under which every step map contracts and
+# Newton converges in about three iterations.
+NEWTON_WORKLOADS = {
+    "newton_k64_v16": WORKLOADS["multi_value_k64_v16"].replace(
+        name="newton_k64_v16", B=1, N=4, C=0, w_kind="orth", w_eps=0.0, w_scale=0.0, seed=9),
+}
+
 WORKLOAD_ORDER = ["tiny_fp32", "fp32_k64", "long_t16k_k64", "big_state_k128",
                   "fwd_bwd_k32_v128"]
 

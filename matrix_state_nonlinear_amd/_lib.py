@@ -39,6 +39,9 @@ SIGNATURES = {
                          _vp, _sz, _vp]),
     "m2rnn_step": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int,
                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "m2rnn_newton_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _int]),
+    "m2rnn_newton_fwd": (_int, [_i64, _i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp,
+                                _vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "m2rnn_block_workspace_bytes": (_sz, [_int, _i64, _i64, _i64, _int]),
     "m2rnn_conv_silu": (_int, [_i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp]),
     "m2rnn_conv_silu_bwd": (_int, [_i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp,

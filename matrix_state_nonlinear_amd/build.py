@@ -14,7 +14,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libm2rnn.so")
 SOURCES = ["m2rnn_api.hip", "m2rnn_gates.hip", "m2rnn_fwd.hip", "m2rnn_bwd.hip",
-           "m2rnn_step.hip", "m2rnn_block.hip"]
+           "m2rnn_step.hip", "m2rnn_block.hip",
+           "m2rnn_newton.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are switched off for every kernel.  MFMA

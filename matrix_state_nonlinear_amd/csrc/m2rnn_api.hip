@@ -95,6 +95,21 @@ hipError_t fill(void* dst, const void* src, int64_t n, int state_dtype, hipStrea
   return hipGetLastError();
 }
 
+// The Newton forward's shapes: V a multiple of 16 up to 64, and wave counts of
+// its kernels within 32-bit wave indices.
+bool newton_supported(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V) {
+  if (!(V == 16 || V == 32 || V == 48 || V == 64) || K > 256 || T >= ((int64_t)1 << 30))
+    return false;
+  if (B * T * N == 0) return true;
+  const NewtonLayout L = newton_layout(B, T, N, K, V, true);
+  const double U = (double)B * (double)N;
+  const double waves = U * (double)num_slabs(K) * (double)L.NTB;
+  const double map_waves = U * (double)L.P * (double)K * (double)(V / 16);
+  return waves < 2.0e9 && map_waves < 2.0e9 && U * (double)T * (double)K * (double)V < 4.0e18;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 }  // namespace
 
 extern "C" {
@@ -216,6 +231,55 @@ int m2rnn_bwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K
   a.nslab = (int)num_slabs(K);
   a.gate_kind = gate_kind;
   return status_of(launch_bwd(a, in_dtype, state_dtype, (hipStream_t)stream));
+}
+
+size_t m2rnn_newton_workspace_bytes(int64_t B, int64_t T, int64_t n_heads, int64_t K, int64_t V,
+                                    int states_given) {
+  if (!sizes_ok(B, T, n_heads, K, V) || !newton_supported(B, T, n_heads, K, V)) return 0;
+  if (B * T * n_heads == 0) return 0;
+  return align_up(newton_layout(B, T, n_heads, K, V, states_given != 0).total_floats * 4, 256);
+}
+
+int m2rnn_newton_fwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K,
+                     int64_t V, int in_dtype, const void* k, const void* v, const void* q,
+                     const void* f, const void* W, const void* w_r, const void* H0, int iters,
+                     void* y, void* HT, void* states, void* residual, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (!sizes_ok(B, T, n_heads, K, V) || !qk_heads_ok(n_heads, qk_heads))
+    return M2RNN_ERR_INVALID_ARG;
+  if (in_dtype != M2RNN_F32 && in_dtype != M2RNN_BF16) {
+    return in_dtype_known(in_dtype) ? M2RNN_ERR_UNSUPPORTED : M2RNN_ERR_INVALID_ARG;
+  }
+  if (iters < 0 || iters > 64) return M2RNN_ERR_INVALID_ARG;
+  const bool empty = B * T * n_heads == 0;
+  if (!empty && (!k || !v || !q || !f || !W || !w_r || !y)) return M2RNN_ERR_INVALID_ARG;
+  if (!aligned16(H0) || !aligned16(y) || !aligned16(HT) || !aligned16(states) ||
+      !aligned16(workspace))
+    return M2RNN_ERR_INVALID_ARG;
+  if (!newton_supported(B, T, n_heads, K, V)) return M2RNN_ERR_UNSUPPORTED;
+  const hipStream_t st = (hipStream_t)stream;
+  if (empty) {
+    hipError_t e = fill(HT, H0, B * n_heads * K * V, M2RNN_F32, st);
+    if (e == hipSuccess) e = fill(residual, nullptr, iters + 1, M2RNN_F32, st);
+    return status_of(e);
+  }
+  const NewtonLayout L = newton_layout(B, T, n_heads, K, V, states != nullptr);
+  const size_t need = align_up(L.total_floats * 4, 256);
+  if (!workspace || workspace_bytes < need) return M2RNN_ERR_WORKSPACE;
+  float* ws = (float*)workspace;
+  NewtonArgs a{};
+  a.k = k; a.v = v; a.q = q;
+  a.f = (const float*)f; a.W = (const float*)W; a.w_r = (const float*)w_r;
+  a.H0 = (const float*)H0;
+  a.y = (float*)y; a.HT = (float*)HT;
+  a.X = states ? (float*)states : ws + L.X;
+  a.S = ws + L.S; a.R = ws + L.R;
+  a.M = ws + L.M; a.E = ws + L.E; a.D = ws + L.D;
+  a.res = (unsigned*)residual;
+  a.B = B; a.T = T; a.N = n_heads; a.NQ = qk_heads; a.K = K; a.V = V;
+  a.iters = iters;
+  a.L = L.L; a.P = L.P; a.TL = L.TL; a.NTB = L.NTB;
+  return status_of(launch_newton(a, in_dtype, st));
 }
 
 int m2rnn_step(int64_t B, int64_t n_heads, int64_t qk_heads, int64_t K, int64_t V, int in_dtype,

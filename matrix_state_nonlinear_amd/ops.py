@@ -180,6 +180,52 @@ def m2rnn_bwd(k, v, q, gate_kind: int, logit, alpha, beta, f, W, w_r, H0, ckpt, 
     return out
 
 
+def m2rnn_newton_workspace_bytes(B: int, T: int, n_heads: int, K: int, V: int,
+                                 states_given: bool) -> int:
+    return int(_lib.lib().m2rnn_newton_workspace_bytes(B, T, n_heads, K, V,
+                                                       int(bool(states_given))))
+
+
+def m2rnn_newton_fwd(k, v, q, f, W, w_r, H0=None, iters: int = 3, want_ht: bool = True,
+                     want_states: bool = False, want_residual: bool = False, out=None,
+                     workspace=None):
+    """Parallel-in-time forward by Newton's method (fp32 state, V in 16/32/48/64).
+
+    Arguments as for m2rnn_fwd (k, q, v in float32 or bfloat16; f, W, w_r, H0
+    float32).  Returns (y, HT or None, states [B, N, T, K, V] or None,
+    residual [iters + 1] or None); ``out`` may hold preallocated
+    (y, HT, states, residual).
+    """
+    N, NQ = _heads(k, v)
+    B, T, _, K = k.shape
+    V = v.shape[-1]
+    sd = torch.float32
+    _need(v, (B, T, N, V), k.dtype, "v")
+    _need(q, (B, T, NQ, K), k.dtype, "q")
+    _need(f, (B, T, N), sd, "f")
+    _need(W, (N, V, V), sd, "W")
+    _need(w_r, (N, V), sd, "w_r")
+    _opt(H0, (B, N, K, V), sd, "H0")
+    dev = k.device
+    if out is not None:
+        y, HT, states, res = out
+    else:
+        y = torch.empty((B, T, N, V), dtype=sd, device=dev)
+        HT = torch.empty((B, N, K, V), dtype=sd, device=dev) if want_ht else None
+        states = torch.empty((B, N, T, K, V), dtype=sd, device=dev) if want_states else None
+        res = torch.empty((iters + 1,), dtype=sd, device=dev) if want_residual else None
+    _opt(states, (B, N, T, K, V), sd, "states")
+    _opt(res, (iters + 1,), sd, "residual")
+    ws, wsb = _workspace(m2rnn_newton_workspace_bytes(B, T, N, K, V, states is not None), dev,
+                         workspace)
+    st = _lib.lib().m2rnn_newton_fwd(B, T, N, NQ, K, V, _DT[k.dtype], _ptr(k), _ptr(v), _ptr(q),
+                                     _ptr(f), _ptr(W), _ptr(w_r), _ptr(H0), int(iters), _ptr(y),
+                                     _ptr(HT), _ptr(states), _ptr(res), _ptr(ws), wsb,
+                                     _stream(dev))
+    check(st, "m2rnn_newton_fwd")
+    return y, HT, states, res
+
+
 def m2rnn_step(H, k, v, q, f, W, w_r, out=None):
     """One token of every sequence (decoding): H [B, N, K, V] (state dtype) is
     updated in place from H_{t-1} to H_t, and y [B, N, V] is returned.  k, q

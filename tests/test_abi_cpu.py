@@ -243,3 +243,55 @@ def test_block_entry_points_reject_bad_arguments(L):
               None) == E.M2RNN_ERR_INVALID_ARG
     assert rb(4, 8, BF, F32, 1e-6, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4,
               None) == E.M2RNN_ERR_WORKSPACE
+
+
+def newton(L, **kw):
+    a = dict(B=2, T=8, N=1, NQ=None, K=16, V=16, ind=_lib.M2RNN_F32, k=FAKE, v=FAKE, q=FAKE,
+             f=FAKE, W=FAKE, w_r=FAKE, H0=None, iters=3, y=FAKE, HT=None, states=None, res=None,
+             ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    NQ = a["N"] if a["NQ"] is None else a["NQ"]
+    return L.m2rnn_newton_fwd(a["B"], a["T"], a["N"], NQ, a["K"], a["V"], a["ind"], a["k"],
+                              a["v"], a["q"], a["f"], a["W"], a["w_r"], a["H0"], a["iters"],
+                              a["y"], a["HT"], a["states"], a["res"], a["ws"], a["wsb"],
+                              a["stream"])
+
+
+def test_newton_workspace_size(L):
+    ws = L.m2rnn_newton_workspace_bytes
+    # one head, K = V = 16, T = 100: chunks of one step (P = 100), so
+    # X, S, R [100, 16, 16] and E, D [100, 16, 16] and M [100, 16, 16, 16]
+    seq = 100 * 16 * 16
+    assert ws(1, 100, 1, 16, 16, 0) == (3 * seq + 2 * seq + 16 * seq) * 4
+    assert ws(1, 100, 1, 16, 16, 1) == (2 * seq + 2 * seq + 16 * seq) * 4
+    # enough (unit, row) pairs for a full device: one chunk, no maps
+    seq2 = 4 * 32 * 40 * 64 * 16
+    assert ws(4, 40, 32, 64, 16, 1) == 2 * seq2 * 4
+    assert ws(1, 10, 1, 16, 24, 0) == 0   # V not a multiple of 16
+    assert ws(1, 10, 1, 16, 80, 0) == 0   # V above 64
+    assert ws(0, 10, 1, 16, 16, 0) == 0   # empty
+
+
+def test_newton_rejects_bad_arguments(L):
+    E = _lib
+    assert newton(L, B=-1) == E.M2RNN_ERR_INVALID_ARG
+    assert newton(L, K=0) == E.M2RNN_ERR_INVALID_ARG
+    assert newton(L, N=4, NQ=3) == E.M2RNN_ERR_INVALID_ARG
+    assert newton(L, iters=-1) == E.M2RNN_ERR_INVALID_ARG
+    assert newton(L, iters=65) == E.M2RNN_ERR_INVALID_ARG
+    assert newton(L, ind=7) == E.M2RNN_ERR_INVALID_ARG
+    assert newton(L, y=None) == E.M2RNN_ERR_INVALID_ARG
+    assert newton(L, f=None) == E.M2RNN_ERR_INVALID_ARG
+    assert newton(L, H0=FAKE + 4) == E.M2RNN_ERR_INVALID_ARG      # not 16-byte aligned
+    assert newton(L, states=FAKE + 8) == E.M2RNN_ERR_INVALID_ARG
+    assert newton(L, ws=FAKE + 4) == E.M2RNN_ERR_INVALID_ARG
+    assert newton(L, ind=E.M2RNN_F64) == E.M2RNN_ERR_UNSUPPORTED
+    assert newton(L, V=24) == E.M2RNN_ERR_UNSUPPORTED
+    assert newton(L, V=128) == E.M2RNN_ERR_UNSUPPORTED
+    assert newton(L, K=257) == E.M2RNN_ERR_UNSUPPORTED
+    assert newton(L, ws=None, wsb=0) == E.M2RNN_ERR_WORKSPACE
+    assert newton(L, wsb=1000) == E.M2RNN_ERR_WORKSPACE
+    # empty: nothing to read; H_T and the residual are NULL here, so nothing is written
+    none = dict(k=None, v=None, q=None, f=None, W=None, w_r=None, y=None, ws=None, wsb=0)
+    assert newton(L, T=0, **none) == E.M2RNN_OK
+    assert newton(L, B=0, **none) == E.M2RNN_OK
