@@ -13,8 +13,8 @@ oracle's, and each iteration adds the rounding of a linear recurrence whose
 step maps contract, so the states stay within a few 1e-6; the readout sums K
 rows.  Bounds: 1e-5 absolute on states, H_T and y (observed: below 1e-6),
 and 1e-5 + 1e-3 |ref| on each iterate's residual (a converged fp32 residual
-bottoms out near 1e-7, the float64 one near 1e-16).  Shapes cover V = 16, 32, 48, 64; K with a ragged last
-slab; shared and per-head q/k; a given H_0; bf16 and fp32 inputs; chunks of one
+bottoms out near 1e-7, the float64 one near 1e-16).  Shapes cover V = 16,
+32, 48, 64; K with a ragged last slab; shared and per-head q/k; a given H_0; bf16 and fp32 inputs; chunks of one
 step and of many steps; a single chunk (no scan); and the full Newton workload.
 """
 import math
@@ -152,8 +152,6 @@ def test_newton_workload_full_size():
 
 @pytest.mark.parametrize("B,T,N", [(0, 5, 2), (2, 0, 2), (2, 5, 0)])
 def test_newton_empty(B, T, N):
-    wl, inp = orth_case(B=max(B, 1), T=max(T, 1), N=max(N, 1), K=20, V=16, NQ=max(N, 1),
-                        with_h0=True)
     dev = "cuda:0"
     k = torch.zeros((B, T, N, 20), device=dev)
     v = torch.zeros((B, T, N, 16), device=dev)
