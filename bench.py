@@ -44,8 +44,8 @@ def parse():
                     help="target duration of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true",
-                    help="skip the MFMA fraction of every workload and the decode-step and "
-                         "block-kernel rates")
+                    help="skip the MFMA fraction of every workload and the decode-step, "
+                         "block-kernel and Newton rates")
     ap.add_argument("--recompute", action="store_true",
                     help="the backward recomputes the states inside each checkpoint interval "
                          "instead of reading the per-step rc the forward stores")
@@ -54,6 +54,9 @@ def parse():
                          "print those rates")
     ap.add_argument("--block-only", action="store_true",
                     help="only time the block prologue / epilogue kernels and print those rates")
+    ap.add_argument("--newton-only", action="store_true",
+                    help="only time the parallel-in-time Newton forward beside the sequential "
+                         "one on the Newton workload and print those rates")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="first copy this many GiB twice with torch (a plain copy of known "
                          "size, to calibrate HBM byte counters)")
@@ -193,6 +196,65 @@ def decode_rates(reps=50):
     return rows
 
 
+def newton_rates(reps=5, iters=3):
+    """The parallel-in-time Newton forward (m2rnn_newton_fwd, three iterations)
+    beside the sequential forward kernel on the Newton workload (one sequence,
+    four value heads of K = 64, V = 16, shared q/k, contractive W) and on one
+    head of it.  Rates are tokens x heads per second of the whole call; the
+    dominant kernel, the chunk maps, does 2 V^3 flops per (unit, row, step) and
+    iteration on the fp32 MFMA units (V times the sequential forward's 2 K V^2
+    per token and head); its share of the fp32 MFMA peak is given over the whole
+    call."""
+    import torch
+
+    from m2rnn_inputs import NEWTON_WORKLOADS, make_inputs, to_device
+    from matrix_state_nonlinear_amd import (m2rnn_fwd, m2rnn_gates, m2rnn_newton_fwd,
+                                            m2rnn_newton_workspace_bytes)
+
+    base = NEWTON_WORKLOADS["newton_k64_v16"]
+    rows = []
+    for wl in (base, base.replace(name="newton_k64_v16_one_head", N=1)):
+        inp = make_inputs(wl)
+        d = to_device(inp, "float32")
+        f = m2rnn_gates(d["logit"], wl.gate, d["alpha"], d["beta"])
+        ws = torch.empty(m2rnn_newton_workspace_bytes(wl.B, wl.T, wl.N, wl.K, wl.V, False),
+                         dtype=torch.uint8, device="cuda")
+        y = torch.empty((wl.B, wl.T, wl.N, wl.V), device="cuda")
+        stream = torch.cuda.current_stream()
+
+        def timed(fn):
+            fn()
+            stream.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            stream.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        ms_seq = timed(lambda: m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"],
+                                         want_ht=False, out=(y, None, None)))
+        ms_newton = timed(lambda: m2rnn_newton_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"],
+                                                   iters=iters, want_ht=False, workspace=ws,
+                                                   out=(y, None, None, None)))
+        _, _, _, res = m2rnn_newton_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"], iters=iters,
+                                        want_residual=True, workspace=ws)
+        stream.synchronize()
+        th = wl.B * wl.T * wl.N
+        maps_flops = iters * 2.0 * wl.V ** 3 * wl.K * wl.T * wl.B * wl.N
+        rows.append({"workload": wl.name, "B": wl.B, "T": wl.T, "n_heads": wl.N,
+                     "qk_heads": wl.qk_heads, "K": wl.K, "V": wl.V, "iters": iters,
+                     "ms": ms_newton, "tokens_heads_per_s": th / ms_newton * 1e3,
+                     "sequential_ms": ms_seq, "sequential_tokens_heads_per_s": th / ms_seq * 1e3,
+                     "speedup": ms_seq / ms_newton, "residual": [float(r) for r in res.tolist()],
+                     "maps_flops": maps_flops,
+                     "maps_mfma_frac_whole_call": maps_flops / (ms_newton * 1e-3) / 1e12
+                     / MFMA_F32_PEAK_TFLOPS})
+        del d, f, ws, y, inp
+        torch.cuda.empty_cache()
+    return rows
+
 def block_rates(reps=20):
     """The block around the recurrence at the long-context workload's sizes:
     the causal conv + SiLU prologue on one projected tensor [4, 16384, 1024]
@@ -305,10 +367,14 @@ def main():
     from matrix_state_nonlinear_amd import m2rnn_bwd, m2rnn_fwd, m2rnn_gates
     from matrix_state_nonlinear_amd.ops import m2rnn_workspace_bytes
 
-    if args.decode_only or args.block_only:
+    if args.decode_only or args.block_only or args.newton_only:
         torch.cuda.set_device(0)
-        print(json.dumps({"decode": decode_rates()} if args.decode_only
-                         else {"block": block_rates()}), flush=True)
+        if args.decode_only:
+            print(json.dumps({"decode": decode_rates()}), flush=True)
+        elif args.block_only:
+            print(json.dumps({"block": block_rates()}), flush=True)
+        else:
+            print(json.dumps({"newton": newton_rates()}), flush=True)
         return
 
     if args.copy_calibration_gib > 0:
@@ -448,6 +514,7 @@ def main():
         out["per_config"] = per_config_fractions()
         out["decode"] = decode_rates()
         out["block"] = block_rates()
+        out["newton"] = newton_rates()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = oracle_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -253,7 +253,7 @@ int m2rnn_newton_fwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, in
   if (iters < 0 || iters > 64) return M2RNN_ERR_INVALID_ARG;
   const bool empty = B * T * n_heads == 0;
   if (!empty && (!k || !v || !q || !f || !W || !w_r || !y)) return M2RNN_ERR_INVALID_ARG;
-  if (!aligned16(H0) || !aligned16(y) || !aligned16(HT) || !aligned16(states) ||
+  if (!aligned16(v) || !aligned16(H0) || !aligned16(y) || !aligned16(HT) || !aligned16(states) ||
       !aligned16(workspace))
     return M2RNN_ERR_INVALID_ARG;
   if (!newton_supported(B, T, n_heads, K, V)) return M2RNN_ERR_UNSUPPORTED;

@@ -33,7 +33,15 @@
 // tile c, column 16 c + 4 (l / 16) + r.  One wave holds all V / 16 tiles of its
 // slab, so no state leaves registers between steps.
 //
+// Prefetches.  Inputs are loaded one step or group ahead of their use, and
+// every such load is issued unconditionally (addresses clamped to the last
+// valid step): a prefetch under a condition leaves a different number of loads
+// in flight on the two paths, and the wait before the next use then has to
+// drain them all, the prefetch included.
+//
 // Supported: fp32 state, V in {16, 32, 48, 64}, any K <= 256.
+
+#include <type_traits>
 
 #include "m2rnn_device.h"
 #include "m2rnn_internal.h"
@@ -75,10 +83,39 @@ __device__ __forceinline__ void slab_times_w(const float (&wa)[VT][4 * VT], cons
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *(const f32x4*)p; }
 __device__ __forceinline__ void st4(float* p, f32x4 x) { *(f32x4*)p = x; }
 
+// Four consecutive inputs (16-byte aligned for fp32, 8-byte for bf16) as fp32.
+__device__ __forceinline__ f32x4 ld4_in(const float* p) { return ld4(p); }
+__device__ __forceinline__ f32x4 ld4_in(const uint16_t* p) {
+  const uint2 raw = *(const uint2*)p;
+  return f32x4{__builtin_bit_cast(float, raw.x << 16), __builtin_bit_cast(float, raw.x & 0xffff0000u),
+               __builtin_bit_cast(float, raw.y << 16), __builtin_bit_cast(float, raw.y & 0xffff0000u)};
+}
+
+// Gates of steps t .. t + G - 1 (clamped to t_last), step t + m in lane m (and
+// in the lanes congruent to it mod G): the address depends on the lane, so this
+// is a vector load, which completes in order with the other vector loads (a
+// wave-uniform address would become a scalar load, and waiting for one scalar
+// load waits for all of them, prefetched ones included).
+__device__ __forceinline__ float load_gates(const float* fp, int64_t N, int64_t t, int64_t t_last,
+                                            int G) {
+  const int span = G < 2 ? 2 : G;  // at least two distinct steps: the address must vary
+  int64_t tt = t + (int64_t)(((int)threadIdx.x & 63) % span);
+  if (tt > t_last) tt = t_last;
+  return fp[tt * N];
+}
+// The value of x in lane m (m wave-uniform).
+__device__ __forceinline__ float lane_value(float x, int m) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), m));
+}
+
 __device__ __forceinline__ int64_t nslab_of(int64_t K) { return (K + 15) / 16; }
 
+// The wave's index in the grid, in a scalar register: everything derived from
+// it (unit, chunk, slab, loop bounds) is then wave-uniform to the compiler, so
+// the step loops are uniform branches and their addresses scalar arithmetic.
 __device__ __forceinline__ int global_wave() {
-  return (int)blockIdx.x * kWavesPerGroup + ((int)threadIdx.x >> 6);
+  return __builtin_amdgcn_readfirstlane((int)blockIdx.x * kWavesPerGroup +
+                                        ((int)threadIdx.x >> 6));
 }
 
 }  // namespace
@@ -118,6 +155,8 @@ __global__ void __launch_bounds__(256) m2rnn_newton_init_kernel(NewtonArgs a) {
 // S_t = (1 - f_t)(1 - Z_t^2), R_t = X_t - f_t X_{t-1} - (1 - f_t) Z_t, and the
 // largest |R_t| into *res (as the bit pattern of a non-negative float, whose
 // unsigned order is the numeric order).  STORE = false only measures the residual.
+// X_{t-1} is carried from the previous step; the next step's inputs are loaded
+// while the current one is computed.
 template <typename InT, int VT, bool STORE>
 __global__ void __launch_bounds__(256) m2rnn_newton_linearize_kernel(NewtonArgs a,
                                                                      unsigned* res) {
@@ -155,20 +194,37 @@ __global__ void __launch_bounds__(256) m2rnn_newton_linearize_kernel(NewtonArgs 
   const InT* kp = (const InT*)a.k + ((b * T) * a.NQ + n / grp) * K + rowc;
   const InT* vp = (const InT*)a.v + ((b * T) * N + n) * V;
   const float* fp = a.f + (b * T) * N + n;
-  float rmax = 0.0f;
-  for (int64_t t = t0; t < t1; ++t) {
+  // inputs of one step, loaded one step ahead of their use
+  struct In {
+    f32x4 x[VT];   // X_t (own columns)
+    f32x4 v[VT];   // v_t (own columns)
+    float k, f;    // k_t of the lane's row; gates of steps t (lane 0) and t + 1
+  };
+  auto load_in = [&](int64_t t, In& in) {
     const int64_t sidx = ((u * T + t) * K + rowc) * V;
-    f32x4 xc[VT];
 #pragma unroll
-    for (int c = 0; c < VT; ++c) xc[c] = ld4(a.X + sidx + ncol(c, g, 0));
-    const float ks = kTanhScale<float> * load_as<float>(kp + t * a.NQ * K);
-    const float ff = fp[t * N];
+    for (int c = 0; c < VT; ++c) {
+      in.x[c] = ld4(a.X + sidx + ncol(c, g, 0));
+      in.v[c] = ld4_in(vp + t * N * V + ncol(c, g, 0));
+    }
+    in.k = load_as<float>(kp + t * a.NQ * K);
+    in.f = load_gates(fp, N, t, t1 - 1, 2);
+  };
+  float rmax = 0.0f;
+  In cur, nxt;
+  load_in(t0, cur);
+  for (int64_t t = t0; t < t1; ++t) {
+    load_in(t + 1 < t1 ? t + 1 : t, nxt);  // unconditional: see the note on prefetches
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t sidx = ((u * T + t) * K + rowc) * V;
+    const float ks = kTanhScale<float> * cur.k;
+    const float ff = lane_value(cur.f, 0);
     const float omf = 1.0f - ff;
     f32x4 acc[VT];
 #pragma unroll
     for (int c = 0; c < VT; ++c)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[c][r] = ks * load_as<float>(vp + t * N * V + ncol(c, g, r));
+      for (int r = 0; r < 4; ++r) acc[c][r] = ks * cur.v[c][r];
     slab_times_w<VT>(wa, xp, acc);
     f32x4 sv[VT], rv[VT];
 #pragma unroll
@@ -179,7 +235,7 @@ __global__ void __launch_bounds__(256) m2rnn_newton_linearize_kernel(NewtonArgs 
         // F = f X + (1 - f)(1 - 2 rc);  1 - Z^2 = 4 rc (1 - rc)
         const float F = fma_r(-2.0f * omf, rc, fma_r(ff, xp[c][r], omf));
         sv[c][r] = 4.0f * omf * rc * (1.0f - rc);
-        rv[c][r] = xc[c][r] - F;
+        rv[c][r] = cur.x[c][r] - F;
         rmax = fmaxf(rmax, fabsf(rv[c][r]));
       }
     if (STORE && row_ok) {
@@ -190,7 +246,8 @@ __global__ void __launch_bounds__(256) m2rnn_newton_linearize_kernel(NewtonArgs 
       }
     }
 #pragma unroll
-    for (int c = 0; c < VT; ++c) xp[c] = xc[c];
+    for (int c = 0; c < VT; ++c) xp[c] = cur.x[c];
+    cur = nxt;
   }
   if (res) {
     if (!row_ok) rmax = 0.0f;
@@ -233,20 +290,21 @@ __global__ void __launch_bounds__(256) m2rnn_newton_maps_kernel(NewtonArgs a) {
   const float* sp = a.S + (u * T * K + i) * V;   // step t: sp + t K V
   const float* fp = a.f + (b * T) * N + n;       // step t: fp + t N
   f32x4 cs[G][VT], ns[G][VT];
-  float cf[G], nf[G];
-  auto load_group = [&](int64_t tg, f32x4 (&s4)[G][VT], float (&f1)[G]) {
+  float cf, nf;  // gates of the group, step m in lane m
+  auto load_group = [&](int64_t tg, f32x4 (&s4)[G][VT], float& f1) {
 #pragma unroll
     for (int m = 0; m < G; ++m) {
       const int64_t t = tg + m < t1 ? tg + m : t1 - 1;  // past the chunk: repeat its last step (unused)
 #pragma unroll
       for (int c = 0; c < VT; ++c) s4[m][c] = ld4(sp + t * K * V + ncol(c, g, 0));
-      f1[m] = fp[t * N];
     }
+    f1 = load_gates(fp, N, tg, t1 - 1, G);
   };
-  auto run_group = [&](int64_t tg, const f32x4 (&s4)[G][VT], const float (&f1)[G]) {
+  auto run_group = [&](auto full, int64_t tg, const f32x4 (&s4)[G][VT], float f1) {
 #pragma unroll
     for (int m = 0; m < G; ++m) {
-      if (tg + m < t1) {
+      if (decltype(full)::value || tg + m < t1) {
+        const float fm = lane_value(f1, m);
         f32x4 acc[VT];
 #pragma unroll
         for (int c = 0; c < VT; ++c) acc[c] = f32x4{0, 0, 0, 0};
@@ -254,18 +312,25 @@ __global__ void __launch_bounds__(256) m2rnn_newton_maps_kernel(NewtonArgs a) {
 #pragma unroll
         for (int c = 0; c < VT; ++c)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) pm[c][r] = fma_r(f1[m], pm[c][r], acc[c][r] * s4[m][c][r]);
+          for (int r = 0; r < 4; ++r) pm[c][r] = fma_r(fm, pm[c][r], acc[c][r] * s4[m][c][r]);
       }
     }
   };
+  const std::true_type full;
+  const std::false_type part;
   load_group(t0, cs, cf);
-  for (int64_t tg = t0; tg < t1; tg += 2 * G) {
-    if (tg + G < t1) load_group(tg + G, ns, nf);
-    run_group(tg, cs, cf);
-    if (tg + G >= t1) break;
-    if (tg + 2 * G < t1) load_group(tg + 2 * G, cs, cf);
-    run_group(tg + G, ns, nf);
+  int64_t tg = t0;
+  for (; tg + 2 * G <= t1; tg += 2 * G) {
+    load_group(tg + G, ns, nf);
+    __builtin_amdgcn_sched_barrier(0);  // the prefetch stays ahead of the group's steps
+    run_group(full, tg, cs, cf);
+    load_group(tg + 2 * G, cs, cf);
+    __builtin_amdgcn_sched_barrier(0);
+    run_group(full, tg + G, ns, nf);
   }
+  load_group(tg + G, ns, nf);  // fewer than 2 G steps left
+  run_group(part, tg, cs, cf);
+  run_group(part, tg + G, ns, nf);
   float* mp = a.M + (((u * P + p) * K + i) * V + brow) * V;
 #pragma unroll
   for (int c = 0; c < VT; ++c) st4(mp + ncol(c, g, 0), pm[c]);
@@ -278,7 +343,7 @@ __global__ void __launch_bounds__(256) m2rnn_newton_maps_kernel(NewtonArgs a) {
 template <int VT, bool APPLY>
 __global__ void __launch_bounds__(256) m2rnn_newton_solve_kernel(NewtonArgs a) {
   constexpr int V = 16 * VT;
-  constexpr int G = VT == 1 ? 4 : VT == 2 ? 2 : 1;  // two groups of inputs fit in registers
+  constexpr int G = VT == 1 ? 6 : VT == 2 ? 2 : 1;  // two groups of inputs fit in registers
   const int gw = global_wave();
   const int64_t U = a.B * a.N, K = a.K, T = a.T, N = a.N, P = a.P;
   const int64_t nslab = nslab_of(K);
@@ -307,7 +372,7 @@ __global__ void __launch_bounds__(256) m2rnn_newton_solve_kernel(NewtonArgs a) {
   struct In {
     f32x4 s[G][VT], r[G][VT];
     f32x4 x[APPLY ? G : 1][VT];  // APPLY: X_t before the update
-    float f[G];
+    float f;                     // gates, step m of the group in lane m
   };
   In cur, nxt;
   auto load_group = [&](int64_t tg, In& in) {
@@ -320,13 +385,14 @@ __global__ void __launch_bounds__(256) m2rnn_newton_solve_kernel(NewtonArgs a) {
         in.r[m][c] = ld4(a.R + base + t * K * V + ncol(c, g, 0));
         if constexpr (APPLY) in.x[m][c] = ld4(a.X + base + t * K * V + ncol(c, g, 0));
       }
-      in.f[m] = fp[t * N];
     }
+    in.f = load_gates(fp, N, tg, t1 - 1, G);
   };
-  auto run_group = [&](int64_t tg, const In& in) {
+  auto run_group = [&](auto full, int64_t tg, const In& in) {
 #pragma unroll
     for (int m = 0; m < G; ++m) {
-      if (tg + m < t1) {
+      if (decltype(full)::value || tg + m < t1) {
+        const float fm = lane_value(in.f, m);
         f32x4 acc[VT];
 #pragma unroll
         for (int c = 0; c < VT; ++c) acc[c] = f32x4{0, 0, 0, 0};
@@ -335,7 +401,7 @@ __global__ void __launch_bounds__(256) m2rnn_newton_solve_kernel(NewtonArgs a) {
         for (int c = 0; c < VT; ++c)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            d[c][r] = fma_r(in.f[m], d[c][r], fma_r(acc[c][r], in.s[m][c][r], -in.r[m][c][r]));
+            d[c][r] = fma_r(fm, d[c][r], fma_r(acc[c][r], in.s[m][c][r], -in.r[m][c][r]));
         if constexpr (APPLY) {
           if (row_ok) {
             float* xp = a.X + base + (tg + m) * K * V;
@@ -346,14 +412,21 @@ __global__ void __launch_bounds__(256) m2rnn_newton_solve_kernel(NewtonArgs a) {
       }
     }
   };
+  const std::true_type full;
+  const std::false_type part;
   load_group(t0, cur);
-  for (int64_t tg = t0; tg < t1; tg += 2 * G) {
-    if (tg + G < t1) load_group(tg + G, nxt);
-    run_group(tg, cur);
-    if (tg + G >= t1) break;
-    if (tg + 2 * G < t1) load_group(tg + 2 * G, cur);
-    run_group(tg + G, nxt);
+  int64_t tg = t0;
+  for (; tg + 2 * G <= t1; tg += 2 * G) {
+    load_group(tg + G, nxt);
+    __builtin_amdgcn_sched_barrier(0);  // the prefetch stays ahead of the group's steps
+    run_group(full, tg, cur);
+    load_group(tg + 2 * G, cur);
+    __builtin_amdgcn_sched_barrier(0);
+    run_group(full, tg + G, nxt);
   }
+  load_group(tg + G, nxt);  // fewer than 2 G steps left
+  run_group(part, tg, cur);
+  run_group(part, tg + G, nxt);
   if (!APPLY && row_ok) {
     float* ep = a.E + ((u * P + p) * K + row) * V;
 #pragma unroll
@@ -382,18 +455,22 @@ __global__ void __launch_bounds__(256) m2rnn_newton_scan_kernel(NewtonArgs a) {
   const int64_t ic = i < K ? i : K - 1;
   const int src0 = rs * V;  // lane holding column 0 of this lane's row
 
-  float m0[V], m1[V];
-  auto load_m = [&](int64_t p, float (&m)[V]) {
+  // column j of M[u][p][i] in m[0 .. V), E[u][p][i][j] in m[V]; a ring of R
+  // chunks is in flight (loads clamped to the last chunk: see the note on prefetches)
+  constexpr int R = VT == 1 ? 4 : 2;
+  float ring[R][V + 1];
+  auto load_m = [&](int64_t p, float (&m)[V + 1]) {
+    if (p > P - 1) p = P - 1;
     const float* mp = a.M + ((u * P + p) * K + ic) * V * V + j;
 #pragma unroll
     for (int l = 0; l < V; ++l) m[l] = mp[l * V];
+    m[V] = a.E[((u * P + p) * K + ic) * V + j];
   };
   float dcur = 0.0f;
-  auto apply = [&](int64_t p, const float (&m)[V]) {
+  auto apply = [&](int64_t p, const float (&m)[V + 1]) {
     const int64_t o = ((u * P + p) * K + ic) * V + j;
     if (ok) a.D[o] = dcur;
-    if (p + 1 == P) return;
-    float s0 = a.E[o], s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+    float s0 = m[V], s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
 #pragma unroll
     for (int l = 0; l < V; l += 4) {
       s0 = fma_r(__shfl(dcur, src0 + l, 64), m[l], s0);
@@ -403,14 +480,20 @@ __global__ void __launch_bounds__(256) m2rnn_newton_scan_kernel(NewtonArgs a) {
     }
     dcur = (s0 + s1) + (s2 + s3);
   };
-  load_m(0, m0);
-  for (int64_t p = 0; p < P; p += 2) {
-    if (p + 1 < P) load_m(p + 1, m1);
-    apply(p, m0);
-    if (p + 1 >= P) break;
-    if (p + 2 < P) load_m(p + 2, m0);
-    apply(p + 1, m1);
+#pragma unroll
+  for (int r = 0; r < R; ++r) load_m(r, ring[r]);
+  int64_t p = 0;
+  for (; p + R <= P; p += R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      apply(p + r, ring[r]);
+      load_m(p + r + R, ring[r]);
+      __builtin_amdgcn_sched_barrier(0);  // the ring's loads stay R chunks ahead
+    }
   }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (p + r < P) apply(p + r, ring[r]);
 }
 
 // ---- readout y_t = X_t^T q_t + w_r (.) v_t, one thread per (unit, step, four
@@ -431,6 +514,7 @@ __global__ void __launch_bounds__(256) m2rnn_newton_readout_kernel(NewtonArgs a)
     const float* xp = a.X + (u * T + t) * K * V + j;
     const bool last = a.HT && t == T - 1;
     f32x4 acc = {0, 0, 0, 0};
+#pragma unroll 8
     for (int64_t i = 0; i < K; ++i) {
       const f32x4 x = ld4(xp + i * V);
       const float qq = load_as<float>(qp + i);
@@ -455,9 +539,20 @@ NewtonLayout newton_layout(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V
   const int64_t U = B * N;
   const int64_t VT = V / 16;
   const int64_t nslab = num_slabs(K);
-  // Chunks: enough map waves for about eight per SIMD (1024 SIMDs).
+  // Chunks.  The two solves walk L = T / P steps and the scan P chunks, one
+  // after the other, so P near sqrt(T) balances them (measured: 2.5 sqrt(T) is
+  // slower, the solves being bound by their occupancy rather than by L); the
+  // maps want at least eight waves per SIMD (1024 SIMDs).  When the (unit, row)
+  // pairs alone fill the device there is nothing to gain from chunks: one
+  // chunk, solved directly.
   const int64_t map_waves = U * K * VT;
-  int64_t P = (8192 + map_waves - 1) / (map_waves > 0 ? map_waves : 1);
+  int64_t P = 1;
+  if (map_waves < 8192) {
+    P = (8192 + map_waves - 1) / (map_waves > 0 ? map_waves : 1);
+    int64_t sq = 1;
+    while (sq * sq < T) ++sq;  // ceil(sqrt(T))
+    if (P < sq) P = sq;
+  }
   if (P > T) P = T;
   if (P < 1) P = 1;
   L.L = (T + P - 1) / P;

@@ -283,6 +283,7 @@ def test_newton_rejects_bad_arguments(L):
     assert newton(L, y=None) == E.M2RNN_ERR_INVALID_ARG
     assert newton(L, f=None) == E.M2RNN_ERR_INVALID_ARG
     assert newton(L, H0=FAKE + 4) == E.M2RNN_ERR_INVALID_ARG      # not 16-byte aligned
+    assert newton(L, v=FAKE + 8) == E.M2RNN_ERR_INVALID_ARG
     assert newton(L, states=FAKE + 8) == E.M2RNN_ERR_INVALID_ARG
     assert newton(L, ws=FAKE + 4) == E.M2RNN_ERR_INVALID_ARG
     assert newton(L, ind=E.M2RNN_F64) == E.M2RNN_ERR_UNSUPPORTED

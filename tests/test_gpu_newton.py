@@ -89,7 +89,7 @@ def test_newton_iterates_match_oracle(V, K, NQ):
 
 @pytest.mark.parametrize("bf16", [True, False])
 def test_newton_long_chunks_with_h0(bf16):
-    # 4 units of 64 rows, V = 16: 32 chunks of 94 steps (the last one shorter)
+    # 4 units of 64 rows, V = 16: 55 chunks of 55 steps (the last one of 30)
     wl, inp = orth_case(B=1, T=3000, N=4, K=64, V=16, NQ=1, bf16=bf16, with_h0=True)
     _, _, out = run(wl, inp, 3)
     check_against_oracle(wl, inp, 3, out, f"T=3000 bf16={bf16}")
