@@ -5,6 +5,7 @@
 
 #include "../../include/m2rnn.h"
 #include "m2rnn_internal.h"
+#include "m2rnn_newton_internal.h"
 
 using namespace m2rnn;
 

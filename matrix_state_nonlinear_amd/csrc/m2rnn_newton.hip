@@ -45,6 +45,7 @@
 
 #include "m2rnn_device.h"
 #include "m2rnn_internal.h"
+#include "m2rnn_newton_internal.h"
 
 namespace m2rnn {
 
