@@ -204,7 +204,7 @@ int m2rnn_step(int64_t B, int64_t n_heads, int64_t qk_heads, int64_t K, int64_t 
  *
  * fp32 state only: in_dtype F32 or BF16 (k, v, q); f, W, w_r, H0 and every
  * output fp32.  V must be 16, 32, 48 or 64 (else M2RNN_ERR_UNSUPPORTED); K <= 256;
- * 0 <= iters <= 64.  H0, y, HT, states and the workspace must be 16-byte aligned.
+ * 0 <= iters <= 64.  v, H0, y, HT, states and the workspace must be 16-byte aligned.
  *   k, q, v, f, W, w_r, H0     as for m2rnn_fwd (H0 may be NULL = zeros)
  *   y        [B, T, n_heads, V]      out, the readout of the final iterate
  *   HT       [B, n_heads, K, V]      out or NULL, its last state
