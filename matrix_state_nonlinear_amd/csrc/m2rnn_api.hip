@@ -274,6 +274,7 @@ int m2rnn_newton_fwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, in
   a.H0 = (const float*)H0;
   a.y = (float*)y; a.HT = (float*)HT;
   a.X = states ? (float*)states : ws + L.X;
+  a.Xn = ws + L.X2;
   a.S = ws + L.S; a.R = ws + L.R;
   a.M = ws + L.M; a.E = ws + L.E; a.D = ws + L.D;
   a.res = (unsigned*)residual;

@@ -339,12 +339,22 @@ __global__ void __launch_bounds__(256) m2rnn_newton_maps_kernel(NewtonArgs a) {
 
 // ---- chunk solve: one wave per (unit, chunk p, 16-row slab):
 //     d <- f_t d + (d W) (.) S_t - R_t
-// from d = D[u][p] (or zero), over the chunk's steps.  APPLY: X_t += d_t for
-// every step (the Newton update); else the chunk's end value goes to E[u][p].
-template <int VT, bool APPLY>
-__global__ void __launch_bounds__(256) m2rnn_newton_solve_kernel(NewtonArgs a) {
+// from d = D[u][p] (or zero), over the chunk's steps.  Without APPLY the
+// chunk's end value goes to E[u][p].  APPLY: the new iterate X_t + d_t is
+// written to Xn for every step (Xn = X updates in place; with LIN they are two
+// buffers, since another wave reads the state before its chunk from X).  LIN
+// (with APPLY) also linearises the new
+// iterate as it is produced, for the next iteration or its residual: with x the
+// new states, Z_t = tanh(x_{t-1} W + k_t v_t^T), S_t = (1 - f_t)(1 - Z_t^2) and
+// R_t = x_t - F(x_{t-1}) overwrite S_t and R_t once step t has used them
+// (later steps' loads read later indices), and max |R_t| goes to *res.  The
+// chunk's first x_{t-1} is H_0 (t = 0) or X_{t0-1} + D[u][p], both known before
+// the previous chunk's wave has written anything.
+template <typename InT, int VT, bool APPLY, bool LIN>
+__global__ void __launch_bounds__(256) m2rnn_newton_solve_kernel(NewtonArgs a, unsigned* res) {
   constexpr int V = 16 * VT;
-  constexpr int G = VT == 1 ? 6 : VT == 2 ? 2 : 1;  // two groups of inputs fit in registers
+  // steps per group: two groups of inputs fit in registers
+  constexpr int G = VT == 1 ? (LIN ? 4 : 6) : VT == 2 ? 2 : 1;
   const int gw = global_wave();
   const int64_t U = a.B * a.N, K = a.K, T = a.T, N = a.N, P = a.P;
   const int64_t nslab = nslab_of(K);
@@ -354,6 +364,7 @@ __global__ void __launch_bounds__(256) m2rnn_newton_solve_kernel(NewtonArgs a) {
   const int64_t p = (gw / nslab) % P;
   const int64_t u = gw / nslab / P;
   const int64_t b = u / N, n = u % N;
+  const int grp = (int)(N / a.NQ);
   const int64_t row = slab * 16 + li;
   const bool row_ok = row < K;
   const int64_t rowc = row_ok ? row : K - 1;
@@ -367,12 +378,29 @@ __global__ void __launch_bounds__(256) m2rnn_newton_solve_kernel(NewtonArgs a) {
 #pragma unroll
   for (int c = 0; c < VT; ++c)
     d[c] = from_d ? ld4(a.D + ((u * P + p) * K + rowc) * V + ncol(c, g, 0)) : f32x4{0, 0, 0, 0};
+  // LIN: the new state before the step being computed
+  f32x4 xprev[LIN ? VT : 1];
+  if constexpr (LIN) {
+    if (t0 == 0) {
+#pragma unroll
+      for (int c = 0; c < VT; ++c)
+        xprev[c] = a.H0 ? ld4(a.H0 + (u * K + rowc) * V + ncol(c, g, 0)) : f32x4{0, 0, 0, 0};
+    } else {
+#pragma unroll
+      for (int c = 0; c < VT; ++c)
+        xprev[c] = ld4(a.X + ((u * T + t0 - 1) * K + rowc) * V + ncol(c, g, 0)) + d[c];
+    }
+  }
+  const InT* kp = (const InT*)a.k + ((b * T) * a.NQ + n / grp) * K + rowc;
+  const InT* vp = (const InT*)a.v + ((b * T) * N + n) * V;
 
   const int64_t base = (u * T * K + rowc) * V;   // step t: base + t K V
   const float* fp = a.f + (b * T) * N + n;
   struct In {
     f32x4 s[G][VT], r[G][VT];
-    f32x4 x[APPLY ? G : 1][VT];  // APPLY: X_t before the update
+    f32x4 x[APPLY ? G : 1][VT];  // APPLY: X_t of the current iterate
+    f32x4 v[LIN ? G : 1][VT];    // LIN: v_t (own columns)
+    float k[LIN ? G : 1];        // LIN: k_t of the lane's row
     float f;                     // gates, step m of the group in lane m
   };
   In cur, nxt;
@@ -385,10 +413,13 @@ __global__ void __launch_bounds__(256) m2rnn_newton_solve_kernel(NewtonArgs a) {
         in.s[m][c] = ld4(a.S + base + t * K * V + ncol(c, g, 0));
         in.r[m][c] = ld4(a.R + base + t * K * V + ncol(c, g, 0));
         if constexpr (APPLY) in.x[m][c] = ld4(a.X + base + t * K * V + ncol(c, g, 0));
+        if constexpr (LIN) in.v[m][c] = ld4_in(vp + t * N * V + ncol(c, g, 0));
       }
+      if constexpr (LIN) in.k[m] = load_as<float>(kp + t * a.NQ * K);
     }
     in.f = load_gates(fp, N, tg, t1 - 1, G);
   };
+  float rmax = 0.0f;
   auto run_group = [&](auto full, int64_t tg, const In& in) {
 #pragma unroll
     for (int m = 0; m < G; ++m) {
@@ -404,10 +435,41 @@ __global__ void __launch_bounds__(256) m2rnn_newton_solve_kernel(NewtonArgs a) {
           for (int r = 0; r < 4; ++r)
             d[c][r] = fma_r(fm, d[c][r], fma_r(acc[c][r], in.s[m][c][r], -in.r[m][c][r]));
         if constexpr (APPLY) {
-          if (row_ok) {
-            float* xp = a.X + base + (tg + m) * K * V;
+          const int64_t o = base + (tg + m) * K * V;
+          f32x4 xn[VT];
 #pragma unroll
-            for (int c = 0; c < VT; ++c) st4(xp + ncol(c, g, 0), in.x[m][c] + d[c]);
+          for (int c = 0; c < VT; ++c) xn[c] = in.x[m][c] + d[c];
+          if (row_ok) {
+#pragma unroll
+            for (int c = 0; c < VT; ++c) st4(a.Xn + o + ncol(c, g, 0), xn[c]);
+          }
+          if constexpr (LIN) {
+            const float omf = 1.0f - fm;
+            f32x4 al[VT];
+#pragma unroll
+            for (int c = 0; c < VT; ++c) al[c] = f32x4{0, 0, 0, 0};
+            slab_times_w<VT>(wa, xprev, al);
+            f32x4 sv[VT], rv[VT];
+#pragma unroll
+            for (int c = 0; c < VT; ++c)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float rc = tanh_rc_scaled(
+                    kTanhScale<float> * fma_r(in.k[m], in.v[m][c][r], al[c][r]));
+                const float F = fma_r(-2.0f * omf, rc, fma_r(fm, xprev[c][r], omf));
+                sv[c][r] = 4.0f * omf * rc * (1.0f - rc);
+                rv[c][r] = xn[c][r] - F;
+                rmax = fmaxf(rmax, fabsf(rv[c][r]));
+              }
+            if (row_ok) {
+#pragma unroll
+              for (int c = 0; c < VT; ++c) {
+                st4(a.S + o + ncol(c, g, 0), sv[c]);
+                st4(a.R + o + ncol(c, g, 0), rv[c]);
+              }
+            }
+#pragma unroll
+            for (int c = 0; c < VT; ++c) xprev[c] = xn[c];
           }
         }
       }
@@ -432,6 +494,12 @@ __global__ void __launch_bounds__(256) m2rnn_newton_solve_kernel(NewtonArgs a) {
     float* ep = a.E + ((u * P + p) * K + row) * V;
 #pragma unroll
     for (int c = 0; c < VT; ++c) st4(ep + ncol(c, g, 0), d[c]);
+  }
+  if (LIN && res) {
+    if (!row_ok) rmax = 0.0f;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o, 64));
+    if (lane == 0) atomicMax(res, __float_as_uint(rmax));
   }
 }
 
@@ -575,6 +643,7 @@ NewtonLayout newton_layout(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V
     return at;
   };
   L.X = states_given ? 0 : take(seq);
+  L.X2 = take(seq);
   L.S = take(seq);
   L.R = take(seq);
   L.M = take(chunk * (size_t)V);
@@ -601,32 +670,63 @@ hipError_t launch_newton_vt(const NewtonArgs& a, hipStream_t st) {
   const int64_t VT64 = VT;
   unsigned* res = a.res;
   if (res) hipLaunchKernelGGL(m2rnn_newton_zero_kernel, dim3(1), dim3(64), 0, st, res, a.iters + 1);
+  const unsigned g_solve = grid_of(U * a.P * nslab);
+  // Linearise inside the applying solve when its waves cover the 1024 SIMDs
+  // (it is then bound by throughput, and the fused pass saves a read of the
+  // iterate); with fewer waves the solve is bound by its per-step latency,
+  // which the fused work lengthens, and a separate pass is faster (measured).
+  const bool fuse = U * a.P * nslab >= 1024;
+  // Fused, iteration i reads iterate i from one state buffer and writes
+  // iterate i + 1 to the other, and the guess goes where the last iterate must
+  // end up after `iters` swaps (a.X: the caller's states or the workspace's
+  // first buffer).  Separate, the update is applied in place.
+  NewtonArgs c = a;
+  if (!fuse) {
+    c.Xn = a.X;
+  } else if (a.iters & 1) {
+    c.X = a.Xn;
+    c.Xn = a.X;
+  }
   hipLaunchKernelGGL(m2rnn_newton_init_kernel<InT>, dim3(grid_elems(U * a.T * K * a.V / 4)),
-                     dim3(256), 0, st, a);
-  const unsigned g_lin = grid_of(U * nslab * a.NTB);
+                     dim3(256), 0, st, c);
+  if (a.iters > 0 || res)  // the guess's linearisation (and residual)
+    hipLaunchKernelGGL((m2rnn_newton_linearize_kernel<InT, VT, true>),
+                       dim3(grid_of(U * nslab * a.NTB)), dim3(256), 0, st, c, res);
   for (int it = 0; it < a.iters; ++it) {
-    hipLaunchKernelGGL((m2rnn_newton_linearize_kernel<InT, VT, true>), dim3(g_lin), dim3(256), 0,
-                       st, a, res ? res + it : nullptr);
-    NewtonArgs b = a;
+    if (!fuse && it > 0)  // the iterate's linearisation (and residual)
+      hipLaunchKernelGGL((m2rnn_newton_linearize_kernel<InT, VT, true>),
+                         dim3(grid_of(U * nslab * a.NTB)), dim3(256), 0, st, c,
+                         res ? res + it : nullptr);
+    NewtonArgs b = c;
     if (a.P > 1) {
       hipLaunchKernelGGL((m2rnn_newton_maps_kernel<VT>), dim3(grid_of(U * a.P * K * VT64)),
-                         dim3(256), 0, st, a);
-      hipLaunchKernelGGL((m2rnn_newton_solve_kernel<VT, false>), dim3(grid_of(U * a.P * nslab)),
-                         dim3(256), 0, st, a);
+                         dim3(256), 0, st, c);
+      hipLaunchKernelGGL((m2rnn_newton_solve_kernel<InT, VT, false, false>), dim3(g_solve),
+                         dim3(256), 0, st, c, nullptr);
       hipLaunchKernelGGL((m2rnn_newton_scan_kernel<VT>),
                          dim3(grid_of(U * ((K + 64 / (16 * VT) - 1) / (64 / (16 * VT))))),
-                         dim3(256), 0, st, a);
+                         dim3(256), 0, st, c);
     } else {
       b.D = nullptr;  // one chunk: the update starts from zero
     }
-    hipLaunchKernelGGL((m2rnn_newton_solve_kernel<VT, true>), dim3(grid_of(U * a.P * nslab)),
-                       dim3(256), 0, st, b);
+    // the new iterate is linearised on the way unless it is the last one and
+    // no residual is asked for
+    if (fuse && (it + 1 < a.iters || res))
+      hipLaunchKernelGGL((m2rnn_newton_solve_kernel<InT, VT, true, true>), dim3(g_solve),
+                         dim3(256), 0, st, b, res ? res + it + 1 : nullptr);
+    else
+      hipLaunchKernelGGL((m2rnn_newton_solve_kernel<InT, VT, true, false>), dim3(g_solve),
+                         dim3(256), 0, st, b, nullptr);
+    float* t = c.X;
+    c.X = c.Xn;
+    c.Xn = t;  // (the same buffer when not fused)
   }
-  if (res)  // the residual of the final iterate
-    hipLaunchKernelGGL((m2rnn_newton_linearize_kernel<InT, VT, false>), dim3(g_lin), dim3(256), 0,
-                       st, a, res + a.iters);
+  if (!fuse && res && a.iters > 0)  // the residual of the last iterate
+    hipLaunchKernelGGL((m2rnn_newton_linearize_kernel<InT, VT, false>),
+                       dim3(grid_of(U * nslab * a.NTB)), dim3(256), 0, st, c, res + a.iters);
+  // c.X now holds the last iterate (a.X)
   hipLaunchKernelGGL(m2rnn_newton_readout_kernel<InT>, dim3(grid_elems(U * a.T * a.V / 4)),
-                     dim3(256), 0, st, a);
+                     dim3(256), 0, st, c);
   return hipGetLastError();
 }
 

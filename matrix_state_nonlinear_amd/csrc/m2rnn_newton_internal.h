@@ -18,6 +18,7 @@ struct NewtonArgs {
   float* y;          // [B, T, N, V]
   float* HT;         // [B, N, K, V] or null
   float* X;          // [B N, T, K, V] iterate: X[u][t] is the state after step t
+  float* Xn;         // [B N, T, K, V] the next iterate (the two buffers alternate)
   float* S;          // [B N, T, K, V] (1 - f_t)(1 - Z_t^2) at the linearisation
   float* R;          // [B N, T, K, V] residual X_t - F(X_{t-1})
   float* M;          // [B N, P, K, V, V] chunk maps (P > 1)
@@ -32,7 +33,7 @@ struct NewtonArgs {
 // Workspace layout (offsets in floats, 64-float aligned) and schedule sizes.
 struct NewtonLayout {
   int64_t L, P, TL, NTB;
-  size_t X, S, R, M, E, D;  // X unused when the caller's states buffer holds the iterate
+  size_t X, X2, S, R, M, E, D;  // X unused when the caller's states buffer holds the iterate
   size_t total_floats;
 };
 NewtonLayout newton_layout(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V,

@@ -259,14 +259,15 @@ def newton(L, **kw):
 
 def test_newton_workspace_size(L):
     ws = L.m2rnn_newton_workspace_bytes
-    # one head, K = V = 16, T = 100: chunks of one step (P = 100), so
-    # X, S, R [100, 16, 16] and E, D [100, 16, 16] and M [100, 16, 16, 16]
+    # one head, K = V = 16, T = 100: chunks of one step (P = 100), so two
+    # iterates X, S, R [100, 16, 16] and E, D [100, 16, 16] and M [100, 16, 16, 16]
     seq = 100 * 16 * 16
-    assert ws(1, 100, 1, 16, 16, 0) == (3 * seq + 2 * seq + 16 * seq) * 4
-    assert ws(1, 100, 1, 16, 16, 1) == (2 * seq + 2 * seq + 16 * seq) * 4
+    assert ws(1, 100, 1, 16, 16, 0) == (4 * seq + 2 * seq + 16 * seq) * 4
+    # the caller's states buffer holds one of the two iterates
+    assert ws(1, 100, 1, 16, 16, 1) == (3 * seq + 2 * seq + 16 * seq) * 4
     # enough (unit, row) pairs for a full device: one chunk, no maps
     seq2 = 4 * 32 * 40 * 64 * 16
-    assert ws(4, 40, 32, 64, 16, 1) == 2 * seq2 * 4
+    assert ws(4, 40, 32, 64, 16, 1) == 3 * seq2 * 4
     assert ws(1, 10, 1, 16, 24, 0) == 0   # V not a multiple of 16
     assert ws(1, 10, 1, 16, 80, 0) == 0   # V above 64
     assert ws(0, 10, 1, 16, 16, 0) == 0   # empty

@@ -15,7 +15,8 @@ rows.  Bounds: 1e-5 absolute on states, H_T and y (observed: below 1e-6),
 and 1e-5 + 1e-3 |ref| on each iterate's residual (a converged fp32 residual
 bottoms out near 1e-7, the float64 one near 1e-16).  Shapes cover V = 16,
 32, 48, 64; K with a ragged last slab; shared and per-head q/k; a given H_0; bf16 and fp32 inputs; chunks of one
-step and of many steps; a single chunk (no scan); and the full Newton workload.
+step and of many steps; a single chunk (no scan); the linearisation fused into
+the applying solve and separate; and the full Newton workload.
 """
 import math
 
@@ -93,6 +94,17 @@ def test_newton_long_chunks_with_h0(bf16):
     wl, inp = orth_case(B=1, T=3000, N=4, K=64, V=16, NQ=1, bf16=bf16, with_h0=True)
     _, _, out = run(wl, inp, 3)
     check_against_oracle(wl, inp, 3, out, f"T=3000 bf16={bf16}")
+
+
+@pytest.mark.parametrize("V", [16, 64])
+def test_newton_fused_linearisation_matches_oracle(V):
+    # 16 units of 64 rows: the applying solve has B N P ceil(K / 16) >= 1024
+    # waves, so it linearises each new iterate itself (the separate pass is
+    # used below that); iterates and residuals against the oracle
+    wl, inp = orth_case(B=4, T=400, N=4, K=64, V=V, NQ=2, with_h0=True)
+    for iters in (1, 3):
+        _, _, out = run(wl, inp, iters)
+        check_against_oracle(wl, inp, iters, out, f"fused V={V}")
 
 
 def test_newton_single_chunk():
