@@ -367,16 +367,6 @@ def main():
     from matrix_state_nonlinear_amd import m2rnn_bwd, m2rnn_fwd, m2rnn_gates
     from matrix_state_nonlinear_amd.ops import m2rnn_workspace_bytes
 
-    if args.decode_only or args.block_only or args.newton_only:
-        torch.cuda.set_device(0)
-        if args.decode_only:
-            print(json.dumps({"decode": decode_rates()}), flush=True)
-        elif args.block_only:
-            print(json.dumps({"block": block_rates()}), flush=True)
-        else:
-            print(json.dumps({"newton": newton_rates()}), flush=True)
-        return
-
     if args.copy_calibration_gib > 0:
         n = int(args.copy_calibration_gib * (1 << 28))
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -386,6 +376,15 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         torch.cuda.empty_cache()
+    if args.decode_only or args.block_only or args.newton_only:
+        torch.cuda.set_device(0)
+        if args.decode_only:
+            print(json.dumps({"decode": decode_rates()}), flush=True)
+        elif args.block_only:
+            print(json.dumps({"block": block_rates()}), flush=True)
+        else:
+            print(json.dumps({"newton": newton_rates()}), flush=True)
+        return
 
     wl = WORKLOADS[args.workload]
     C = args.C
