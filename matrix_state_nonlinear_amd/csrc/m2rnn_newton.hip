@@ -121,33 +121,32 @@ __device__ __forceinline__ int global_wave() {
 
 }  // namespace
 
-// ---- initial guess X_t = F(0, x_t) = (1 - f_t) tanh(k_t v_t^T): one thread
-// per four consecutive columns.
+// ---- initial guess X_t = F(0, x_t) = (1 - f_t) tanh(k_t v_t^T): a workgroup per
+// (unit, step) at a time, a thread per four consecutive columns of the [K, V]
+// state (the indices within the state are 32-bit; the step's are per workgroup).
 template <typename InT>
 __global__ void __launch_bounds__(256) m2rnn_newton_init_kernel(NewtonArgs a) {
-  const int64_t V4 = a.V / 4, K = a.K, T = a.T, N = a.N;
-  const int64_t total = a.B * N * T * K * V4;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t K = a.K, T = a.T, N = a.N, V = a.V;
+  const int V4 = (int)(V / 4), KV4 = (int)K * V4;
+  const int64_t rows = a.B * N * T;
   const int grp = (int)(N / a.NQ);
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
-    const int64_t j = (e % V4) * 4;
-    int64_t rest = e / V4;
-    const int64_t i = rest % K;
-    rest /= K;
-    const int64_t t = rest % T;
-    const int64_t u = rest / T;
+  for (int64_t rw = blockIdx.x; rw < rows; rw += gridDim.x) {
+    const int64_t u = rw / T, t = rw % T;
     const int64_t b = u / N, n = u % N;
     const int64_t tok = b * T + t;
-    const float kk = load_as<float>((const InT*)a.k + (tok * a.NQ + n / grp) * K + i);
-    const float ff = a.f[tok * N + n];
-    const InT* vp = (const InT*)a.v + (tok * N + n) * a.V + j;
-    f32x4 x;
+    const InT* kp = (const InT*)a.k + (tok * a.NQ + n / grp) * K;
+    const InT* vp = (const InT*)a.v + (tok * N + n) * V;
+    const float omf = 1.0f - a.f[tok * N + n];
+    float* xp = a.X + rw * K * V;
+    for (int e = threadIdx.x; e < KV4; e += blockDim.x) {
+      const int i = e / V4, j = (e - i * V4) * 4;
+      const float kk = kTanhScale<float> * load_as<float>(kp + i);
+      const f32x4 vv = ld4_in(vp + j);
+      f32x4 x;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float rc = tanh_rc_scaled(kTanhScale<float> * kk * load_as<float>(vp + r));
-      x[r] = (1.0f - ff) * (1.0f - 2.0f * rc);
+      for (int r = 0; r < 4; ++r) x[r] = omf * (1.0f - 2.0f * tanh_rc_scaled(kk * vv[r]));
+      st4(xp + (int64_t)i * V + j, x);
     }
-    st4(a.X + ((u * T + t) * K + i) * a.V + j, x);
   }
 }
 
@@ -687,8 +686,11 @@ hipError_t launch_newton_vt(const NewtonArgs& a, hipStream_t st) {
     c.X = a.Xn;
     c.Xn = a.X;
   }
-  hipLaunchKernelGGL(m2rnn_newton_init_kernel<InT>, dim3(grid_elems(U * a.T * K * a.V / 4)),
-                     dim3(256), 0, st, c);
+  {
+    int64_t rows = U * a.T;
+    if (rows > 65536) rows = 65536;
+    hipLaunchKernelGGL(m2rnn_newton_init_kernel<InT>, dim3((unsigned)rows), dim3(256), 0, st, c);
+  }
   if (a.iters > 0 || res)  // the guess's linearisation (and residual)
     hipLaunchKernelGGL((m2rnn_newton_linearize_kernel<InT, VT, true>),
                        dim3(grid_of(U * nslab * a.NTB)), dim3(256), 0, st, c, res);

@@ -107,6 +107,23 @@ def test_newton_fused_linearisation_matches_oracle(V):
         check_against_oracle(wl, inp, iters, out, f"fused V={V}")
 
 
+@pytest.mark.parametrize("B,T,N,K,V", [(1, 1, 1, 1, 16), (2, 2, 1, 3, 48), (1, 5, 2, 17, 32)])
+def test_newton_small_edges(B, T, N, K, V):
+    # one step, one state row, sequences shorter than a prefetch group
+    wl, inp = orth_case(B=B, T=T, N=N, K=K, V=V, NQ=1, with_h0=True)
+    for iters in (0, 1, 2):
+        _, _, out = run(wl, inp, iters)
+        check_against_oracle(wl, inp, iters, out, f"B={B} T={T} N={N} K={K} V={V}")
+
+
+def test_newton_single_chunk_fused():
+    # 256 units x 64 rows: a single chunk, and the applying solve's waves cover
+    # the device, so the fused linearisation runs from H_0 with no scan
+    wl, inp = orth_case(B=4, T=20, N=64, K=64, V=16, NQ=1, with_h0=True)
+    _, _, out = run(wl, inp, 2)
+    check_against_oracle(wl, inp, 2, out, "one chunk, fused")
+
+
 def test_newton_single_chunk():
     # 128 units x 64 rows fill the device: one chunk, the update solved directly
     wl, inp = orth_case(B=4, T=40, N=32, K=64, V=16, NQ=1)
