@@ -80,7 +80,11 @@ struct FwdSmem {
   Real q[RING][16];           // q_i of a step
 };
 
-template <typename InT, typename Real, int VT, bool RCS>
+// RCS: also store every step's rc.  FULL (with RCS): every row of the slab and
+// every column of the tiles exists and the state is fp32, so each lane's rc store
+// is one unguarded 16-byte store; the guards (branches on row and column) cost
+// more than the store itself in the step.
+template <typename InT, typename Real, int VT, bool RCS, bool FULL>
 __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT * FwdTraits<Real, VT>::PACK))
     m2rnn_fwd_kernel(FwdArgs a) {
   using Tr = FwdTraits<Real, VT>;
@@ -448,7 +452,11 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT * FwdTraits<Real, VT>
       }
       if constexpr (Tr::NW > 1) sm.xb[P][w * TPW + p][lane] = hown[p];
     }
-    if constexpr (RCS) {  // the step's rc for the backward (no recompute there)
+    if constexpr (RCS && FULL) {  // the step's rc for the backward (no recompute there)
+#pragma unroll
+      for (int p = 0; p < TPW; ++p) *(R4*)(rcp + col_of(p, 0)) = rcv[p];
+      rcp += KV;
+    } else if constexpr (RCS) {
       // non-temporal: rc is read back only by the backward, long after
       if (st_vec) {
         if (row_ok) {
@@ -558,11 +566,18 @@ static hipError_t launch_fwd_vt(const FwdArgs& a, hipStream_t stream) {
                 "LDS budget");
   const int64_t units = a.B * a.N * a.nslab;
   const int64_t wgs = (units + Tr::PACK - 1) / Tr::PACK;
-  if (a.rc)  // also store every step's rc
-    hipLaunchKernelGGL((m2rnn_fwd_kernel<InT, Real, VT, true>), dim3((unsigned)wgs),
+  // every tile full: K rows in whole slabs, V columns in whole tiles, fp32
+  // state, and rc 16-byte aligned
+  const bool full = sizeof(Real) == 4 && a.K % 16 == 0 && a.V == Tr::VP &&
+                    ((uintptr_t)a.rc & 15) == 0;
+  if (a.rc && full)  // also store every step's rc
+    hipLaunchKernelGGL((m2rnn_fwd_kernel<InT, Real, VT, true, true>), dim3((unsigned)wgs),
+                       dim3(Tr::NT * Tr::PACK), 0, stream, a);
+  else if (a.rc)
+    hipLaunchKernelGGL((m2rnn_fwd_kernel<InT, Real, VT, true, false>), dim3((unsigned)wgs),
                        dim3(Tr::NT * Tr::PACK), 0, stream, a);
   else
-    hipLaunchKernelGGL((m2rnn_fwd_kernel<InT, Real, VT, false>), dim3((unsigned)wgs),
+    hipLaunchKernelGGL((m2rnn_fwd_kernel<InT, Real, VT, false, false>), dim3((unsigned)wgs),
                        dim3(Tr::NT * Tr::PACK), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.nslab == 1) return err;
