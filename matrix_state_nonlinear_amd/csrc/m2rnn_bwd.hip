@@ -165,7 +165,11 @@ BwdWorkspace bwd_workspace_layout(int64_t B, int64_t T, int64_t N, int64_t NQ, i
 }
 
 
-template <typename InT, typename Real, int VT, bool RC>
+// RC: rebuild the states from the forward's rc.  FULL: every row of the slab
+// and every column of the tiles exists and the state is fp32 (the launcher
+// checks), so the per-step row and column guards and the scalar fallbacks of the
+// rc loads and dv stores are compiled out.
+template <typename InT, typename Real, int VT, bool RC, bool FULL>
 __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
     m2rnn_bwd_kernel(BwdArgs a, BwdWorkspace L) {
   using Tr = BwdTraits<Real, VT>;
@@ -260,7 +264,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
       }
 #pragma unroll
     for (int p = 0; p < TPW; ++p) pin_values(wrc[p][0], wrc[p][1], wrc[p][2], wrc[p][3]);
-    const bool dv_vec = sizeof(Real) == 4 && (V & 3) == 0;
+    const bool dv_vec = sizeof(Real) == 4 && (FULL || (V & 3) == 0);
     // output pointers at token (b, t = 0, n); step t adds t N rows
     Real* const dq_row = dq_base + tok0 * K + row;
     Real* const dv_tok = nslab == 1 ? (Real*)a.dv + tok0 * V
@@ -272,7 +276,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
     R4 rcn[TPW];
     const Real* rc_lane = nullptr;
     const int64_t KV = K * V;
-    const bool rc_vec = sizeof(Real) == 4 && (V & 3) == 0;
+    const bool rc_vec = sizeof(Real) == 4 && (FULL || (V & 3) == 0);
     auto load_rc = [&](int t) {
       const int tt = t < T32 ? t : T32 - 1;
       const Real* src = rc_lane + (int64_t)tt * KV;
@@ -280,7 +284,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
       for (int p = 0; p < TPW; ++p) {
         if (rc_vec) {
           const int c0 = col_of(p, 0);
-          rcn[p] = *(const R4*)(src + (c0 < V ? c0 : 0));
+          rcn[p] = *(const R4*)(src + (FULL || c0 < V ? c0 : 0));
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -328,7 +332,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             // padding rows and columns keep S = 0: rc = 1/2 there, as recomputed
-            rc[r] = (row_ok && col_of(p, r) < V) ? rcc[p][r] : Real(0.5);
+            rc[r] = (FULL || (row_ok && col_of(p, r) < V)) ? rcc[p][r] : Real(0.5);
             h[p][r] = fma_r(m2omf, rc[r], fma_r(f, h[p][r], omf));
           }
           sm.hr[(hbase + I + 1) & (M - 1)][wr * TPW + p][lane] = h[p];
@@ -435,7 +439,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
               }
               const int col0 = col_of(p, 0);
               if (dv_vec) {
-                if (col0 < V) *(R4*)(dvp + col0) = sv;
+                if (FULL || col0 < V) *(R4*)(dvp + col0) = sv;
               } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
@@ -812,7 +816,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
           s4 = (x[0] + x[1]) + (x[2] + x[3]);
         }
         s4 = cross_row_sum(s4);
-        if (g == 0 && row_ok) dk_row[(int64_t)tp * NK] = s4;
+        if (g == 0 && (FULL || row_ok)) dk_row[(int64_t)tp * NK] = s4;
       }
       if (wr == (1 % NW)) {
         Real s4 = 0;
@@ -1327,11 +1331,18 @@ static hipError_t launch_bwd_vt(const BwdArgs& a0, hipStream_t stream) {
     a.cks_count = nck;
     a.cks_step = Tr::S / a.C;
   }
-  if (a.rc)  // the forward's rc replaces the recomputation inside each chunk
-    hipLaunchKernelGGL((m2rnn_bwd_kernel<InT, Real, VT, true>), dim3((unsigned)units),
+  // every tile full: K rows in whole slabs, V columns in whole tiles, fp32 state,
+  // rc 16-byte aligned
+  const bool full = sizeof(Real) == 4 && a.K % 16 == 0 && a.V == Tr::VP &&
+                    ((uintptr_t)a.rc & 15) == 0;
+  if (a.rc && full)  // the forward's rc replaces the recomputation inside each chunk
+    hipLaunchKernelGGL((m2rnn_bwd_kernel<InT, Real, VT, true, true>), dim3((unsigned)units),
+                       dim3(Tr::NT), 0, stream, a, L);
+  else if (a.rc)
+    hipLaunchKernelGGL((m2rnn_bwd_kernel<InT, Real, VT, true, false>), dim3((unsigned)units),
                        dim3(Tr::NT), 0, stream, a, L);
   else
-    hipLaunchKernelGGL((m2rnn_bwd_kernel<InT, Real, VT, false>), dim3((unsigned)units),
+    hipLaunchKernelGGL((m2rnn_bwd_kernel<InT, Real, VT, false, false>), dim3((unsigned)units),
                        dim3(Tr::NT), 0, stream, a, L);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
