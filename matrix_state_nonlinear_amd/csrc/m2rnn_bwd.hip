@@ -408,7 +408,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
         if (g == 0) sm.rq[jp][li][wr] = dqp;
       }
       // dq of the previous phase's step: the per-wave sums, added by wave 0
-      if (wr == 0 && g == 0 && row_ok && j >= 1 && j <= nch * S) {
+      if (wr == 0 && g == 0 && (FULL || row_ok) && j >= 1 && j <= nch * S) {
         const int tf = I > 0 ? cF * S + I - 1 : cF * S + 2 * S - 1;
         if (tf < T32) {
           Real sq = 0;

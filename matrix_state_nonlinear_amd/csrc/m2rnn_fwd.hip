@@ -80,10 +80,10 @@ struct FwdSmem {
   Real q[RING][16];           // q_i of a step
 };
 
-// RCS: also store every step's rc.  FULL (with RCS): every row of the slab and
-// every column of the tiles exists and the state is fp32, so each lane's rc store
-// is one unguarded 16-byte store; the guards (branches on row and column) cost
-// more than the store itself in the step.
+// RCS: also store every step's rc.  FULL: every row of the slab and every
+// column of the tiles exists and the state is fp32, so each lane's rc,
+// checkpoint and final-state stores are unguarded 16-byte stores; the guards
+// (branches on row and column) cost more than the stores themselves.
 template <typename InT, typename Real, int VT, bool RCS, bool FULL>
 __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT * FwdTraits<Real, VT>::PACK))
     m2rnn_fwd_kernel(FwdArgs a) {
@@ -179,6 +179,11 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT * FwdTraits<Real, VT>
   const bool st_vec = sizeof(Real) == 4 && (V & 3) == 0;
   // this lane's values of a [K, V] array (row `row`, its tiles' columns)
   auto write_rows = [&](Real* dst, const R4 (&val)[TPW]) {
+    if constexpr (FULL) {  // every row and column exists: one 16-byte store per tile
+#pragma unroll
+      for (int p = 0; p < TPW; ++p) *(R4*)(dst + col_of(p, 0)) = val[p];
+      return;
+    }
     if (!row_ok) return;
 #pragma unroll
     for (int p = 0; p < TPW; ++p) {
@@ -567,18 +572,25 @@ static hipError_t launch_fwd_vt(const FwdArgs& a, hipStream_t stream) {
   const int64_t units = a.B * a.N * a.nslab;
   const int64_t wgs = (units + Tr::PACK - 1) / Tr::PACK;
   // every tile full: K rows in whole slabs, V columns in whole tiles, fp32
-  // state, and rc 16-byte aligned
-  const bool full = sizeof(Real) == 4 && a.K % 16 == 0 && a.V == Tr::VP &&
-                    ((uintptr_t)a.rc & 15) == 0;
-  if (a.rc && full)  // also store every step's rc
-    hipLaunchKernelGGL((m2rnn_fwd_kernel<InT, Real, VT, true, true>), dim3((unsigned)wgs),
-                       dim3(Tr::NT * Tr::PACK), 0, stream, a);
-  else if (a.rc)
-    hipLaunchKernelGGL((m2rnn_fwd_kernel<InT, Real, VT, true, false>), dim3((unsigned)wgs),
-                       dim3(Tr::NT * Tr::PACK), 0, stream, a);
-  else
-    hipLaunchKernelGGL((m2rnn_fwd_kernel<InT, Real, VT, false, false>), dim3((unsigned)wgs),
-                       dim3(Tr::NT * Tr::PACK), 0, stream, a);
+  // state, and the rc, checkpoint and H_T arrays 16-byte aligned
+  auto al = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  const bool full = sizeof(Real) == 4 && a.K % 16 == 0 && a.V == Tr::VP && al(a.rc) &&
+                    al(a.ckpt) && al(a.HT);
+  const dim3 grid((unsigned)wgs), block(Tr::NT * Tr::PACK);
+  if constexpr (sizeof(Real) == 4) {
+    if (full) {
+      if (a.rc)  // also store every step's rc
+        hipLaunchKernelGGL((m2rnn_fwd_kernel<InT, Real, VT, true, true>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((m2rnn_fwd_kernel<InT, Real, VT, false, true>), grid, block, 0, stream, a);
+    }
+  }
+  if (!full) {
+    if (a.rc)
+      hipLaunchKernelGGL((m2rnn_fwd_kernel<InT, Real, VT, true, false>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((m2rnn_fwd_kernel<InT, Real, VT, false, false>), grid, block, 0, stream, a);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.nslab == 1) return err;
   const int64_t total = a.B * a.T * a.N * a.V;
