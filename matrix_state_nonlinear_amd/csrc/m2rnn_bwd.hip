@@ -1335,15 +1335,19 @@ static hipError_t launch_bwd_vt(const BwdArgs& a0, hipStream_t stream) {
   // rc 16-byte aligned
   const bool full = sizeof(Real) == 4 && a.K % 16 == 0 && a.V == Tr::VP &&
                     ((uintptr_t)a.rc & 15) == 0;
-  if (a.rc && full)  // the forward's rc replaces the recomputation inside each chunk
-    hipLaunchKernelGGL((m2rnn_bwd_kernel<InT, Real, VT, true, true>), dim3((unsigned)units),
-                       dim3(Tr::NT), 0, stream, a, L);
-  else if (a.rc)
-    hipLaunchKernelGGL((m2rnn_bwd_kernel<InT, Real, VT, true, false>), dim3((unsigned)units),
-                       dim3(Tr::NT), 0, stream, a, L);
-  else
-    hipLaunchKernelGGL((m2rnn_bwd_kernel<InT, Real, VT, false, false>), dim3((unsigned)units),
-                       dim3(Tr::NT), 0, stream, a, L);
+  const dim3 grid((unsigned)units), block(Tr::NT);
+  if constexpr (sizeof(Real) == 4) {
+    if (full && a.rc)  // the forward's rc replaces the recomputation inside each chunk
+      hipLaunchKernelGGL((m2rnn_bwd_kernel<InT, Real, VT, true, true>), grid, block, 0, stream, a, L);
+    else if (full)
+      hipLaunchKernelGGL((m2rnn_bwd_kernel<InT, Real, VT, false, true>), grid, block, 0, stream, a, L);
+  }
+  if (!full) {
+    if (a.rc)
+      hipLaunchKernelGGL((m2rnn_bwd_kernel<InT, Real, VT, true, false>), grid, block, 0, stream, a, L);
+    else
+      hipLaunchKernelGGL((m2rnn_bwd_kernel<InT, Real, VT, false, false>), grid, block, 0, stream, a, L);
+  }
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   const int64_t tokens = a.B * a.T * a.N;
