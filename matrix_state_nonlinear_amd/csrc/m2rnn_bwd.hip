@@ -1235,34 +1235,61 @@ __global__ void __launch_bounds__(256)
                             const Real* __restrict__ beta, const Real* __restrict__ dlogit,
                             Real* __restrict__ col_part) {
   constexpr int kMaxCols = 16 * kMaxValueTiles + 2;
-  __shared__ Real red[4][kMaxCols];
+  __shared__ Real red[16][kMaxCols];  // [wave x rows per load][column] partials
+  __shared__ Real red2[2][256];       // the two per-head columns, one row per thread
   const int64_t rb = blockIdx.x;
   const int64_t n = blockIdx.y;
   const int ncol = (int)V + 2;
   const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
   const int64_t r0 = rb * 256;
   const int64_t r1 = (r0 + 256) < rows ? (r0 + 256) : rows;
-  const int64_t rstep = 4 * N * V;  // element step between rows r and r + 4
-  for (int col = lane; col < ncol; col += 64) {
+  // value columns: with V < 64 one load covers rpl = min(4, 64 / V) rows (lane:
+  // row offset lane / V, column lane % V), so narrow heads use most lanes
+  const int rpl = V < 16 ? 4 : V < 64 ? (int)(64 / V) : 1;
+  const int ro = V < 64 ? lane / (int)V : 0;
+  const int64_t rstep = 4 * rpl * N * V;  // element step between a lane's rows
+  for (int c0 = 0; c0 < (int)V; c0 += 64) {
+    const int col = V < 64 ? lane % (int)V : c0 + lane;
     Real s = 0;
-    if (col < V) {
-      int64_t i = ((r0 + grp) * N + n) * V + col;
-      for (int64_t r = r0 + grp; r < r1; r += 4, i += rstep) s += dy[i] * load_as<Real>(v + i);
-    } else if (kind == kGateExpSoftplus) {
-      for (int64_t r = r0 + grp; r < r1; r += 4) {
-        const int64_t i = r * N + n;
-        if (col == V) {
-          s += -df[i] * softplus_(logit[i] + beta[n]) * f[i];
-        } else {
-          s += dlogit[i];
-        }
-      }
+    if (ro < rpl && col < (int)V) {
+      const int64_t rfirst = r0 + grp * rpl + ro;
+      int64_t i = (rfirst * N + n) * V + col;
+      for (int64_t r = rfirst; r < r1; r += 4 * rpl, i += rstep) s += dy[i] * load_as<Real>(v + i);
+      red[grp * rpl + ro][col] = s;
     }
-    red[grp][col] = s;
+  }
+  // the per-head columns (exp-softplus gate): dalpha and dbeta terms of row r0 + tid
+  if (kind == kGateExpSoftplus) {
+    const int64_t r = r0 + threadIdx.x;
+    Real ta = 0, tb = 0;
+    if (r < r1) {
+      const int64_t i = r * N + n;
+      ta = -df[i] * softplus_(logit[i] + beta[n]) * f[i];
+      tb = dlogit[i];
+    }
+    red2[0][threadIdx.x] = ta;
+    red2[1][threadIdx.x] = tb;
   }
   __syncthreads();
-  for (int col = threadIdx.x; col < ncol; col += blockDim.x)
-    col_part[(rb * N + n) * ncol + col] = ((red[0][col] + red[1][col]) + red[2][col]) + red[3][col];
+  // fixed-order sums: value columns over the 4 rpl partials, per-head columns
+  // over the 256 rows by a tree
+  for (int col = threadIdx.x; col < (int)V; col += blockDim.x) {
+    Real s = 0;
+    for (int k = 0; k < 4 * rpl; ++k) s += red[k][col];
+    col_part[(rb * N + n) * ncol + col] = s;
+  }
+  if (kind == kGateExpSoftplus) {
+    for (int h = 128; h >= 1; h >>= 1) {
+      if ((int)threadIdx.x < 2 * h) {
+        const int w = threadIdx.x / h, k = threadIdx.x % h;
+        red2[w][k] += red2[w][k + h];
+      }
+      __syncthreads();
+    }
+    if (threadIdx.x < 2) col_part[(rb * N + n) * ncol + V + threadIdx.x] = red2[threadIdx.x][0];
+  } else if (threadIdx.x < 2) {
+    col_part[(rb * N + n) * ncol + V + threadIdx.x] = Real(0);
+  }
 }
 
 // stage 2: sum the row blocks in order
