@@ -16,9 +16,14 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Every tensor pointer is DEVICE memory owned by the caller, C-contiguous,
- *   in the layout stated next to it.  The library allocates nothing and keeps
- *   no state between calls; calls are asynchronous on `stream` (a hipStream_t,
- *   NULL = the default stream) and never synchronise the device.
+ *   in the layout stated next to it, aligned to its element type.  The library
+ *   allocates nothing; between calls it keeps only a per-device cache of one
+ *   occupancy query (m2rnn_step; atomic, so concurrent host threads are safe).
+ *   Calls are asynchronous on `stream` (a hipStream_t, NULL = the default
+ *   stream) and never synchronise the device.
+ * - Wider (16-byte) memory accesses are used where an array's address and row
+ *   length allow them and element accesses otherwise, so no alignment beyond
+ *   the element type's is required (m2rnn_newton_fwd states its own).
  * - Outputs are overwritten, never accumulated, and must not alias inputs.
  * - `state_dtype` (M2RNN_F32 or M2RNN_F64) is the type of the recurrent state,
  *   of every accumulation, and of every floating-point tensor except k, v, q:

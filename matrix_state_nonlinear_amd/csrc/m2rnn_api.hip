@@ -109,7 +109,36 @@ bool newton_supported(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V) {
   return waves < 2.0e9 && map_waves < 2.0e9 && U * (double)T * (double)K * (double)V < 4.0e18;
 }
 
-bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+// The argument checks of m2rnn_bwd, before any
+// workspace: M2RNN_OK or the status to return.
+int bwd_check(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K, int64_t V,
+              int in_dtype, int state_dtype, const void* k, const void* v, const void* q,
+              int gate_kind, const void* logit, const void* alpha, const void* beta,
+              const void* f, const void* W, const void* w_r, const void* ckpt, int64_t C,
+              const void* dy, const void* dk, const void* dv, const void* dq, const void* dlogit,
+              const void* dW, const void* dw_r, const void* dalpha, const void* dbeta) {
+  if (!sizes_ok(B, T, n_heads, K, V) || !qk_heads_ok(n_heads, qk_heads))
+    return M2RNN_ERR_INVALID_ARG;
+  if (!in_dtype_known(in_dtype) || !state_dtype_known(state_dtype)) return M2RNN_ERR_INVALID_ARG;
+  const bool empty = B * T * n_heads == 0;
+  const bool heads = n_heads > 0;  // per-head outputs exist
+  if (!empty && (!k || !v || !q || !logit || !f || !W || !w_r || !ckpt || !dy))
+    return M2RNN_ERR_INVALID_ARG;
+  if (!empty && (!dk || !dv || !dq || !dlogit)) return M2RNN_ERR_INVALID_ARG;
+  if (heads && (!dW || !dw_r)) return M2RNN_ERR_INVALID_ARG;
+  if (C < 1) return M2RNN_ERR_INVALID_ARG;
+  if (gate_kind == M2RNN_GATE_SIGMOID) {
+    if (alpha || beta || dalpha || dbeta) return M2RNN_ERR_INVALID_ARG;
+  } else if (gate_kind == M2RNN_GATE_EXP_SOFTPLUS) {
+    if (heads && (!dalpha || !dbeta)) return M2RNN_ERR_INVALID_ARG;
+    if (!empty && (!alpha || !beta)) return M2RNN_ERR_INVALID_ARG;
+  } else {
+    return M2RNN_ERR_INVALID_ARG;
+  }
+  if (!sizes_supported(B, T, n_heads, K, V) || !dtypes_ok(in_dtype, state_dtype))
+    return M2RNN_ERR_UNSUPPORTED;
+  return M2RNN_OK;
+}
 
 }  // namespace
 
@@ -189,26 +218,11 @@ int m2rnn_bwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K
               void* dq,
               void* dlogit, void* dW, void* dw_r, void* dalpha, void* dbeta, void* dH0,
               void* workspace, size_t workspace_bytes, void* stream) {
-  if (!sizes_ok(B, T, n_heads, K, V) || !qk_heads_ok(n_heads, qk_heads))
-    return M2RNN_ERR_INVALID_ARG;
-  if (!in_dtype_known(in_dtype) || !state_dtype_known(state_dtype)) return M2RNN_ERR_INVALID_ARG;
+  const int chk = bwd_check(B, T, n_heads, qk_heads, K, V, in_dtype, state_dtype, k, v, q,
+                            gate_kind, logit, alpha, beta, f, W, w_r, ckpt, C, dy, dk, dv, dq,
+                            dlogit, dW, dw_r, dalpha, dbeta);
+  if (chk != M2RNN_OK) return chk;
   const bool empty = B * T * n_heads == 0;
-  const bool heads = n_heads > 0;  // per-head outputs exist
-  if (!empty && (!k || !v || !q || !logit || !f || !W || !w_r || !ckpt || !dy))
-    return M2RNN_ERR_INVALID_ARG;
-  if (!empty && (!dk || !dv || !dq || !dlogit)) return M2RNN_ERR_INVALID_ARG;
-  if (heads && (!dW || !dw_r)) return M2RNN_ERR_INVALID_ARG;
-  if (C < 1) return M2RNN_ERR_INVALID_ARG;
-  if (gate_kind == M2RNN_GATE_SIGMOID) {
-    if (alpha || beta || dalpha || dbeta) return M2RNN_ERR_INVALID_ARG;
-  } else if (gate_kind == M2RNN_GATE_EXP_SOFTPLUS) {
-    if (heads && (!dalpha || !dbeta)) return M2RNN_ERR_INVALID_ARG;
-    if (!empty && (!alpha || !beta)) return M2RNN_ERR_INVALID_ARG;
-  } else {
-    return M2RNN_ERR_INVALID_ARG;
-  }
-  if (!sizes_supported(B, T, n_heads, K, V) || !dtypes_ok(in_dtype, state_dtype))
-    return M2RNN_ERR_UNSUPPORTED;
   if (empty) {
     // no step: dH_0 = dH_T (zero when NULL); dW, dw_r (and dalpha, dbeta) are
     // sums over no tokens; the per-token gradients are empty

@@ -264,7 +264,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
       }
 #pragma unroll
     for (int p = 0; p < TPW; ++p) pin_values(wrc[p][0], wrc[p][1], wrc[p][2], wrc[p][3]);
-    const bool dv_vec = sizeof(Real) == 4 && (FULL || (V & 3) == 0);
+    const bool dv_vec = sizeof(Real) == 4 && (FULL || a.dv_vec);
     // output pointers at token (b, t = 0, n); step t adds t N rows
     Real* const dq_row = dq_base + tok0 * K + row;
     Real* const dv_tok = nslab == 1 ? (Real*)a.dv + tok0 * V
@@ -276,7 +276,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
     R4 rcn[TPW];
     const Real* rc_lane = nullptr;
     const int64_t KV = K * V;
-    const bool rc_vec = sizeof(Real) == 4 && (FULL || (V & 3) == 0);
+    const bool rc_vec = sizeof(Real) == 4 && (FULL || a.rc_vec);
     auto load_rc = [&](int t) {
       const int tt = t < T32 ? t : T32 - 1;
       const Real* src = rc_lane + (int64_t)tt * KV;
@@ -906,7 +906,7 @@ __global__ void __launch_bounds__(256)
       if (i < ne) dst[i] = h[i];
   };
   if (t0 % S == 0) write_start(t0);
-  if (sizeof(Real) == 4 && ne == 4 && (KV & 3) == 0) {
+  if (sizeof(Real) == 4 && ne == 4 && (KV & 3) == 0 && a.rc_vec) {
     // four consecutive fp32 elements: one 16-byte load per step, eight steps'
     // loads issued ahead of their use
     using R4 = typename Vec4<Real>::type;
@@ -1358,10 +1358,15 @@ static hipError_t launch_bwd_vt(const BwdArgs& a0, hipStream_t stream) {
     a.cks_count = nck;
     a.cks_step = Tr::S / a.C;
   }
+  // 16-byte rc loads and dv stores where fp32 columns come in fours and the
+  // arrays are aligned for them (dv goes to the workspace partials when the
+  // head has several slabs)
+  const bool v4 = sizeof(Real) == 4 && (a.V & 3) == 0;
+  a.rc_vec = v4 && aligned16(a.rc);
+  a.dv_vec = v4 && aligned16(a.nslab == 1 ? a.dv : (const void*)(ws + L.dv_part));
   // every tile full: K rows in whole slabs, V columns in whole tiles, fp32 state,
-  // rc 16-byte aligned
-  const bool full = sizeof(Real) == 4 && a.K % 16 == 0 && a.V == Tr::VP &&
-                    ((uintptr_t)a.rc & 15) == 0;
+  // rc and the dv destination 16-byte aligned
+  const bool full = sizeof(Real) == 4 && a.K % 16 == 0 && a.V == Tr::VP && a.rc_vec && a.dv_vec;
   const dim3 grid((unsigned)units), block(Tr::NT);
   if constexpr (sizeof(Real) == 4) {
     if (full && a.rc)  // the forward's rc replaces the recomputation inside each chunk
@@ -1388,7 +1393,8 @@ static hipError_t launch_bwd_vt(const BwdArgs& a0, hipStream_t stream) {
     if (total < ((int64_t)1 << 31)) {
       hipLaunchKernelGGL((m2rnn_slab_sum_kernel<Real, Real>), dim3(grid_for(total)), dim3(256), 0,
                          stream, (int)tokens, (int)a.N, (int)a.V, a.nslab, total, ws + L.dv_part,
-                         (const Real*)a.dy, (const Real*)a.w_r, (Real*)a.dv);
+                         (const Real*)a.dy, (const Real*)a.w_r, (Real*)a.dv,
+                         slab_sum_vec<Real, Real>(a.V, ws + L.dv_part, a.dy, a.w_r, a.dv));
     } else {
       hipLaunchKernelGGL((m2rnn_bwd_dv_kernel<Real>), dim3(grid_for(total)), dim3(256), 0, stream,
                          total, a.N, a.V, a.nslab, ws + L.dv_part, (const Real*)a.dy,

@@ -277,15 +277,16 @@ __device__ __forceinline__ int64_t clamp_idx(int64_t x, int64_t hi) { return x <
 
 // out[row][j] = sum over slabs sl of part[sl][row][j] (in slab order)
 //               + w_r[row mod N][j] * x[row][j],   rows = B T N token rows.
-// Elementwise and HBM-bound.  fp32 with V a multiple of 4: one 16-byte access
-// per array and thread; 32-bit indices (the launcher checks rows V < 2^31).
+// Elementwise and HBM-bound.  `vec` (slab_sum_vec: fp32, V a multiple of 4,
+// every array aligned for it): one 16-byte access per array and thread (8-byte
+// for bf16 x); 32-bit indices (the launcher checks rows V < 2^31).
 template <typename InT, typename Real>
 __global__ void __launch_bounds__(256)
     m2rnn_slab_sum_kernel(int rows, int N, int V, int nslab, int64_t slab_stride,
                           const Real* __restrict__ part, const InT* __restrict__ x,
-                          const Real* __restrict__ w_r, Real* __restrict__ out) {
+                          const Real* __restrict__ w_r, Real* __restrict__ out, bool vec) {
   const int stride = gridDim.x * blockDim.x;
-  if (sizeof(Real) == 4 && (V & 3) == 0) {
+  if (sizeof(Real) == 4 && vec) {
     const int cpr = V >> 2;  // 4-column groups per row
     const int total = rows * cpr;
     for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < total; c += stride) {
@@ -319,6 +320,15 @@ __global__ void __launch_bounds__(256)
       out[e] = fma_r(w_r[(int64_t)n * V + j], (Real)load_in(x + e), acc);
     }
   }
+}
+
+// Whether m2rnn_slab_sum_kernel may take its vector path for these arrays.
+template <typename InT, typename Real>
+inline bool slab_sum_vec(int64_t V, const void* part, const void* x, const void* w_r,
+                         const void* out) {
+  const uintptr_t xa = sizeof(InT) == 2 ? 7 : 15;
+  return sizeof(Real) == 4 && (V & 3) == 0 && (((uintptr_t)part | (uintptr_t)w_r | (uintptr_t)out) & 15) == 0 &&
+         ((uintptr_t)x & xa) == 0;
 }
 
 }  // namespace m2rnn

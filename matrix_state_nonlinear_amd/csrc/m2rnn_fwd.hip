@@ -175,8 +175,9 @@ __global__ void __launch_bounds__((FwdTraits<Real, VT>::NT * FwdTraits<Real, VT>
       hown[p][r] = (a.H0 && row_ok && col < V) ? ((const Real*)a.H0)[state_base + col] : Real(0);
     }
   const int64_t nck = a.ckpt ? (T + a.C - 1) / a.C : 0;
-  // where a lane's four columns are consecutive (fp32), one 16-byte store
-  const bool st_vec = sizeof(Real) == 4 && (V & 3) == 0;
+  // where a lane's four columns are consecutive (fp32) and the arrays are
+  // 16-byte aligned, one 16-byte store
+  const bool st_vec = sizeof(Real) == 4 && a.st_vec;
   // this lane's values of a [K, V] array (row `row`, its tiles' columns)
   auto write_rows = [&](Real* dst, const R4 (&val)[TPW]) {
     if constexpr (FULL) {  // every row and column exists: one 16-byte store per tile
@@ -573,9 +574,7 @@ static hipError_t launch_fwd_vt(const FwdArgs& a, hipStream_t stream) {
   const int64_t wgs = (units + Tr::PACK - 1) / Tr::PACK;
   // every tile full: K rows in whole slabs, V columns in whole tiles, fp32
   // state, and the rc, checkpoint and H_T arrays 16-byte aligned
-  auto al = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
-  const bool full = sizeof(Real) == 4 && a.K % 16 == 0 && a.V == Tr::VP && al(a.rc) &&
-                    al(a.ckpt) && al(a.HT);
+  const bool full = sizeof(Real) == 4 && a.K % 16 == 0 && a.V == Tr::VP && a.st_vec;
   const dim3 grid((unsigned)wgs), block(Tr::NT * Tr::PACK);
   if constexpr (sizeof(Real) == 4) {
     if (full) {
@@ -599,7 +598,8 @@ static hipError_t launch_fwd_vt(const FwdArgs& a, hipStream_t stream) {
   if (total < ((int64_t)1 << 31)) {
     hipLaunchKernelGGL((m2rnn_slab_sum_kernel<InT, Real>), dim3((unsigned)blocks), dim3(256), 0,
                        stream, (int)(a.B * a.T * a.N), (int)a.N, (int)a.V, a.nslab, total,
-                       (const Real*)a.ypart, (const InT*)a.v, (const Real*)a.w_r, (Real*)a.y);
+                       (const Real*)a.ypart, (const InT*)a.v, (const Real*)a.w_r, (Real*)a.y,
+                       slab_sum_vec<InT, Real>(a.V, a.ypart, a.v, a.w_r, a.y));
   } else {
     hipLaunchKernelGGL((m2rnn_fwd_reduce_kernel<InT, Real>), dim3((unsigned)blocks), dim3(256), 0,
                        stream, total, a.N, a.V, a.nslab, (const Real*)a.ypart, (const InT*)a.v,
@@ -621,7 +621,10 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   }
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int in_dtype, int state_dtype, hipStream_t stream) {
+hipError_t launch_fwd(const FwdArgs& a0, int in_dtype, int state_dtype, hipStream_t stream) {
+  FwdArgs a = a0;
+  a.st_vec = state_dtype == kF32 && (a.V & 3) == 0 && aligned16(a.ckpt) && aligned16(a.HT) &&
+             aligned16(a.rc);
   if (state_dtype == kF32) {
     if (in_dtype == kF32) return launch_fwd_t<float, float>(a, stream);
     if (in_dtype == kBF16) return launch_fwd_t<uint16_t, float>(a, stream);

@@ -47,6 +47,7 @@ struct FwdArgs {
   int64_t B, T, N, K, V, C;
   int64_t NQ;        // heads of q and k; value head n reads q/k head n / (N / NQ)
   int nslab;
+  int st_vec;        // fp32, V % 4 == 0 and ckpt, HT, rc 16-byte aligned: 16-byte state stores
 };
 
 struct BwdArgs {
@@ -83,7 +84,11 @@ struct BwdArgs {
   int64_t NQ;        // heads of q and k; value head n reads q/k head n / (N / NQ)
   int nslab;
   int gate_kind;
+  int rc_vec;        // fp32, V % 4 == 0 and rc 16-byte aligned: 16-byte rc loads
+  int dv_vec;        // fp32, V % 4 == 0 and the dv destination 16-byte aligned: 16-byte stores
 };
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 // Workspace layout of the backward: offsets in elements of the state type,
 // each region aligned to 64 elements.

@@ -25,6 +25,7 @@
 // in turn (the workgroup stages W once for all of them) and loads the next
 // (row, slab) while computing the current one (16-byte loads in fp32).
 
+#include <atomic>
 #include <type_traits>
 
 #include "m2rnn_device.h"
@@ -264,12 +265,14 @@ static hipError_t launch_step_vt(StepArgs a, hipStream_t stream) {
   static_assert(sizeof(typename Vec4<Real>::type) * VT * VT * 64 <= 160 * 1024, "LDS budget");
   // Workgroups the device holds at once (occupancy x compute units), per
   // device, found once.  Each wave takes enough units that the grid fits in
-  // one round, so every workgroup stages W once for several batch rows.
+  // one round, so every workgroup stages W once for several batch rows.  The
+  // cache is atomic: host threads may call concurrently, and all of them
+  // compute and store the same value.
   constexpr int kMaxDevices = 64;
-  static int resident[kMaxDevices] = {};
+  static std::atomic<int> resident[kMaxDevices];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = kMaxDevices;
-  int cap = dev < kMaxDevices ? resident[dev] : 0;
+  int cap = dev < kMaxDevices ? resident[dev].load(std::memory_order_relaxed) : 0;
   if (cap <= 0) {
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, m2rnn_step_kernel<InT, Real, VT>,
@@ -280,7 +283,7 @@ static hipError_t launch_step_vt(StepArgs a, hipStream_t stream) {
       cus = 256;
     }
     cap = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
-    if (dev < kMaxDevices) resident[dev] = cap;
+    if (dev < kMaxDevices) resident[dev].store(cap, std::memory_order_relaxed);
   }
   const int64_t groups = (a.B + 3) / 4;  // groups of four batch rows per head
   int64_t upw = (a.N * groups + cap - 1) / cap;

@@ -129,6 +129,12 @@ def m2rnn_fwd(k, v, q, f, W, w_r, H0=None, C: int = 0, want_ht: bool = True,
         HT = torch.empty((B, N, K, V), dtype=sd, device=dev) if want_ht else None
         ckpt = (torch.empty((B, N, math.ceil(T / C), K, V), dtype=sd, device=dev)
                 if C and C > 0 else None)
+    _need(y, (B, T, N, V), sd, "y")
+    _opt(HT, (B, N, K, V), sd, "HT")
+    if ckpt is not None:
+        if not C or C < 1:
+            raise ValueError("a checkpoint buffer needs C >= 1")
+        _need(ckpt, (B, N, math.ceil(T / C), K, V), sd, "ckpt")
     _opt(rc_out, (B, N, T, K, V), sd, "rc_out")
     ws, wsb = _workspace(m2rnn_workspace_bytes(False, B, T, N, NQ, K, V, max(C, 1), sd), dev,
                          workspace)
@@ -140,13 +146,10 @@ def m2rnn_fwd(k, v, q, f, W, w_r, H0=None, C: int = 0, want_ht: bool = True,
     return y, HT, ckpt
 
 
-def m2rnn_bwd(k, v, q, gate_kind: int, logit, alpha, beta, f, W, w_r, H0, ckpt, C: int, dy,
-              dHT=None, want_dh0: bool = True, workspace=None, rc=None):
-    """Backward of m2rnn_fwd.  Returns a dict with dk, dv, dq, dlogit, dW, dw_r,
-    dalpha and dbeta (exp-softplus gate only, else None) and dH0 (or None).
-    dk and dq have the shape of k and q: with shared heads (NQ < N) each is
-    the sum over the value heads that read it.  ``rc`` (from m2rnn_fwd's rc_out)
-    replaces the recomputation of the states; the results are the same."""
+def _bwd_outputs(k, v, q, gate_kind, logit, alpha, beta, f, W, w_r, H0, ckpt, C, dy, dHT,
+                 want_dh0, rc, out):
+    """Checks the backward's inputs and returns (B, T, N, NQ, K, V, state dtype,
+    output dict) with the given or newly allocated gradient buffers."""
     N, NQ = _heads(k, v)
     B, T, _, K = k.shape
     V = v.shape[-1]
@@ -163,21 +166,53 @@ def m2rnn_bwd(k, v, q, gate_kind: int, logit, alpha, beta, f, W, w_r, H0, ckpt, 
     _opt(dHT, (B, N, K, V), sd, "dHT")
     _opt(rc, (B, N, T, K, V), sd, "rc")
     dev = k.device
-    e = lambda *s: torch.empty(s, dtype=sd, device=dev)  # noqa: E731
-    out = {"dk": e(B, T, NQ, K), "dv": e(B, T, N, V), "dq": e(B, T, NQ, K),
-           "dlogit": e(B, T, N), "dW": e(N, V, V), "dw_r": e(N, V),
-           "dalpha": e(N) if gate_kind == _lib.M2RNN_GATE_EXP_SOFTPLUS else None,
-           "dbeta": e(N) if gate_kind == _lib.M2RNN_GATE_EXP_SOFTPLUS else None,
-           "dH0": e(B, N, K, V) if want_dh0 else None}
+    exp_gate = gate_kind == _lib.M2RNN_GATE_EXP_SOFTPLUS
+    shapes = {"dk": (B, T, NQ, K), "dv": (B, T, N, V), "dq": (B, T, NQ, K), "dlogit": (B, T, N),
+              "dW": (N, V, V), "dw_r": (N, V), "dalpha": (N,) if exp_gate else None,
+              "dbeta": (N,) if exp_gate else None, "dH0": (B, N, K, V) if want_dh0 else None}
+    given = dict(out) if out is not None else {}
+    res = {}
+    for name, shape in shapes.items():
+        if name in given:
+            res[name] = given[name]
+            if shape is None:
+                if res[name] is not None:
+                    raise ValueError(f"{name} is not an output of this gate")
+            else:
+                (_opt if name == "dH0" else _need)(res[name], shape, sd, name)
+        else:
+            res[name] = None if shape is None else torch.empty(shape, dtype=sd, device=dev)
+    return B, T, N, NQ, K, V, sd, res
+
+
+def _bwd_args(k, v, q, gate_kind, logit, alpha, beta, f, W, w_r, H0, ckpt, C, rc, dy, dHT, o):
+    """The pointer arguments of the backward entry points, in ABI order
+    from k to dH0."""
+    return (_ptr(k), _ptr(v), _ptr(q), int(gate_kind), _ptr(logit), _ptr(alpha), _ptr(beta),
+            _ptr(f), _ptr(W), _ptr(w_r), _ptr(H0), _ptr(ckpt), int(C), _ptr(rc), _ptr(dy),
+            _ptr(dHT), _ptr(o["dk"]), _ptr(o["dv"]), _ptr(o["dq"]), _ptr(o["dlogit"]),
+            _ptr(o["dW"]), _ptr(o["dw_r"]), _ptr(o["dalpha"]), _ptr(o["dbeta"]), _ptr(o["dH0"]))
+
+
+def m2rnn_bwd(k, v, q, gate_kind: int, logit, alpha, beta, f, W, w_r, H0, ckpt, C: int, dy,
+              dHT=None, want_dh0: bool = True, workspace=None, rc=None, out=None):
+    """Backward of m2rnn_fwd.  Returns a dict with dk, dv, dq, dlogit, dW, dw_r,
+    dalpha and dbeta (exp-softplus gate only, else None) and dH0 (or None).
+    dk and dq have the shape of k and q: with shared heads (NQ < N) each is
+    the sum over the value heads that read it.  ``rc`` (from m2rnn_fwd's rc_out)
+    replaces the recomputation of the states; the results are the same.
+    ``out`` may hold preallocated gradient buffers under those names (any
+    missing one is allocated; dH0 = None there skips it)."""
+    B, T, N, NQ, K, V, sd, o = _bwd_outputs(k, v, q, gate_kind, logit, alpha, beta, f, W, w_r,
+                                            H0, ckpt, C, dy, dHT, want_dh0, rc, out)
+    dev = k.device
     ws, wsb = _workspace(m2rnn_workspace_bytes(True, B, T, N, NQ, K, V, C, sd), dev, workspace)
     st = _lib.lib().m2rnn_bwd(
-        B, T, N, NQ, K, V, _DT[k.dtype], _DT[sd], _ptr(k), _ptr(v), _ptr(q), int(gate_kind),
-        _ptr(logit), _ptr(alpha), _ptr(beta), _ptr(f), _ptr(W), _ptr(w_r), _ptr(H0), _ptr(ckpt),
-        int(C), _ptr(rc), _ptr(dy), _ptr(dHT), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dq"]),
-        _ptr(out["dlogit"]), _ptr(out["dW"]), _ptr(out["dw_r"]), _ptr(out["dalpha"]),
-        _ptr(out["dbeta"]), _ptr(out["dH0"]), _ptr(ws), wsb, _stream(dev))
+        B, T, N, NQ, K, V, _DT[k.dtype], _DT[sd],
+        *_bwd_args(k, v, q, gate_kind, logit, alpha, beta, f, W, w_r, H0, ckpt, C, rc, dy, dHT, o),
+        _ptr(ws), wsb, _stream(dev))
     check(st, "m2rnn_bwd")
-    return out
+    return o
 
 
 def m2rnn_newton_workspace_bytes(B: int, T: int, n_heads: int, K: int, V: int,
@@ -214,6 +249,8 @@ def m2rnn_newton_fwd(k, v, q, f, W, w_r, H0=None, iters: int = 3, want_ht: bool 
         HT = torch.empty((B, N, K, V), dtype=sd, device=dev) if want_ht else None
         states = torch.empty((B, N, T, K, V), dtype=sd, device=dev) if want_states else None
         res = torch.empty((iters + 1,), dtype=sd, device=dev) if want_residual else None
+    _need(y, (B, T, N, V), sd, "y")
+    _opt(HT, (B, N, K, V), sd, "HT")
     _opt(states, (B, N, T, K, V), sd, "states")
     _opt(res, (iters + 1,), sd, "residual")
     ws, wsb = _workspace(m2rnn_newton_workspace_bytes(B, T, N, K, V, states is not None), dev,

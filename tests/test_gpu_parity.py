@@ -19,7 +19,7 @@ import torch
 
 import oracle
 from m2rnn_inputs import WORKLOADS, WORKLOAD_ORDER, Workload, make_inputs, to_device
-from matrix_state_nonlinear_amd import m2rnn_bwd, m2rnn_fwd, m2rnn_gates
+from matrix_state_nonlinear_amd import m2rnn_bwd, m2rnn_fwd, m2rnn_gates, m2rnn_workspace_bytes
 
 pytestmark = pytest.mark.gpu
 
@@ -206,8 +206,10 @@ def test_backward_workload_recipes(name, sd):
 
 
 @pytest.mark.parametrize("K,V,C", [(1, 1, 1), (17, 40, 7), (40, 72, 64), (33, 100, 5),
-                                   (16, 128, 3)])
+                                   (16, 128, 3), (20, 20, 3), (32, 32, 4), (9, 24, 2)])
 def test_backward_shapes(K, V, C):
+    # V = 20, 24, 32: the column sums of dw_r, dalpha, dbeta read 3 or 2 rows
+    # per load (V in 17..32), V <= 16: 4 rows, V >= 64: one
     wl = WORKLOADS["fwd_bwd_k32_v128"].replace(B=2, T=29, N=2, K=K, V=V,
                                                kq_scale=1 / math.sqrt(K),
                                                v_scale=1 / math.sqrt(V), w_scale=1 / math.sqrt(V))
@@ -305,3 +307,53 @@ def test_stored_rc_forward_and_backward(K, V, C, NQ, sd):
     for name in g0:
         if g0[name] is not None:
             assert torch.equal(g0[name], g1[name]), name
+
+
+# ---------------------------------------------------------------- alignment
+
+def _offset_view(shape, dtype, elems=1, dev="cuda:0"):
+    """A contiguous tensor that starts `elems` elements into its storage, so it
+    is aligned to its element type but not to 16 bytes."""
+    n = int(np.prod(shape))
+    return torch.empty(n + elems, dtype=dtype, device=dev)[elems:].view(shape)
+
+
+@pytest.mark.parametrize("K,V,C", [(64, 64, 4), (32, 128, 6), (16, 16, 2), (40, 72, 3)])
+def test_element_aligned_buffers_give_identical_results(K, V, C):
+    """Arrays that are aligned to their element type but not to 16 bytes take
+    the element-access paths of the kernels (the 16-byte ones need 16-byte
+    addresses): results equal those with 16-byte aligned buffers, bit for bit."""
+    wl = WORKLOADS["fwd_bwd_k32_v128"].replace(B=2, T=37, N=2, K=K, V=V,
+                                               kq_scale=1 / math.sqrt(K),
+                                               v_scale=1 / math.sqrt(V), w_scale=1 / math.sqrt(V))
+    inp = make_inputs(wl, with_dy=True, with_h0=True, with_dht=True)
+    d = to_device(inp, "float32")
+    f = m2rnn_gates(d["logit"], wl.gate, d["alpha"], d["beta"])
+    B, T, N = wl.B, wl.T, wl.N
+    f32 = torch.float32
+    rc0 = torch.empty((B, N, T, K, V), dtype=f32, device=f.device)
+    y0, HT0, ck0 = m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"], d["H0"], C, rc_out=rc0)
+    y1 = _offset_view((B, T, N, V), f32)
+    HT1 = _offset_view((B, N, K, V), f32)
+    ck1 = _offset_view((B, N, math.ceil(T / C), K, V), f32)
+    rc1 = _offset_view((B, N, T, K, V), f32)
+    nws = m2rnn_workspace_bytes(False, B, T, N, N, K, V, C, f32)
+    ws1 = _offset_view((nws // 4 + 1,), f32)
+    m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"], d["H0"], C, out=(y1, HT1, ck1),
+              rc_out=rc1, workspace=ws1.view(torch.uint8))
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(HT0, HT1) and torch.equal(ck0, ck1)
+    assert torch.equal(rc0, rc1)
+    args = (d["k"], d["v"], d["q"], wl.gate, d["logit"], d["alpha"], d["beta"], f, d["W"],
+            d["w_r"], d["H0"], ck0, C, d["dy"], d["dHT"])
+    g0 = m2rnn_bwd(*args, rc=rc0)
+    out = {"dv": _offset_view((B, T, N, V), f32), "dk": _offset_view((B, T, N, K), f32)}
+    nwb = m2rnn_workspace_bytes(True, B, T, N, N, K, V, C, f32)
+    wsb = _offset_view((nwb // 4 + 1,), f32)
+    g1 = m2rnn_bwd(*args, rc=rc1, out=out, workspace=wsb.view(torch.uint8))
+    g2 = m2rnn_bwd(*args, rc=None, out=None)
+    torch.cuda.synchronize()
+    for name in g0:
+        if g0[name] is not None:
+            assert torch.equal(g0[name], g1[name]), name
+            assert torch.equal(g0[name], g2[name]), name
