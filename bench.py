@@ -94,6 +94,32 @@ def measured_bwd_traffic(workload, C, stored_rc):
     return float(fields["traffic_bytes_per_call"])
 
 
+def stream_bytes(wl):
+    """Algorithmic bytes streamed per call, per the workload's dtypes: forward
+    reads k, q (NQ heads), v, f and writes y; backward reads k, q, v, f, the
+    gate logit and dy and writes dk, dq, dv and dlogit (fp32 gradients).
+    Checkpoints, the optional per-step rc, W and per-head sums are not counted."""
+    in_b = 2 if wl.bf16 else 4
+    tok = wl.B * wl.T
+    kq = 2 * tok * wl.qk_heads * wl.K
+    vv = tok * wl.N * wl.V
+    g = tok * wl.N
+    fwd = (kq + vv) * in_b + 4 * g + 4 * vv
+    bwd = (kq + vv) * in_b + 8 * g + 4 * vv + 4 * (kq + vv + g)
+    return fwd, bwd
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def per_config_fractions(reps=3):
     """Achieved fraction of the fp32 MFMA peak of every workload: the forward
     call alone (no checkpoints) and, for the workloads that define a
@@ -124,11 +150,13 @@ def per_config_fractions(reps=3):
         d = to_device(inp, "float32")
         f = m2rnn_gates(d["logit"], wl.gate, d["alpha"], d["beta"])
         th = wl.B * wl.T * wl.N
+        fb, bb = stream_bytes(wl)
         ms = timed(lambda: m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"], None, 0))
         tf = 2.0 * th * wl.K * wl.V * wl.V / (ms * 1e-3) / 1e12
         row = {"workload": wl.name, "B": wl.B, "T": wl.T, "n_heads": wl.N,
                "qk_heads": wl.qk_heads, "K": wl.K, "V": wl.V,
-               "fwd_ms": ms, "fwd_tflops": tf, "fwd_mfma_frac": tf / MFMA_F32_PEAK_TFLOPS}
+               "fwd_ms": ms, "fwd_tflops": tf, "fwd_mfma_frac": tf / MFMA_F32_PEAK_TFLOPS,
+               "fwd_stream_bytes": fb, "fwd_stream_gbs": fb / (ms * 1e-3) / 1e9}
         if wl.C > 0:
             rc = torch.empty((wl.B, wl.N, wl.T, wl.K, wl.V), dtype=torch.float32, device="cuda")
             _, _, ck = m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"], None, wl.C,
@@ -140,10 +168,13 @@ def per_config_fractions(reps=3):
             ms_rc = timed(lambda: bw(rc))
             fl = 4.0 * th * wl.K * wl.V * wl.V
             tf = fl / (ms * 1e-3) / 1e12
+            rcb = th * wl.K * wl.V * 4
             row.update({"C": wl.C, "bwd_ms": ms, "bwd_tflops": tf,
-                        "bwd_mfma_frac": tf / MFMA_F32_PEAK_TFLOPS, "bwd_stored_rc_ms": ms_rc,
+                        "bwd_mfma_frac": tf / MFMA_F32_PEAK_TFLOPS, "bwd_stream_bytes": bb,
+                        "bwd_stream_gbs": bb / (ms * 1e-3) / 1e9, "bwd_stored_rc_ms": ms_rc,
                         "bwd_stored_rc_mfma_frac": fl / (ms_rc * 1e-3) / 1e12
-                        / MFMA_F32_PEAK_TFLOPS})
+                        / MFMA_F32_PEAK_TFLOPS,
+                        "bwd_stored_rc_stream_gbs": (bb + rcb) / (ms_rc * 1e-3) / 1e9})
             del rc, ck
         rows.append(row)
         del d, f, inp
@@ -345,7 +376,7 @@ def oracle_baseline(wl, target_s):
         pass
     cores = threads or len(os.sched_getaffinity(0))
     return {"value": wl.B * Ts * wl.N / el, "unit": "tokens*heads/s", "cores": int(cores),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"float64 numpy oracle, gates+forward+backward (forward rerun inside the "
                       f"backward), all {wl.B * wl.N} (b,n) units, first {Ts} of {wl.T} steps, "
                       f"{el:.1f} s; {len(os.sched_getaffinity(0))} host cpus visible, "
@@ -425,19 +456,32 @@ def main():
             ev[3].record(stream)
         return g
 
-    def recompute_bwd_ms(reps=3):
-        # the backward that recomputes the states (no rc), on the same checkpoints
-        def run():
+    def recompute_step_ms(reps=3):
+        # the whole step without the per-step rc: the forward stores only the
+        # checkpoints and the backward recomputes the states from them
+        def run(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            m2rnn_gates(d["logit"], wl.gate, d["alpha"], d["beta"], out=f)
+            m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"], None, C, out=(y, HT, ckpt),
+                      workspace=wsf)
+            if ev is not None:
+                ev[1].record(stream)
             m2rnn_bwd(d["k"], d["v"], d["q"], wl.gate, d["logit"], d["alpha"], d["beta"], f,
                       d["W"], d["w_r"], None, ckpt, C, d["dy"], workspace=wsb)
+            if ev is not None:
+                ev[2].record(stream)
         run()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            run()
-        e1.record(stream)
-        stream.synchronize()
-        return e0.elapsed_time(e1) / reps
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for ev in evs:
+            run(ev)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / reps
+        fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        return wall, fwd, bwd
 
     for _ in range(args.warmup):
         step()
@@ -457,7 +501,6 @@ def main():
     ms_step = wall * 1e3 / args.steps
     th = B * T * N
     flops = {"fwd": 2.0 * th * K * V * V, "bwd": 4.0 * th * K * V * V}
-    in_b = 2 if wl.bf16 else 4
     kernels = {}
     for n in names:
         ms = avg_ms[n]
@@ -470,9 +513,14 @@ def main():
             gbs = th * 8 / (ms * 1e-3) / 1e9   # read logit, write f (fp32)
             entry.update({"bound": "hbm", "achieved_gbs": gbs, "frac": gbs / HBM_PEAK_GBS})
         kernels[n] = entry
-    # streamed bytes of the forward call: k, q, v, f in; y (and rc) out
-    fwd_bytes = th * ((2 * K + V) * in_b + 4 + 4 * V + (4 * K * V if rc is not None else 0))
-    kernels["fwd"]["stream_gbs"] = fwd_bytes / (avg_ms["fwd"] * 1e-3) / 1e9
+    # streamed bytes of each call (stream_bytes), plus the per-step rc written by
+    # the forward and read by the backward when it is stored
+    fb, bb = stream_bytes(wl)
+    rcb = th * K * V * 4 if rc is not None else 0
+    kernels["fwd"]["stream_bytes"] = fb + rcb
+    kernels["fwd"]["stream_gbs"] = (fb + rcb) / (avg_ms["fwd"] * 1e-3) / 1e9
+    kernels["bwd"]["stream_bytes"] = bb + rcb
+    kernels["bwd"]["stream_gbs"] = (bb + rcb) / (avg_ms["bwd"] * 1e-3) / 1e9
     dom = max(("fwd", "bwd"), key=lambda n: avg_ms[n])
     dom_tf = kernels[dom]["achieved_tflops"]
     out = {
@@ -493,6 +541,8 @@ def main():
                    "C": C, "kvq_dtype": "bf16" if wl.bf16 else "f32", "state_dtype": "f32",
                    "gate": "exp_softplus" if wl.gate == 1 else "sigmoid",
                    "backward_states": "recomputed" if rc is None else "stored rc",
+                   "ckpt_bytes": int(ckpt.numel() * 4),
+                   "rc_bytes": 0 if rc is None else int(rc.numel() * 4),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": f"m2rnn_{dom} (whole call)", "achieved": dom_tf,
                      "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -506,9 +556,15 @@ def main():
         "kernels": kernels,
     }
     if rc is not None:
-        ms = recompute_bwd_ms()
-        out["bwd_recompute"] = {"ms": ms, "mfma_frac": flops["bwd"] / (ms * 1e-3) / 1e12
-                                / MFMA_F32_PEAK_TFLOPS}
+        # the same step with no per-step rc (checkpoints only, states recomputed)
+        wall, fms, bms = recompute_step_ms()
+        out["recompute_step"] = {
+            "ms_per_step": wall, "tokens_heads_per_s": th / (wall * 1e-3),
+            "fwd_ms": fms, "bwd_ms": bms,
+            "fwd_mfma_frac": flops["fwd"] / (fms * 1e-3) / 1e12 / MFMA_F32_PEAK_TFLOPS,
+            "bwd_mfma_frac": flops["bwd"] / (bms * 1e-3) / 1e12 / MFMA_F32_PEAK_TFLOPS,
+            "ckpt_bytes": int(ckpt.numel() * 4), "rc_bytes": 0}
+        out["bwd_recompute"] = {"ms": bms, "mfma_frac": out["recompute_step"]["bwd_mfma_frac"]}
     if not args.no_per_config:
         out["per_config"] = per_config_fractions()
         out["decode"] = decode_rates()
