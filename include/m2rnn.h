@@ -17,8 +17,9 @@
  * ---------------------------------------
  * - Every tensor pointer is DEVICE memory owned by the caller, C-contiguous,
  *   in the layout stated next to it, aligned to its element type.  The library
- *   allocates nothing; between calls it keeps only a per-device cache of one
- *   occupancy query (m2rnn_step; atomic, so concurrent host threads are safe).
+ *   allocates nothing; between calls it keeps only per-device caches of one
+ *   occupancy query (m2rnn_step) and of its scratch array's address
+ *   (m2rnn_bwd_noalloc), both atomic, so concurrent host threads are safe.
  *   Calls are asynchronous on `stream` (a hipStream_t, NULL = the default
  *   stream) and never synchronise the device.
  * - Wider (16-byte) memory accesses are used where an array's address and row
@@ -68,8 +69,12 @@ typedef enum {
   M2RNN_ERR_INVALID_ARG = 1, /* bad size, NULL pointer, bad enum, missing/extra gate parameters */
   M2RNN_ERR_UNSUPPORTED = 2, /* K > 256, V > 128, or an unsupported dtype pairing */
   M2RNN_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than the *_workspace_bytes query */
-  M2RNN_ERR_HIP = 4          /* a kernel launch failed */
+  M2RNN_ERR_HIP = 4,         /* a kernel launch failed */
+  M2RNN_ERR_SCRATCH = 5      /* m2rnn_bwd_noalloc: the call needs more than the static scratch */
 } m2rnn_status;
+
+/* Bytes of the static per-device scratch that m2rnn_bwd_noalloc works in. */
+#define M2RNN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 typedef enum { M2RNN_F32 = 0, M2RNN_BF16 = 1, M2RNN_F64 = 2 } m2rnn_dtype;
 
@@ -170,6 +175,31 @@ int m2rnn_bwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K
               int64_t C, const void* rc, const void* dy, const void* dHT, void* dk, void* dv,
               void* dq, void* dlogit, void* dW, void* dw_r, void* dalpha, void* dbeta,
               void* dH0, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * m2rnn_bwd_noalloc -- m2rnn_bwd for callers that cannot allocate device
+ * memory or pass a workspace: code being captured into a HIP graph, tight
+ * serving or training loops, harnesses that forbid hipMalloc.  Same arguments,
+ * results and checks as m2rnn_bwd, without workspace / workspace_bytes: the
+ * kernels work in a fixed array of M2RNN_NOALLOC_SCRATCH_BYTES (64 MiB) that
+ * the library holds on each device it runs on until the process ends.  A call
+ * whose workspace (m2rnn_workspace_bytes(1, ...)) exceeds that returns
+ * M2RNN_ERR_SCRATCH and launches nothing.  The call allocates nothing; its
+ * first call on a device looks up that device's array address.  `stream` must
+ * belong to the calling thread's current device (else M2RNN_ERR_INVALID_ARG).
+ * Every call on a device shares that device's array and leaves its partial
+ * sums there (the kernels write every element they read, so nothing needs
+ * clearing): calls that may overlap on one device -- on different streams, or
+ * from different host threads -- race and must be serialised by the caller.
+ */
+int m2rnn_bwd_noalloc(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K,
+                      int64_t V, int in_dtype, int state_dtype, const void* k, const void* v,
+                      const void* q, int gate_kind, const void* logit, const void* alpha,
+                      const void* beta, const void* f, const void* W, const void* w_r,
+                      const void* H0, const void* ckpt, int64_t C, const void* rc,
+                      const void* dy, const void* dHT, void* dk, void* dv, void* dq,
+                      void* dlogit, void* dW, void* dw_r, void* dalpha, void* dbeta, void* dH0,
+                      void* stream);
 
 /*
  * m2rnn_step -- one token of every sequence (decoding): the state is updated in

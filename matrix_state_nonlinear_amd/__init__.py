@@ -12,3 +12,4 @@ from .ops import (m2rnn_conv_silu, m2rnn_conv_silu_bwd, m2rnn_gate_rmsnorm,  # n
 from .ops import (m2rnn_bwd, m2rnn_fwd, m2rnn_gates, m2rnn_step, m2rnn_workspace_bytes,  # noqa: F401
                   m2rnn_status_string)
 from .ops import m2rnn_newton_fwd, m2rnn_newton_workspace_bytes  # noqa: F401
+from .ops import m2rnn_bwd_noalloc  # noqa: F401

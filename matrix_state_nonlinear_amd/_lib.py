@@ -16,6 +16,8 @@ M2RNN_ERR_INVALID_ARG = 1
 M2RNN_ERR_UNSUPPORTED = 2
 M2RNN_ERR_WORKSPACE = 3
 M2RNN_ERR_HIP = 4
+M2RNN_ERR_SCRATCH = 5
+NOALLOC_SCRATCH_BYTES = 64 << 20   # M2RNN_NOALLOC_SCRATCH_BYTES
 
 M2RNN_F32 = 0
 M2RNN_BF16 = 1
@@ -37,6 +39,10 @@ SIGNATURES = {
                          _vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                          _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                          _vp, _sz, _vp]),
+    "m2rnn_bwd_noalloc": (_int, [_i64, _i64, _i64, _i64, _i64, _i64, _int, _int,
+                                 _vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _vp]),
     "m2rnn_step": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int,
                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "m2rnn_newton_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _int]),

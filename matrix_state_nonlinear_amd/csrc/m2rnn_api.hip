@@ -3,6 +3,8 @@
 
 #include <limits.h>
 
+#include <atomic>
+
 #include "../../include/m2rnn.h"
 #include "m2rnn_internal.h"
 #include "m2rnn_newton_internal.h"
@@ -109,7 +111,7 @@ bool newton_supported(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V) {
   return waves < 2.0e9 && map_waves < 2.0e9 && U * (double)T * (double)K * (double)V < 4.0e18;
 }
 
-// The argument checks of m2rnn_bwd, before any
+// The argument checks of m2rnn_bwd and m2rnn_bwd_noalloc, before any
 // workspace: M2RNN_OK or the status to return.
 int bwd_check(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K, int64_t V,
               int in_dtype, int state_dtype, const void* k, const void* v, const void* q,
@@ -140,6 +142,33 @@ int bwd_check(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K
   return M2RNN_OK;
 }
 
+// Workspace of m2rnn_bwd_noalloc: one fixed array per device, held until the
+// process ends.  Host code never uses the array's name as an address (on the
+// host it names a stand-in): the device address comes from
+// hipGetSymbolAddress, once per device, and is passed to the kernels like any
+// workspace.
+constexpr size_t kScratchBytes = M2RNN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) __attribute__((used)) unsigned char scratch[kScratchBytes];
+
+constexpr int kScratchDevices = 64;
+std::atomic<void*> scratch_ptr[kScratchDevices];
+
+// Device address of `scratch` on device `dev` (the current device), looked
+// up on the first call there.  Concurrent first calls look it up alike and
+// store the same address.
+hipError_t scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -151,6 +180,8 @@ const char* m2rnn_status_string(int status) {
     case M2RNN_ERR_UNSUPPORTED: return "M2RNN_ERR_UNSUPPORTED: K > 256, V > 128 or dtype pairing";
     case M2RNN_ERR_WORKSPACE: return "M2RNN_ERR_WORKSPACE: workspace missing or too small";
     case M2RNN_ERR_HIP: return "M2RNN_ERR_HIP: kernel launch failed";
+    case M2RNN_ERR_SCRATCH:
+      return "M2RNN_ERR_SCRATCH: the call needs more workspace than the static scratch holds";
     default: return "M2RNN: unknown status";
   }
 }
@@ -246,6 +277,34 @@ int m2rnn_bwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K
   a.nslab = (int)num_slabs(K);
   a.gate_kind = gate_kind;
   return status_of(launch_bwd(a, in_dtype, state_dtype, (hipStream_t)stream));
+}
+
+int m2rnn_bwd_noalloc(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K,
+                      int64_t V, int in_dtype, int state_dtype, const void* k, const void* v,
+                      const void* q, int gate_kind, const void* logit, const void* alpha,
+                      const void* beta, const void* f, const void* W, const void* w_r,
+                      const void* H0, const void* ckpt, int64_t C, const void* rc,
+                      const void* dy, const void* dHT, void* dk, void* dv, void* dq,
+                      void* dlogit, void* dW, void* dw_r, void* dalpha, void* dbeta, void* dH0,
+                      void* stream) {
+  const int chk = bwd_check(B, T, n_heads, qk_heads, K, V, in_dtype, state_dtype, k, v, q,
+                            gate_kind, logit, alpha, beta, f, W, w_r, ckpt, C, dy, dk, dv, dq,
+                            dlogit, dW, dw_r, dalpha, dbeta);
+  if (chk != M2RNN_OK) return chk;
+  const size_t need = bwd_ws_bytes(B, T, n_heads, qk_heads, K, V, C, state_dtype);
+  if (B * T * n_heads != 0 && need > kScratchBytes) return M2RNN_ERR_SCRATCH;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return M2RNN_ERR_HIP;
+  if (stream) {  // the scratch address is the current device's
+    int sdev = -1;
+    if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess) return M2RNN_ERR_HIP;
+    if (sdev != dev) return M2RNN_ERR_INVALID_ARG;
+  }
+  void* ws = nullptr;
+  if (scratch_address(dev, &ws) != hipSuccess) return M2RNN_ERR_HIP;
+  return m2rnn_bwd(B, T, n_heads, qk_heads, K, V, in_dtype, state_dtype, k, v, q, gate_kind,
+                   logit, alpha, beta, f, W, w_r, H0, ckpt, C, rc, dy, dHT, dk, dv, dq, dlogit,
+                   dW, dw_r, dalpha, dbeta, dH0, ws, kScratchBytes, stream);
 }
 
 size_t m2rnn_newton_workspace_bytes(int64_t B, int64_t T, int64_t n_heads, int64_t K, int64_t V,

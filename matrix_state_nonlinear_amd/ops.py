@@ -186,7 +186,7 @@ def _bwd_outputs(k, v, q, gate_kind, logit, alpha, beta, f, W, w_r, H0, ckpt, C,
 
 
 def _bwd_args(k, v, q, gate_kind, logit, alpha, beta, f, W, w_r, H0, ckpt, C, rc, dy, dHT, o):
-    """The pointer arguments of the backward entry points, in ABI order
+    """The pointer arguments shared by m2rnn_bwd and m2rnn_bwd_noalloc, in ABI order
     from k to dH0."""
     return (_ptr(k), _ptr(v), _ptr(q), int(gate_kind), _ptr(logit), _ptr(alpha), _ptr(beta),
             _ptr(f), _ptr(W), _ptr(w_r), _ptr(H0), _ptr(ckpt), int(C), _ptr(rc), _ptr(dy),
@@ -212,6 +212,22 @@ def m2rnn_bwd(k, v, q, gate_kind: int, logit, alpha, beta, f, W, w_r, H0, ckpt, 
         *_bwd_args(k, v, q, gate_kind, logit, alpha, beta, f, W, w_r, H0, ckpt, C, rc, dy, dHT, o),
         _ptr(ws), wsb, _stream(dev))
     check(st, "m2rnn_bwd")
+    return o
+
+
+def m2rnn_bwd_noalloc(k, v, q, gate_kind: int, logit, alpha, beta, f, W, w_r, H0, ckpt, C: int,
+                      dy, dHT=None, want_dh0: bool = True, rc=None, out=None):
+    """m2rnn_bwd without a workspace: the library's static per-device scratch
+    (NOALLOC_SCRATCH_BYTES) holds the partial sums.  With every gradient buffer
+    given in ``out``, nothing is allocated.  Calls that may overlap on one
+    device share the scratch and race."""
+    B, T, N, NQ, K, V, sd, o = _bwd_outputs(k, v, q, gate_kind, logit, alpha, beta, f, W, w_r,
+                                            H0, ckpt, C, dy, dHT, want_dh0, rc, out)
+    st = _lib.lib().m2rnn_bwd_noalloc(
+        B, T, N, NQ, K, V, _DT[k.dtype], _DT[sd],
+        *_bwd_args(k, v, q, gate_kind, logit, alpha, beta, f, W, w_r, H0, ckpt, C, rc, dy, dHT, o),
+        _stream(k.device))
+    check(st, "m2rnn_bwd_noalloc")
     return o
 
 

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in range(5):
+    for s in range(6):
         assert _lib.status_string(s).startswith("M2RNN")
     assert "unknown" in _lib.status_string(99)
 
@@ -174,6 +174,35 @@ def test_bwd_rejects_bad_arguments(L):
     assert bwd(L, V=200) == E.M2RNN_ERR_UNSUPPORTED
     assert bwd(L) == E.M2RNN_ERR_WORKSPACE                             # always needs workspace
     assert bwd(L, ws=FAKE, wsb=64) == E.M2RNN_ERR_WORKSPACE
+
+
+def test_bwd_noalloc_checks_before_touching_the_device(L):
+    # the argument checks of m2rnn_bwd, then the scratch limit, all on the host
+    # (no GPU here: a call that got past them would fail with M2RNN_ERR_HIP)
+    E = _lib
+
+    def na(**kw):
+        a = dict(B=2, T=8, N=1, NQ=None, K=16, V=16, ind=E.M2RNN_F32, sd=E.M2RNN_F32, k=FAKE,
+                 v=FAKE, q=FAKE, gate=E.M2RNN_GATE_SIGMOID, logit=FAKE, alpha=None, beta=None,
+                 f=FAKE, W=FAKE, w_r=FAKE, H0=None, ckpt=FAKE, C=4, rc=None, dy=FAKE, dHT=None,
+                 dk=FAKE, dv=FAKE, dq=FAKE, dlogit=FAKE, dW=FAKE, dw_r=FAKE, dalpha=None,
+                 dbeta=None, dH0=None, stream=None)
+        a.update(kw)
+        if a["NQ"] is None:
+            a["NQ"] = a["N"]
+        keys = ["B", "T", "N", "NQ", "K", "V", "ind", "sd", "k", "v", "q", "gate", "logit",
+                "alpha", "beta", "f", "W", "w_r", "H0", "ckpt", "C", "rc", "dy", "dHT", "dk",
+                "dv", "dq", "dlogit", "dW", "dw_r", "dalpha", "dbeta", "dH0", "stream"]
+        return L.m2rnn_bwd_noalloc(*[a[k] for k in keys])
+
+    assert na(C=0) == E.M2RNN_ERR_INVALID_ARG
+    assert na(dy=None) == E.M2RNN_ERR_INVALID_ARG
+    assert na(alpha=FAKE) == E.M2RNN_ERR_INVALID_ARG
+    assert na(V=200) == E.M2RNN_ERR_UNSUPPORTED
+    big = dict(B=1, T=4096, N=16, K=48, V=128, C=64)
+    need = L.m2rnn_workspace_bytes(1, 1, 4096, 16, 16, 48, 128, 64, E.M2RNN_F32)
+    assert need > E.NOALLOC_SCRATCH_BYTES
+    assert na(**big) == E.M2RNN_ERR_SCRATCH
 
 
 def step(L, **kw):
