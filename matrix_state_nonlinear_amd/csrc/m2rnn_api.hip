@@ -68,9 +68,11 @@ size_t fwd_ws_bytes(int64_t B, int64_t T, int64_t N, int64_t K, int64_t V, int s
                   256);
 }
 
+// The larger of the two backward modes' layouts (recomputing needs the rc ring
+// as well when the main kernel sweeps the intervals), so one size serves both.
 size_t bwd_ws_bytes(int64_t B, int64_t T, int64_t N, int64_t NQ, int64_t K, int64_t V,
                     int64_t C, int state_dtype) {
-  const BwdWorkspace L = bwd_workspace_layout(B, T, N, NQ, K, V, C, state_dtype);
+  const BwdWorkspace L = bwd_workspace_layout(B, T, N, NQ, K, V, C, state_dtype, false);
   return align_up(L.total_elems * real_size(state_dtype), 256);
 }
 
@@ -267,6 +269,7 @@ int m2rnn_bwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K
   }
   const size_t need = bwd_ws_bytes(B, T, n_heads, qk_heads, K, V, C, state_dtype);
   if (need && (!workspace || workspace_bytes < need)) return M2RNN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return M2RNN_ERR_INVALID_ARG;
   BwdArgs a{};
   a.k = k; a.v = v; a.q = q; a.logit = logit; a.alpha = alpha; a.beta = beta; a.f = f;
   a.W = W; a.w_r = w_r; a.H0 = H0; a.ckpt = ckpt; a.rc = rc; a.dy = dy; a.dHT = dHT;

@@ -51,6 +51,7 @@
 // (the accumulators are pinned right after the chain): behind a branch, the
 // compiler did not insert the wait states such a read needs.
 
+#include <type_traits>
 #include <utility>
 
 #include "m2rnn_device.h"
@@ -123,6 +124,7 @@ struct BwdSmem {
   Real rq[2][16][4];               // dq per-wave row sums [row][wave] (at most 4 waves)
   Real rk[2][16][20];              // dk lane partials [row][wave, lane group] (rows of 20)
   Real rf[2][4 * Tr::NW];          // df partials [wave, lane group]
+  Real wr[Tr::VP];                 // w_r of the head (interval sweep: dv's value-residual term)
 };
 
 int bwd_period(int state_dtype, int64_t V) {
@@ -139,12 +141,14 @@ int bwd_period(int state_dtype, int64_t V) {
 }
 
 BwdWorkspace bwd_workspace_layout(int64_t B, int64_t T, int64_t N, int64_t NQ, int64_t K,
-                                  int64_t V, int64_t C, int state_dtype) {
+                                  int64_t V, int64_t C, int state_dtype, bool stored_rc) {
   BwdWorkspace L{};
   const int64_t ns = num_slabs(K);
   L.period = bwd_period(state_dtype, V);
   L.nch = (T + L.period - 1) / L.period;
-  L.subck_needed = (L.period % C) != 0;
+  // (one-step chunks, the fp64 state at V > 96 only, keep the chunk-start pass)
+  L.sweep = L.period >= 2 && C > L.period && C % L.period == 0 && C <= kMaxSweepInterval;
+  L.subck_needed = (L.period % C) != 0 && !L.sweep;
   const int64_t rows = B * T;
   L.row_blocks = (rows + 255) / 256;
   size_t off = 0;
@@ -154,6 +158,9 @@ BwdWorkspace bwd_workspace_layout(int64_t B, int64_t T, int64_t N, int64_t NQ, i
     return at;
   };
   L.subck = take(L.subck_needed ? (size_t)B * N * L.nch * K * V : 0);
+  const size_t ring = L.sweep ? (size_t)B * N * ns * 2 * C * 16 * (16 * value_tiles(V)) : 0;
+  L.ring_s = take(ring);
+  L.ring_r = take(stored_rc ? 0 : ring);
   L.dv_part = take(ns > 1 ? (size_t)ns * B * T * N * V : 0);
   L.df_part = take((size_t)ns * B * T * N);
   L.dW_part = take((size_t)B * ns * N * V * V);
@@ -169,7 +176,7 @@ BwdWorkspace bwd_workspace_layout(int64_t B, int64_t T, int64_t N, int64_t NQ, i
 // and every column of the tiles exists and the state is fp32 (the launcher
 // checks), so the per-step row and column guards and the scalar fallbacks of the
 // rc loads and dv stores are compiled out.
-template <typename InT, typename Real, int VT, bool RC, bool FULL>
+template <typename InT, typename Real, int VT, bool RC, bool FULL, bool SW>
 __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
     m2rnn_bwd_kernel(BwdArgs a, BwdWorkspace L) {
   using Tr = BwdTraits<Real, VT>;
@@ -214,6 +221,396 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
   auto ractive = [&](int j) { return j >= S + 1 && j <= nch * S + S; };
 
   if (role == 0) {
+    if constexpr (SW) {
+    // ======================================================= forward role, interval sweep
+    // Checkpoint intervals of C steps (C a multiple of S) are swept forward in time
+    // once, one interval ahead of the reverse role: from the interval's checkpoint,
+    // the recurrence (MFMA, or the interpolation from the stored rc) produces every
+    // S_{x+1} (and rc_x), which this lane stores at its own positions of the unit's
+    // ring (two interval slots).  The chunk the reverse role takes next is filled
+    // into the LDS rings from there, so no chunk start is ever needed.  Each ring
+    // element is written and read back by the same lane.  The first C / S periods
+    // (one more with one-step chunks) only sweep (the last interval); after them
+    // the sweep runs C / S chunks ahead of the fill, so it finishes each interval before the fill reaches it and
+    // starts interval i - 2 (the same slot as i) only after the fill has left i.
+    const int Ci = (int)a.C;
+    const int CS = Ci / S;                      // chunks per interval
+    const int J = (T32 + Ci - 1) / Ci;          // intervals (= checkpoints)
+    const int n_last = nch - (J - 1) * CS;      // chunks of the last interval
+    // sweep-only periods; one more with one-step chunks, where the fill loads the
+    // next chunk's first step in the phase that would sweep it
+    const int P0 = CS + (S == 1 ? 1 : 0);
+    const int64_t KV = K * V;
+    const int64_t nck = J;
+    // W^T as the A operand, rotated and scaled exactly as in the forward kernel
+    Real wop[RC ? 1 : TPW][RC ? 1 : NS];
+    if constexpr (!RC) {
+#pragma unroll
+      for (int p = 0; p < TPW; ++p) {
+        const int col = (wr * TPW + p) * 16 + li;
+#pragma unroll
+        for (int s0 = 0; s0 < NS; ++s0) {
+          const int s = (s0 + 4 * TPW * wr) % NS;
+          const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
+          wop[p][s0] = Wp[((int64_t)n * V + (l < V ? l : 0)) * V + (col < V ? col : 0)];
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < TPW; ++p) {
+        const int col = (wr * TPW + p) * 16 + li;
+#pragma unroll
+        for (int s0 = 0; s0 < NS; s0 += 4) pin_values(wop[p][s0], wop[p][s0 + 1], wop[p][s0 + 2], wop[p][s0 + 3]);
+#pragma unroll
+        for (int s0 = 0; s0 < NS; ++s0) {
+          const int s = (s0 + 4 * TPW * wr) % NS;
+          const int l = 16 * (s >> 2) + acc_m<Real>(g, s & 3);
+          wop[p][s0] = (col < V && l < V) ? kTanhScale<Real> * wop[p][s0] : Real(0);
+        }
+#pragma unroll
+        for (int s0 = 0; s0 < NS; s0 += 4) pin_values(wop[p][s0], wop[p][s0 + 1], wop[p][s0 + 2], wop[p][s0 + 3]);
+      }
+    }
+    // w_r of the head in LDS (read by dv's value-residual term when the slab is the
+    // whole head), so that it holds no registers through the step loop
+    for (int c = wr * 64 + lane; c < VP; c += NW * 64)
+      sm.wr[c] = c < V ? ((const Real*)a.w_r)[(int64_t)n * V + c] : Real(0);
+    const bool dv_vec = sizeof(Real) == 4 && (FULL || a.dv_vec);
+    Real* const dq_row = dq_base + tok0 * K + row;
+    Real* const dv_tok = nslab == 1 ? (Real*)a.dv + tok0 * V
+                                    : (Real*)a.ws + L.dv_part + ((int64_t)slab * B * T * N + tok0) * V;
+    const int64_t NK = N * K, NV = N * V;
+    bool colv[TPW][4];  // this lane's columns exist
+#pragma unroll
+    for (int p = 0; p < TPW; ++p)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) colv[p][r] = FULL || (row_ok && col_of(p, r) < V);
+
+    // the unit's ring, in R4 units: [slot][position][tile][lane]; step t of
+    // interval t / C sits in slot (t / C) & 1 at position t mod C
+    const size_t ring_unit = (size_t)unit * 2 * Ci * VT * 64;
+    R4* const rs = (R4*)a.ring_s + ring_unit + wr * TPW * 64 + lane;
+    R4* const rr = RC ? nullptr : (R4*)a.ring_r + ring_unit + wr * TPW * 64 + lane;
+    auto rix = [&](int t) __attribute__((always_inline)) -> size_t {
+      const int i = t / Ci;
+      return ((size_t)((i & 1) * Ci + (t - i * Ci)) * VT) * 64;
+    };
+
+    // ---- sweep inputs of step x, loaded one step ahead (clamped to T - 1;
+    // steps past T have f = 1, which keeps the state exactly)
+    struct SwIn {
+      InT k;
+      InT v[TPW][4];
+      Real f;          // gate of the step (lane-dependent address, read from lane 0)
+      R4 rc[TPW];      // stored rc (RC only)
+    };
+    const InT* __restrict__ kp = (const InT*)a.k;
+    const InT* __restrict__ vp = (const InT*)a.v;
+    const Real* __restrict__ fpp = (const Real*)a.f;
+    const Real* rc_lane = RC ? (const Real*)a.rc + ((int64_t)bn * T * K + (row_ok ? row : 0)) * V
+                             : nullptr;
+    const bool rc_vec = sizeof(Real) == 4 && (FULL || a.rc_vec);
+    auto load_sw = [&](int x, SwIn& in) __attribute__((always_inline)) {
+      const int xc = x < T32 ? x : T32 - 1;
+      // gates of steps xc and xc + 1 in alternate lanes: a lane-dependent address
+      int xf = xc + (lane & 1);
+      if (xf > T32 - 1) xf = T32 - 1;
+      in.f = fpp[tok0 + (int64_t)xf * N];
+      if constexpr (RC) {
+        const Real* src = rc_lane + (int64_t)xc * KV;
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) {
+          if (rc_vec) {
+            const int c0 = col_of(p, 0);
+            in.rc[p] = *(const R4*)(src + (FULL || c0 < V ? c0 : 0));
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int col = col_of(p, r);
+              in.rc[p][r] = src[col < V ? col : 0];
+            }
+          }
+        }
+      } else {
+        in.k = kp[(tokq0 + (int64_t)xc * NQ) * K + (row_ok ? row : 0)];
+        const InT* vsrc = vp + (tok0 + (int64_t)xc * N) * V;
+#pragma unroll
+        for (int p = 0; p < TPW; ++p)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int col = col_of(p, r);
+            in.v[p][r] = vsrc[col < V ? col : 0];
+          }
+      }
+    };
+    // a raw input converted in a register (kept there before any select)
+    auto held = [&](auto x) __attribute__((always_inline)) -> Real {
+      Real y = (Real)widen(x);
+      asm volatile("" : "+v"(y));
+      return y;
+    };
+
+    // ---- sweep state: own tiles hs (row `row`, columns col_of(p, r)).  An interval
+    // starts from its checkpoint: the own tiles are loaded one sweep step ahead (ckn)
+    // and, when recomputing, published through the exchange buffer in place of the
+    // previous step's state, so every step reads the other tiles of its B operand
+    // from there
+    R4 hs[TPW], ckn[TPW];
+    auto load_ck = [&](int i) __attribute__((always_inline)) {
+      // the checkpoint H_{iC}, own tiles, from clamped addresses (masked on use)
+      const Real* ck = (const Real*)a.ckpt + (((int64_t)bn * nck + i) * K + (row_ok ? row : 0)) * V;
+#pragma unroll
+      for (int p = 0; p < TPW; ++p)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int col = col_of(p, r);
+          ckn[p][r] = ck[col < V ? col : 0];
+        }
+    };
+    auto take_ck = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int p = 0; p < TPW; ++p) {
+        R4 c = ckn[p];
+        pin_vec(c);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hs[p][r] = colv[p][r] ? c[r] : Real(0);
+      }
+    };
+    // The sweep's position: chunk number s of the sweep order (the intervals from
+    // the last to the first, each one's chunks forward in time) -> its first step.
+    auto sweep_chunk = [&](int s) __attribute__((always_inline)) -> int {
+      if (s < n_last) return ((J - 1) * CS + s) * S;
+      const int m = (s - n_last) / CS, r = (s - n_last) - m * CS;
+      return ((J - 2 - m) * CS + r) * S;
+    };
+    SwIn swc;  // the sweep step's inputs (loaded during the previous step)
+    // one sweep step x (phase parity par); nx: the sweep's next step, or -1
+    auto sweep_step = [&](int par, int x, int nx) __attribute__((always_inline)) {
+      // the next step starts an interval: load its checkpoint now (taken at the end)
+      if (nx >= 0 && nx % Ci == 0) load_ck(nx / Ci);
+      const Real f = x < T32 ? lane_value_r(swc.f, 0) : Real(1);
+      const Real omf = Real(1) - f;
+      const Real m2omf = Real(-2) * omf;
+      R4 rcv[TPW];
+      if constexpr (RC) {
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) {
+          R4 rc = swc.rc[p];
+          pin_vec(rc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) rc[r] = colv[p][r] ? rc[r] : Real(0.5);
+          rcv[p] = rc;
+        }
+        if (nx >= 0) load_sw(nx, swc);  // the inputs are consumed: load the next step's
+      } else {
+        // the scaled rank-1 write k v^T starts the accumulators, as in the forward kernel
+        const Real kk = held(swc.k);
+        const Real ks = kTanhScale<Real> * (row_ok ? kk : Real(0));
+        R4 acc[TPW];
+#pragma unroll
+        for (int p = 0; p < TPW; ++p)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const Real vv = held(swc.v[p][r]);
+            acc[p][r] = ks * (col_of(p, r) < V ? vv : Real(0));
+          }
+        if (nx >= 0) load_sw(nx, swc);  // the inputs are consumed: load the next step's
+        // H W over the slab: the own tiles from registers (or the interval's start
+        // state), then the others from the exchange of the previous sweep step, one
+        // 16-byte LDS read per tile just ahead of its MFMAs
+#pragma unroll
+        for (int q0 = 0; q0 < VT; ++q0) {
+          const R4 t4 = q0 < TPW ? hs[q0] : sm.ck[par ^ 1][(q0 + TPW * wr) % VT][lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x4(wop[p][4 * q0 + r], t4[r], acc[p]);
+        }
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) pin_vec(acc[p]);
+#pragma unroll
+        for (int p = 0; p < TPW; ++p)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) rcv[p][r] = tanh_rc_scaled(acc[p][r]);
+      }
+      const size_t ix = rix(x);
+#pragma unroll
+      for (int p = 0; p < TPW; ++p) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hs[p][r] = fma_r(m2omf, rcv[p][r], fma_r(f, hs[p][r], omf));
+        if constexpr (!RC) rr[ix + p * 64] = rcv[p];
+        rs[ix + p * 64] = hs[p];
+      }
+      // the next step starts an interval: its state is that interval's checkpoint
+      if (nx >= 0 && nx % Ci == 0) take_ck();
+      if constexpr (!RC) {
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) sm.ck[par][wr * TPW + p][lane] = hs[p];
+      }
+    };
+
+    // ---- fill of the LDS rings for the chunk the reverse role takes next:
+    // S_{t+1} and rc_t of step t, loaded one phase ahead
+    R4 fS[TPW], fR[TPW];
+    auto load_fill = [&](int t) __attribute__((always_inline)) {
+      const size_t ix = rix(t);
+#pragma unroll
+      for (int p = 0; p < TPW; ++p) fS[p] = rs[ix + p * 64];
+      if constexpr (RC) {
+        const Real* src = rc_lane + (int64_t)(t < T32 ? t : T32 - 1) * KV;
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) {
+          if (rc_vec) {
+            const int c0 = col_of(p, 0);
+            fR[p] = *(const R4*)(src + (FULL || c0 < V ? c0 : 0));
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int col = col_of(p, r);
+              fR[p][r] = src[col < V ? col : 0];
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) fR[p] = rr[ix + p * 64];
+      }
+    };
+
+    // the sweep's first step: the last interval, from its checkpoint (published for
+    // the first step's B operand as the previous step's state would be)
+    load_sw(sweep_chunk(0), swc);
+    load_ck(J - 1);
+    take_ck();
+    if constexpr (!RC) {
+#pragma unroll
+      for (int p = 0; p < TPW; ++p) sm.ck[1][wr * TPW + p][lane] = hs[p];
+    }
+
+    __syncthreads();  // prologue staging by the side role
+
+    auto sweep_phase = [&](int kt, int I, int jpar) __attribute__((always_inline)) {
+      // sweep chunk kt (if any), its step I; the next step is the same chunk's
+      // I + 1 or the next sweep chunk's first
+      if (kt >= nch) return;
+      const int x = sweep_chunk(kt) + I;
+      const int nx = I + 1 < S ? x + 1 : (kt + 1 < nch ? sweep_chunk(kt + 1) : -1);
+      sweep_step(jpar, x, nx);
+    };
+    // prologue: the last interval's sweep (and the following chunks up to P0)
+    for (int kt = 0; kt < P0; ++kt) {
+      for (int I = 0; I < S; ++I) {
+        sweep_phase(kt, I, (kt * S + I) & 1);
+        __syncthreads();
+      }
+    }
+    if (nch > 0) load_fill((nch - 1) * S);
+
+    auto phase = [&](auto Ic, int k, int cF, bool rec, int slot, int hbase, int slotA, int slotB,
+                     int slotC) {
+      constexpr int I = decltype(Ic)::value;
+      const int j = k * S + I;
+      const int jp = j & 1;
+      const int kt = P0 + k;
+      if (rec) {
+        // the step t = cF S + I of the chunk: S_{t+1} and rc_t from the ring
+        const Real* stp = &sm.st[slot][I * E];
+        R4 s1[TPW], r1[TPW];
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) {
+          s1[p] = fS[p];
+          r1[p] = fR[p];
+          pin_vec(s1[p]);
+          pin_vec(r1[p]);
+          // padding rows and columns take rc = 1/2, as the recomputation gives them
+#pragma unroll
+          for (int r = 0; r < 4; ++r) r1[p][r] = colv[p][r] ? r1[p][r] : Real(0.5);
+        }
+        if (I + 1 < S || cF >= 1) load_fill(I + 1 < S ? cF * S + I + 1 : (cF - 1) * S);
+        Real dqp = 0;
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) {
+          sm.hr[(hbase + I + 1) & (M - 1)][wr * TPW + p][lane] = s1[p];
+          sm.zr[hbase + I][wr * TPW + p][lane] = r1[p];
+          const R4 u = cols4(stp + OFF_U + (wr * TPW + p) * 16, g);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dqp = fma_r(s1[p][r], u[r], dqp);
+        }
+        dqp = cross_row_sum(dqp);
+        if (g == 0) sm.rq[jp][li][wr] = dqp;
+      }
+      // the sweep, C / S chunks ahead of the fill
+      sweep_phase(kt, I, (P0 * S + j) & 1);
+      // dq of the previous phase's step: the per-wave sums, added by wave 0
+      if (wr == 0 && g == 0 && (FULL || row_ok) && j >= 1 && j <= nch * S) {
+        const int tf = I > 0 ? cF * S + I - 1 : cF * S + 2 * S - 1;
+        if (tf < T32) {
+          Real sq = 0;
+#pragma unroll
+          for (int i = 0; i < NW; ++i) sq += sm.rq[jp ^ 1][li][i];
+          dq_row[(int64_t)tf * NK] = sq;
+        }
+      }
+      // dv of the reverse role's step of phase j - 1 (as in the recomputing role)
+      if (ractive(j - 1)) {
+        const int tp = (cF + 2) * S - I + 1;
+        if (tp < T32) {
+          constexpr int tq = (1 - I + S) % S;
+          const Real* stq = &sm.st[S == 1 ? slotC : (I <= 1 ? slotB : slotA)][tq * E];
+          const Real kq = stq[li];
+          Real* dvp = dv_tok + (int64_t)tp * NV;
+#pragma unroll
+          for (int p = 0; p < TPW; ++p) {
+            const R4 Dt = sm.xd[jp ^ 1][wr * TPW + p][lane];
+            R4 sv = row16_sum_x4(Dt, kq);
+            if (li == 0) {
+              if (nslab == 1) {
+                const R4 u = cols4(stq + OFF_U + (wr * TPW + p) * 16, g);
+                const R4 w4 = cols4(&sm.wr[(wr * TPW + p) * 16], g);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sv[r] = fma_r(w4[r], u[r], sv[r]);
+              }
+              const int col0 = col_of(p, 0);
+              if (dv_vec) {
+                if (FULL || col0 < V) *(R4*)(dvp + col0) = sv;
+              } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  if (col_of(p, r) < V) dvp[col_of(p, r)] = sv[r];
+              }
+            }
+          }
+        }
+      }
+      // S_0 (the initial state) for the reverse role's last step
+      if (j == nch * S) {
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) {
+          R4 h0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int col = col_of(p, r);
+            h0[r] = (a.H0 && row_ok && col < V) ? ((const Real*)a.H0)[state_base + col] : Real(0);
+          }
+          sm.hr[0][wr * TPW + p][lane] = h0;
+        }
+      }
+    };
+
+    for (int k = 0; k < nper; ++k) {
+      const int cF = nch - 1 - k;  // chunk filled in this period
+      const bool rec = cF >= 0;
+      const int slot = rec ? cF % NSLOT : 0;
+      const int hbase = rec ? (cF & 1) * S : 0;  // ring position of S_{cF S}
+      const int slotA = cF + 1 >= 0 ? (cF + 1) % NSLOT : 0;
+      const int slotB = cF + 2 >= 0 ? (cF + 2) % NSLOT : 0;
+      const int slotC = cF + 3 >= 0 ? (cF + 3) % NSLOT : 0;
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        ((phase(std::integral_constant<int, I>{}, k, cF, rec, slot, hbase, slotA, slotB, slotC),
+          __syncthreads()),
+         ...);
+      }(std::make_integer_sequence<int, S>{});
+    }
+    } else {
     // ================================================================ forward role
     // W^T as the A operand, rotated so this wave's own tiles come first and
     // scaled by 2 / ln 2, exactly as in the forward kernel
@@ -478,6 +875,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
          ...);
       }(std::make_integer_sequence<int, S>{});
     }
+    }  // SW
   } else if (role == 1) {
     // ================================================================ reverse role
     // W as the A operand of (D W^T)^T = W D^T, rotated like the forward role's
@@ -524,6 +922,9 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
     const int trow = 4 * (li & 3) + (li >> 2);
 
     __syncthreads();  // prologue staging by the side role
+    if constexpr (SW) {  // the forward role's sweep-only periods
+      for (int i = 0; i < ((int)(a.C / S) + (S == 1 ? 1 : 0)) * S; ++i) __syncthreads();
+    }
 
     auto phase = [&](auto Ic, int k, int slotA, int slotB, int par) {
       constexpr int I = decltype(Ic)::value;
@@ -761,10 +1162,13 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
     for (int i = xt; i < 2 * VT * 64; i += NX) (&sm.xd[0][0][0])[i] = R4{0, 0, 0, 0};
     for (int i = xt; i < (int)(sizeof(sm.xdT) / sizeof(Real)); i += NX) (&sm.xdT[0][0][0][0])[i] = Real(0);
     stage_load(nch - 1);
-    ck_load(nch - 1);
+    if constexpr (!SW) ck_load(nch - 1);
     stage_store(nch - 1);
-    ck_store(nch - 1);
+    if constexpr (!SW) ck_store(nch - 1);
     __syncthreads();
+    if constexpr (SW) {  // the forward role's sweep-only periods
+      for (int i = 0; i < ((int)(a.C / S) + (S == 1 ? 1 : 0)) * S; ++i) __syncthreads();
+    }
 
     auto phase = [&](auto Ic, int k, int cF, int par) {
       constexpr int I = decltype(Ic)::value;
@@ -833,13 +1237,13 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
       const bool stage = cF >= 1;
       if (stage) {
         stage_load(cF - 1);
-        ck_load(cF - 1);
+        if constexpr (!SW) ck_load(cF - 1);
       }
       const int par = (cF + 2) & 1;
       auto period_end = [&]() {
         if (stage) {
           stage_store(cF - 1);
-          ck_store(cF - 1);
+          if constexpr (!SW) ck_store(cF - 1);
         }
       };
       [&]<int... I>(std::integer_sequence<int, I...>) {
@@ -1324,13 +1728,20 @@ static hipError_t launch_bwd_vt(const BwdArgs& a0, hipStream_t stream) {
   using Tr = BwdTraits<Real, VT>;
   static_assert(sizeof(BwdSmem<Real, VT>) <= kLdsBytes, "LDS budget");
   BwdArgs a = a0;
-  const BwdWorkspace L =
-      bwd_workspace_layout(a.B, a.T, a.N, a.NQ, a.K, a.V, a.C, sizeof(Real) == 8 ? kF64 : kF32);
+  const BwdWorkspace L = bwd_workspace_layout(a.B, a.T, a.N, a.NQ, a.K, a.V, a.C,
+                                              sizeof(Real) == 8 ? kF64 : kF32, a.rc != nullptr);
   Real* ws = (Real*)a.ws;
   const int64_t units = a.B * a.N * a.nslab;
   const int64_t nck = (a.T + a.C - 1) / a.C;
   hipError_t err;
-  if (L.subck_needed) {
+  if (L.sweep) {
+    // the main kernel sweeps each checkpoint interval itself
+    a.ring_s = ws + L.ring_s;
+    a.ring_r = a.rc ? nullptr : (void*)(ws + L.ring_r);
+    a.cks = nullptr;
+    a.cks_count = 0;
+    a.cks_step = 0;
+  } else if (L.subck_needed) {
     // one workgroup per (slab, checkpoint interval), in launches of at most 2^24 workgroups
     const int64_t total = units * nck;
     if (a.rc) {
@@ -1368,18 +1779,27 @@ static hipError_t launch_bwd_vt(const BwdArgs& a0, hipStream_t stream) {
   // rc and the dv destination 16-byte aligned
   const bool full = sizeof(Real) == 4 && a.K % 16 == 0 && a.V == Tr::VP && a.rc_vec && a.dv_vec;
   const dim3 grid((unsigned)units), block(Tr::NT);
+  // variants: states from the stored rc (RC) or recomputed; every tile full (FULL);
+  // intervals swept by the main kernel (SW)
+  auto go = [&](auto rc_c, auto full_c, auto sw_c) {
+    hipLaunchKernelGGL((m2rnn_bwd_kernel<InT, Real, VT, decltype(rc_c)::value,
+                                         decltype(full_c)::value, decltype(sw_c)::value>),
+                       grid, block, 0, stream, a, L);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  auto pick_sw = [&](auto rc_c, auto full_c) {
+    if (L.sweep) go(rc_c, full_c, T_{});
+    else go(rc_c, full_c, F_{});
+  };
+  auto pick_rc = [&](auto full_c) {
+    if (a.rc) pick_sw(T_{}, full_c);
+    else pick_sw(F_{}, full_c);
+  };
   if constexpr (sizeof(Real) == 4) {
-    if (full && a.rc)  // the forward's rc replaces the recomputation inside each chunk
-      hipLaunchKernelGGL((m2rnn_bwd_kernel<InT, Real, VT, true, true>), grid, block, 0, stream, a, L);
-    else if (full)
-      hipLaunchKernelGGL((m2rnn_bwd_kernel<InT, Real, VT, false, true>), grid, block, 0, stream, a, L);
+    if (full) pick_rc(T_{});
   }
-  if (!full) {
-    if (a.rc)
-      hipLaunchKernelGGL((m2rnn_bwd_kernel<InT, Real, VT, true, false>), grid, block, 0, stream, a, L);
-    else
-      hipLaunchKernelGGL((m2rnn_bwd_kernel<InT, Real, VT, false, false>), grid, block, 0, stream, a, L);
-  }
+  if (!full) pick_rc(F_{});
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   const int64_t tokens = a.B * a.T * a.N;

@@ -247,6 +247,17 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return (bid % kXcd) * (nblocks / kXcd) + bid / kXcd;
 }
 
+// The value of x in lane m (m wave-uniform).
+__device__ __forceinline__ float lane_value_r(float x, int m) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), m));
+}
+__device__ __forceinline__ double lane_value_r(double x, int m) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, m);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), m);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 // Widening loads of the k / v / q element types.
 __device__ __forceinline__ float load_in(const float* p) { return *p; }
 __device__ __forceinline__ float load_in(const uint16_t* p) {

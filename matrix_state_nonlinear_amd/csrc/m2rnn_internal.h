@@ -80,6 +80,11 @@ struct BwdArgs {
   // checkpoints (when C divides S) or states recomputed into the workspace.
   const void* cks;
   int64_t cks_count, cks_step;
+  // Interval sweep (BwdWorkspace::sweep): per unit, two checkpoint intervals of
+  // states S_{t+1} (ring_s) and, when the states are recomputed, rc_t (ring_r),
+  // each [2][C][ceil(V / 16) tiles][64 lanes][4] in the kernels' register layout.
+  void* ring_s;
+  void* ring_r;
   int64_t B, T, N, K, V, C;
   int64_t NQ;        // heads of q and k; value head n reads q/k head n / (N / NQ)
   int nslab;
@@ -96,7 +101,11 @@ struct BwdWorkspace {
   int period;         // S: steps per chunk of the reverse sweep (depends on V and dtype)
   int64_t nch;        // ceil(T / S)
   bool subck_needed;  // C does not divide S: chunk starts are recomputed first
+  bool sweep;         // the main kernel sweeps each checkpoint interval itself instead
+                      // (C a multiple of S, larger, and at most kMaxSweepInterval)
   size_t subck;       // [B, N, nch, K, V] chunk-start states (subck_needed only)
+  size_t ring_s;      // [units, 2, C, 16 VP] states of two intervals (sweep only)
+  size_t ring_r;      // [units, 2, C, 16 VP] rc of two intervals (sweep, recomputing only)
   size_t dv_part;     // [nslab, B, T, N, V]  (nslab > 1 only)
   size_t df_part;     // [nslab, B, T, N]
   size_t dW_part;     // [B * nslab, N, V, V]
@@ -106,8 +115,13 @@ struct BwdWorkspace {
   int64_t row_blocks;
   size_t total_elems;
 };
+// Checkpoint intervals up to this length are swept inside the backward's main
+// kernel (two intervals of states per 16-row slab in the workspace); longer
+// ones get their chunk starts from a separate recomputing pass.
+constexpr int64_t kMaxSweepInterval = 1024;
+
 BwdWorkspace bwd_workspace_layout(int64_t B, int64_t T, int64_t N, int64_t NQ, int64_t K,
-                                  int64_t V, int64_t C, int state_dtype);
+                                  int64_t V, int64_t C, int state_dtype, bool stored_rc);
 
 struct StepArgs {
   const void* k;     // [B, NQ, K]

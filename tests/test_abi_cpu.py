@@ -54,14 +54,20 @@ def test_workspace_sizes(L):
     assert ws(0, 1, 10, 1, 1, 300, 16, 1, _lib.M2RNN_F32) == 0
     assert ws(1, 1, 10, 1, 1, 16, 16, 0, _lib.M2RNN_F32) == 0
     # backward: for V = 64 in fp32 the reverse sweep walks 4-step chunks; a
-    # checkpoint interval dividing 4 provides every chunk start, any other adds
-    # a [B, N, ceil(T / 4), K, V] region of recomputed chunk starts
+    # checkpoint interval dividing 4 provides every chunk start; a multiple of 4
+    # (up to 1024) is swept by the main kernel, which keeps two intervals of
+    # states and of rc per 16-row slab ([units, 2, C, 16, 64] each); any other
+    # adds a [B, N, ceil(T / 4), K, V] region of recomputed chunk starts
     base = ws(1, 2, 64, 2, 2, 32, 64, 4, _lib.M2RNN_F32)
     assert base > 0
     for C in (1, 2):
         assert ws(1, 2, 64, 2, 2, 32, 64, C, _lib.M2RNN_F32) == base
-    for C in (3, 8, 64):
+    for C in (3, 6, 2048):
         assert ws(1, 2, 64, 2, 2, 32, 64, C, _lib.M2RNN_F32) == base + 2 * 2 * 16 * 32 * 64 * 4
+    units = 2 * 2 * 2
+    for C in (8, 64, 1024):
+        assert ws(1, 2, 64, 2, 2, 32, 64, C, _lib.M2RNN_F32) == \
+            base + 2 * units * 2 * C * 16 * 64 * 4
 
 
 def fwd(L, **kw):
@@ -174,6 +180,8 @@ def test_bwd_rejects_bad_arguments(L):
     assert bwd(L, V=200) == E.M2RNN_ERR_UNSUPPORTED
     assert bwd(L) == E.M2RNN_ERR_WORKSPACE                             # always needs workspace
     assert bwd(L, ws=FAKE, wsb=64) == E.M2RNN_ERR_WORKSPACE
+    big = 1 << 30
+    assert bwd(L, ws=FAKE + 4, wsb=big) == E.M2RNN_ERR_INVALID_ARG  # not 16-byte aligned
 
 
 def test_bwd_noalloc_checks_before_touching_the_device(L):

@@ -179,3 +179,79 @@ def replay_with_ring(S, nch, ring):
         for b, p, item in writes:
             store[(b, p)] = (item, j)
     return errors
+
+
+# ---------------------------------------------------------------- interval sweep
+#
+# With checkpoints every C steps (C a multiple of S, C > S) the forward role
+# sweeps each checkpoint interval forward in time once and keeps its states
+# (and rc) in a per-unit ring of two interval slots; the LDS rings of a chunk
+# are filled from there.  Each ring element is written and read by the same
+# lane, so within a phase program order decides: the fill's load for its next
+# step is issued before the sweep's store of that phase.  The replay below uses
+# the kernel's expressions (sweep order, slot (t / C) & 1, position t mod C,
+# C / S sweep-only periods first, one more when S = 1, where the fill's load of
+# the next chunk shares its phase with that chunk's sweep) and checks that every fill load finds the
+# item it needs, stored in an earlier phase and not yet overwritten, and that
+# the sweep covers every step once.
+
+def sweep_chunk(s, nch, CS, S):
+    J = -(-nch // CS)
+    n_last = nch - (J - 1) * CS
+    if s < n_last:
+        return ((J - 1) * CS + s) * S
+    m, r = divmod(s - n_last, CS)
+    return ((J - 2 - m) * CS + r) * S
+
+
+def replay_sweep(S, C, nch, slots_=2):
+    CS = C // S
+    P0 = CS + (1 if S == 1 else 0)
+    jlast = nch * S + S + 1
+    nper = jlast // S + 1
+    ring = {}
+    errors, swept = [], []
+
+    def rix(t):
+        i = t // C
+        return ((i % slots_) if slots_ != 2 else (i & 1), t - i * C)
+
+    def fill_load(t, ph):
+        have = ring.get(rix(t))
+        if have is None or have[0] != ("S", t + 1) or have[1] >= ph:
+            errors.append(f"phase {ph}: fill load of step {t} finds {have}")
+
+    for kt in range(P0 + nper):
+        for I in range(S):
+            ph = kt * S + I
+            k = kt - P0
+            if kt == P0 and I == 0 and nch > 0:
+                pass  # the first fill load happens after the prologue (below)
+            # fill: uses step t (loaded earlier), loads the next step now
+            if k >= 0:
+                cF = nch - 1 - k
+                if cF >= 0:
+                    if I + 1 < S or cF >= 1:
+                        fill_load(cF * S + I + 1 if I + 1 < S else (cF - 1) * S, ph)
+            # sweep (stores after the fill's load in program order)
+            if kt < nch:
+                x = sweep_chunk(kt, nch, CS, S) + I
+                swept.append(x)
+                ring[rix(x)] = (("S", x + 1), ph)
+            if kt == P0 - 1 and I == S - 1 and nch > 0:
+                fill_load((nch - 1) * S, ph + 0.5)   # after the prologue's last barrier
+    return errors, swept
+
+
+@pytest.mark.parametrize("S,C", [(2, 4), (2, 64), (4, 8), (4, 16), (1, 3), (2, 6), (4, 12)])
+@pytest.mark.parametrize("nch", [1, 2, 3, 5, 7, 16, 33, 64])
+def test_interval_sweep_schedule(S, C, nch):
+    errors, swept = replay_sweep(S, C, nch)
+    assert not errors, errors[:5]
+    assert sorted(swept) == list(range(nch * S))
+
+
+def test_interval_sweep_replay_detects_one_slot():
+    """With a single interval slot the sweep overwrites states the fill still needs."""
+    assert any(replay_sweep(S, C, n, slots_=1)[0]
+               for S, C in [(2, 4), (4, 8)] for n in range(3, 12))
