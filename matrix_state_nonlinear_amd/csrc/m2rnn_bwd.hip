@@ -85,7 +85,7 @@ constexpr size_t bwd_smem_bytes(int S) {
   using Sh = BwdShape<Real, VT>;
   return (size_t)(4 * S + (Sh::kXdt ? 6 : 4)) * Sh::kTileset +
          (size_t)bwd_slots(S) * S * Sh::E * sizeof(Real) +
-         (size_t)(2 * 16 * 4 + 2 * 16 * 20 + 2 * 4 * Sh::NW) * sizeof(Real) +
+         (size_t)(2 * 16 * 4 + 2 * 16 * 20 + 2 * 4 * Sh::NW + Sh::VP) * sizeof(Real) +
          (Sh::kXdt ? (size_t)2 * VT * 16 * 4 * sizeof(Real) : 0);
 }
 
@@ -107,7 +107,10 @@ struct BwdTraits : BwdShape<Real, VT> {
   static constexpr int NCK = (16 * Sh::VP + NX - 1) / NX;       // start-state values per thread
 };
 
-template <typename Real, int VT>
+// XT: tiles of the state exchange.  The interval-sweep variant holds every tile
+// twice (positions p and p + VT) where LDS allows, so that a wave reads its
+// rotated B operand tiles at one base address plus constant offsets.
+template <typename Real, int VT, int XT = VT>
 struct BwdSmem {
   using Tr = BwdTraits<Real, VT>;
   using R4 = typename Vec4<Real>::type;
@@ -118,7 +121,8 @@ struct BwdSmem {
   // 20 so that both the scattered writes and the 16-byte reads of 8
   // consecutive lanes spread over the banks
   Real xdT[Tr::kXdt ? 2 : 1][VT][16][Tr::kXdt ? 20 : 1];
-  R4 ck[2][VT][64];                // chunk start states in register layout, by chunk parity
+  R4 ck[2][XT][64];                // chunk start states in register layout, by chunk parity
+                                   // (interval sweep: the exchanged states, by step parity)
   // staged inputs of a chunk, per step: k[16] q[16] v[VP] dy[VP] f (padded)
   Real st[Tr::NSLOT][Tr::S * Tr::E];
   Real rq[2][16][4];               // dq per-wave row sums [row][wave] (at most 4 waves)
@@ -126,6 +130,12 @@ struct BwdSmem {
   Real rf[2][4 * Tr::NW];          // df partials [wave, lane group]
   Real wr[Tr::VP];                 // w_r of the head (interval sweep: dv's value-residual term)
 };
+
+// the exchange of the interval sweep: doubled where it fits
+template <typename Real, int VT>
+constexpr int bwd_sweep_xt() {
+  return sizeof(BwdSmem<Real, VT, 2 * VT>) <= kLdsBytes ? 2 * VT : VT;
+}
 
 int bwd_period(int state_dtype, int64_t V) {
   const bool f64 = state_dtype == kF64;
@@ -185,7 +195,9 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
   constexpr int S = Tr::S, M = Tr::M, NSLOT = Tr::NSLOT, E = Tr::E;
   constexpr int NX = Tr::NX, NLD = Tr::NLD, NCK = Tr::NCK;
   constexpr int OFF_Q = 16, OFF_V = 32, OFF_U = 32 + VP, OFF_F = 32 + 2 * VP;
-  __shared__ BwdSmem<Real, VT> sm;
+  constexpr int XT = SW ? bwd_sweep_xt<Real, VT>() : VT;
+  static_assert(sizeof(BwdSmem<Real, VT, XT>) <= kLdsBytes, "LDS budget");
+  __shared__ BwdSmem<Real, VT, XT> sm;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, g = lane >> 4, li = lane & 15;
@@ -241,7 +253,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
     // next chunk's first step in the phase that would sweep it
     const int P0 = CS + (S == 1 ? 1 : 0);
     const int64_t KV = K * V;
-    const int64_t nck = J;
+    const int64_t n_ckpt = J;
     // W^T as the A operand, rotated and scaled exactly as in the forward kernel
     Real wop[RC ? 1 : TPW][RC ? 1 : NS];
     if constexpr (!RC) {
@@ -286,16 +298,17 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
       for (int r = 0; r < 4; ++r) colv[p][r] = FULL || (row_ok && col_of(p, r) < V);
 
     // the unit's ring, in R4 units: [slot][position][tile][lane]; step t of
-    // interval t / C sits in slot (t / C) & 1 at position t mod C
+    // interval i = t / C sits in slot i & 1 at position t - i C.  Both walks over
+    // it (the sweep and the fill) keep their interval and position in counters,
+    // so no step index is ever divided
     const size_t ring_unit = (size_t)unit * 2 * Ci * VT * 64;
     R4* const rs = (R4*)a.ring_s + ring_unit + wr * TPW * 64 + lane;
     R4* const rr = RC ? nullptr : (R4*)a.ring_r + ring_unit + wr * TPW * 64 + lane;
-    auto rix = [&](int t) __attribute__((always_inline)) -> size_t {
-      const int i = t / Ci;
-      return ((size_t)((i & 1) * Ci + (t - i * Ci)) * VT) * 64;
+    auto rix = [&](int i, int pos) __attribute__((always_inline)) -> size_t {
+      return ((size_t)((i & 1) * Ci + pos) * VT) * 64;
     };
 
-    // ---- sweep inputs of step x, loaded one step ahead (clamped to T - 1;
+    // ---- sweep inputs of step x, loaded one step ahead (clamped to 0..T - 1;
     // steps past T have f = 1, which keeps the state exactly)
     struct SwIn {
       InT k;
@@ -310,7 +323,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
                              : nullptr;
     const bool rc_vec = sizeof(Real) == 4 && (FULL || a.rc_vec);
     auto load_sw = [&](int x, SwIn& in) __attribute__((always_inline)) {
-      const int xc = x < T32 ? x : T32 - 1;
+      const int xc = x < 0 ? 0 : (x < T32 ? x : T32 - 1);
       // gates of steps xc and xc + 1 in alternate lanes: a lane-dependent address
       int xf = xc + (lane & 1);
       if (xf > T32 - 1) xf = T32 - 1;
@@ -349,15 +362,17 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
       return y;
     };
 
-    // ---- sweep state: own tiles hs (row `row`, columns col_of(p, r)).  An interval
-    // starts from its checkpoint: the own tiles are loaded one sweep step ahead (ckn)
-    // and, when recomputing, published through the exchange buffer in place of the
-    // previous step's state, so every step reads the other tiles of its B operand
-    // from there
+    // ---- sweep state: own tiles hs (row `row`, columns col_of(p, r)), published
+    // after every step through the exchange buffer, where each tile sits twice
+    // (p and p + VT): a wave reads its B operand there in its rotated order
+    // (own tiles first, as in the forward kernel) at one base address plus
+    // constant offsets.  An interval starts from its checkpoint: its own tiles are
+    // loaded after the previous interval's last step and published in place of
+    // that step's state
     R4 hs[TPW], ckn[TPW];
     auto load_ck = [&](int i) __attribute__((always_inline)) {
       // the checkpoint H_{iC}, own tiles, from clamped addresses (masked on use)
-      const Real* ck = (const Real*)a.ckpt + (((int64_t)bn * nck + i) * K + (row_ok ? row : 0)) * V;
+      const Real* ck = (const Real*)a.ckpt + (((int64_t)bn * n_ckpt + i) * K + (row_ok ? row : 0)) * V;
 #pragma unroll
       for (int p = 0; p < TPW; ++p)
 #pragma unroll
@@ -375,18 +390,26 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
         for (int r = 0; r < 4; ++r) hs[p][r] = colv[p][r] ? c[r] : Real(0);
       }
     };
-    // The sweep's position: chunk number s of the sweep order (the intervals from
-    // the last to the first, each one's chunks forward in time) -> its first step.
-    auto sweep_chunk = [&](int s) __attribute__((always_inline)) -> int {
-      if (s < n_last) return ((J - 1) * CS + s) * S;
-      const int m = (s - n_last) / CS, r = (s - n_last) - m * CS;
-      return ((J - 2 - m) * CS + r) * S;
-    };
+    // The sweep's order: the intervals from the last to the first, each one's
+    // chunks forward in time.  Cursor: interval s_i, the first step of the current
+    // chunk within it (s_pos), the steps of the interval (s_len; the last one may
+    // be shorter) and the chunks left.
+    int s_i = J - 1, s_pos = 0, s_len = n_last * S, s_left = nch;
+    int s_next = 0;  // the sweep's next step (whose inputs load_sw takes next)
     SwIn swc;  // the sweep step's inputs (loaded during the previous step)
-    // one sweep step x (phase parity par); nx: the sweep's next step, or -1
-    auto sweep_step = [&](int par, int x, int nx) __attribute__((always_inline)) {
-      // the next step starts an interval: load its checkpoint now (taken at the end)
-      if (nx >= 0 && nx % Ci == 0) load_ck(nx / Ci);
+    auto publish = [&](int par) __attribute__((always_inline)) {
+#pragma unroll
+      for (int p = 0; p < TPW; ++p) {
+        sm.ck[par][wr * TPW + p][lane] = hs[p];
+        if constexpr (XT == 2 * VT) sm.ck[par][wr * TPW + p + VT][lane] = hs[p];
+      }
+    };
+    // one sweep step x at ring index ix (phase parity par); nck: the interval
+    // that the next step starts, or -1.  When recomputing, the inputs of the next
+    // step are loaded at the end of the phase, after every other memory access
+    // of the role, so that no wait in between (a spill reload among them) has to
+    // include them; the stored rc is loaded as soon as it is consumed.
+    auto sweep_step = [&](int par, int x, size_t ix, int nck) __attribute__((always_inline)) {
       const Real f = x < T32 ? lane_value_r(swc.f, 0) : Real(1);
       const Real omf = Real(1) - f;
       const Real m2omf = Real(-2) * omf;
@@ -400,7 +423,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
           for (int r = 0; r < 4; ++r) rc[r] = colv[p][r] ? rc[r] : Real(0.5);
           rcv[p] = rc;
         }
-        if (nx >= 0) load_sw(nx, swc);  // the inputs are consumed: load the next step's
+        load_sw(s_next, swc);  // consumed: the next step's rc, a phase ahead
       } else {
         // the scaled rank-1 write k v^T starts the accumulators, as in the forward kernel
         const Real kk = held(swc.k);
@@ -413,13 +436,12 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
             const Real vv = held(swc.v[p][r]);
             acc[p][r] = ks * (col_of(p, r) < V ? vv : Real(0));
           }
-        if (nx >= 0) load_sw(nx, swc);  // the inputs are consumed: load the next step's
-        // H W over the slab: the own tiles from registers (or the interval's start
-        // state), then the others from the exchange of the previous sweep step, one
-        // 16-byte LDS read per tile just ahead of its MFMAs
+        // H W over the slab, the tiles in the forward kernel's order (own first)
+        // from the previous step's exchange, one 16-byte LDS read per tile
+        const R4* const xb = &sm.ck[par ^ 1][TPW * wr][lane];
 #pragma unroll
         for (int q0 = 0; q0 < VT; ++q0) {
-          const R4 t4 = q0 < TPW ? hs[q0] : sm.ck[par ^ 1][(q0 + TPW * wr) % VT][lane];
+          const R4 t4 = XT == 2 * VT ? xb[q0 * 64] : sm.ck[par ^ 1][(q0 + TPW * wr) % VT][lane];
 #pragma unroll
           for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -432,7 +454,6 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
 #pragma unroll
           for (int r = 0; r < 4; ++r) rcv[p][r] = tanh_rc_scaled(acc[p][r]);
       }
-      const size_t ix = rix(x);
 #pragma unroll
       for (int p = 0; p < TPW; ++p) {
 #pragma unroll
@@ -441,22 +462,21 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
         rs[ix + p * 64] = hs[p];
       }
       // the next step starts an interval: its state is that interval's checkpoint
-      if (nx >= 0 && nx % Ci == 0) take_ck();
-      if constexpr (!RC) {
-#pragma unroll
-        for (int p = 0; p < TPW; ++p) sm.ck[par][wr * TPW + p][lane] = hs[p];
+      if (nck >= 0) {  // (once per interval: not prefetched, which would hold registers)
+        load_ck(nck);
+        take_ck();
       }
+      if constexpr (!RC) publish(par);
     };
 
     // ---- fill of the LDS rings for the chunk the reverse role takes next:
     // S_{t+1} and rc_t of step t, loaded one phase ahead
     R4 fS[TPW], fR[TPW];
-    auto load_fill = [&](int t) __attribute__((always_inline)) {
-      const size_t ix = rix(t);
+    auto load_fill = [&](int t, size_t ix) __attribute__((always_inline)) {
 #pragma unroll
       for (int p = 0; p < TPW; ++p) fS[p] = rs[ix + p * 64];
       if constexpr (RC) {
-        const Real* src = rc_lane + (int64_t)(t < T32 ? t : T32 - 1) * KV;
+        const Real* src = rc_lane + (int64_t)(t < 0 ? 0 : (t < T32 ? t : T32 - 1)) * KV;
 #pragma unroll
         for (int p = 0; p < TPW; ++p) {
           if (rc_vec) {
@@ -478,40 +498,58 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
 
     // the sweep's first step: the last interval, from its checkpoint (published for
     // the first step's B operand as the previous step's state would be)
-    load_sw(sweep_chunk(0), swc);
+    load_sw(s_i * Ci, swc);
     load_ck(J - 1);
     take_ck();
-    if constexpr (!RC) {
-#pragma unroll
-      for (int p = 0; p < TPW; ++p) sm.ck[1][wr * TPW + p][lane] = hs[p];
-    }
+    if constexpr (!RC) publish(1);
 
     __syncthreads();  // prologue staging by the side role
 
-    auto sweep_phase = [&](int kt, int I, int jpar) __attribute__((always_inline)) {
-      // sweep chunk kt (if any), its step I; the next step is the same chunk's
-      // I + 1 or the next sweep chunk's first
-      if (kt >= nch) return;
-      const int x = sweep_chunk(kt) + I;
-      const int nx = I + 1 < S ? x + 1 : (kt + 1 < nch ? sweep_chunk(kt + 1) : -1);
-      sweep_step(jpar, x, nx);
+    auto sweep_phase = [&](int I, int jpar) __attribute__((always_inline)) {
+      // step I of the cursor's chunk (if any chunk is left); the next step is the
+      // following one in time, except after an interval's last step, where the
+      // sweep goes on from the start of the interval before it
+      if (s_left <= 0) return;
+      const int x = s_i * Ci + s_pos + I;
+      int nx = x + 1, nck = -1;
+      const bool last = I + 1 == S && s_pos + S == s_len;
+      if (last) {
+        nck = s_i - 1;
+        nx = nck >= 0 ? nck * Ci : 0;
+      }
+      s_next = nx;
+      sweep_step(jpar, x, rix(s_i, s_pos + I), nck);
+      if (I + 1 == S) {  // the chunk is done: advance the cursor
+        --s_left;
+        if (last) {
+          --s_i;
+          s_pos = 0;
+          s_len = Ci;
+        } else {
+          s_pos += S;
+        }
+      }
     };
     // prologue: the last interval's sweep (and the following chunks up to P0)
     for (int kt = 0; kt < P0; ++kt) {
       for (int I = 0; I < S; ++I) {
-        sweep_phase(kt, I, (kt * S + I) & 1);
+        sweep_phase(I, (kt * S + I) & 1);
+        if constexpr (!RC) load_sw(s_next, swc);
         __syncthreads();
       }
     }
-    if (nch > 0) load_fill((nch - 1) * S);
+    // Fill cursor: the interval f_i of the chunk filled in the period and that
+    // chunk's first step within it (f_pos); the fill walks the chunks backward
+    int f_i = J - 1, f_pos = (n_last - 1) * S;
+    if (nch > 0) load_fill((nch - 1) * S, rix(f_i, f_pos));
 
     auto phase = [&](auto Ic, int k, int cF, bool rec, int slot, int hbase, int slotA, int slotB,
                      int slotC) {
       constexpr int I = decltype(Ic)::value;
       const int j = k * S + I;
       const int jp = j & 1;
-      const int kt = P0 + k;
-      if (rec) {
+      auto fill = [&]() __attribute__((always_inline)) {
+        if (!rec) return;
         // the step t = cF S + I of the chunk: S_{t+1} and rc_t from the ring
         const Real* stp = &sm.st[slot][I * E];
         R4 s1[TPW], r1[TPW];
@@ -525,7 +563,6 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
 #pragma unroll
           for (int r = 0; r < 4; ++r) r1[p][r] = colv[p][r] ? r1[p][r] : Real(0.5);
         }
-        if (I + 1 < S || cF >= 1) load_fill(I + 1 < S ? cF * S + I + 1 : (cF - 1) * S);
         Real dqp = 0;
 #pragma unroll
         for (int p = 0; p < TPW; ++p) {
@@ -537,9 +574,17 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
         }
         dqp = cross_row_sum(dqp);
         if (g == 0) sm.rq[jp][li][wr] = dqp;
+      };
+      // the sweep, C / S chunks ahead of the fill.  Recomputing, the sweep goes
+      // after the fill, from the stored rc before it (measured at V = 128: 6 % and
+      // 11 % faster than the other order)
+      if constexpr (RC) {
+        sweep_phase(I, (P0 * S + j) & 1);
+        fill();
+      } else {
+        fill();
+        sweep_phase(I, (P0 * S + j) & 1);
       }
-      // the sweep, C / S chunks ahead of the fill
-      sweep_phase(kt, I, (P0 * S + j) & 1);
       // dq of the previous phase's step: the per-wave sums, added by wave 0
       if (wr == 0 && g == 0 && (FULL || row_ok) && j >= 1 && j <= nch * S) {
         const int tf = I > 0 ? cF * S + I - 1 : cF * S + 2 * S - 1;
@@ -594,6 +639,18 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
           sm.hr[0][wr * TPW + p][lane] = h0;
         }
       }
+      // the next phase's reads from memory, last and unconditionally (a harmless
+      // in-ring address when there is nothing to fill): the fill's next step, then
+      // the sweep's next inputs (when recomputing; the stored rc is loaded by the
+      // sweep step itself)
+      if constexpr (I + 1 < S) {
+        load_fill(cF * S + I + 1, rix(f_i, f_pos + I + 1));
+      } else {
+        // the first step of the chunk before: the same interval, or the end of
+        // the one before it
+        load_fill((cF - 1) * S, f_pos > 0 ? rix(f_i, f_pos - S) : rix(f_i - 1, Ci - S));
+      }
+      if constexpr (!RC) load_sw(s_next, swc);
     };
 
     for (int k = 0; k < nper; ++k) {
@@ -609,6 +666,14 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
           __syncthreads()),
          ...);
       }(std::make_integer_sequence<int, S>{});
+      if (rec) {  // the fill moves to the chunk before
+        if (f_pos > 0) {
+          f_pos -= S;
+        } else {
+          --f_i;
+          f_pos = Ci - S;
+        }
+      }
     }
     } else {
     // ================================================================ forward role
@@ -1789,8 +1854,13 @@ static hipError_t launch_bwd_vt(const BwdArgs& a0, hipStream_t stream) {
   using T_ = std::true_type;
   using F_ = std::false_type;
   auto pick_sw = [&](auto rc_c, auto full_c) {
-    if (L.sweep) go(rc_c, full_c, T_{});
-    else go(rc_c, full_c, F_{});
+    if constexpr (Tr::S >= 2) {  // (the sweep needs chunks of two steps or more)
+      if (L.sweep) {
+        go(rc_c, full_c, T_{});
+        return;
+      }
+    }
+    go(rc_c, full_c, F_{});
   };
   auto pick_rc = [&](auto full_c) {
     if (a.rc) pick_sw(T_{}, full_c);

@@ -188,12 +188,14 @@ def replay_with_ring(S, nch, ring):
 # (and rc) in a per-unit ring of two interval slots; the LDS rings of a chunk
 # are filled from there.  Each ring element is written and read by the same
 # lane, so within a phase program order decides: the fill's load for its next
-# step is issued before the sweep's store of that phase.  The replay below uses
-# the kernel's expressions (sweep order, slot (t / C) & 1, position t mod C,
+# step is issued at the end of the phase, after the sweep's store.  The replay below uses
+# the sweep's definitions (sweep order, slot (t / C) & 1, position t mod C,
 # C / S sweep-only periods first, one more when S = 1, where the fill's load of
-# the next chunk shares its phase with that chunk's sweep) and checks that every fill load finds the
-# item it needs, stored in an earlier phase and not yet overwritten, and that
-# the sweep covers every step once.
+# the next chunk shares its phase with that chunk's sweep) and checks that every
+# fill load finds the item it needs, stored in an earlier phase and not yet
+# overwritten, and that the sweep covers every step once.  The kernel walks the
+# same order with counters instead of divisions; a test below checks that the
+# counters reproduce the definitions.
 
 def sweep_chunk(s, nch, CS, S):
     J = -(-nch // CS)
@@ -227,17 +229,18 @@ def replay_sweep(S, C, nch, slots_=2):
             k = kt - P0
             if kt == P0 and I == 0 and nch > 0:
                 pass  # the first fill load happens after the prologue (below)
-            # fill: uses step t (loaded earlier), loads the next step now
+            # sweep: stores S_{x+1} (and rc_x)
+            if kt < nch:
+                x = sweep_chunk(kt, nch, CS, S) + I
+                swept.append(x)
+                ring[rix(x)] = (("S", x + 1), ph)
+            # fill: uses step t (loaded in the phase before) and loads the next
+            # step at the end of the phase, after the sweep's stores
             if k >= 0:
                 cF = nch - 1 - k
                 if cF >= 0:
                     if I + 1 < S or cF >= 1:
                         fill_load(cF * S + I + 1 if I + 1 < S else (cF - 1) * S, ph)
-            # sweep (stores after the fill's load in program order)
-            if kt < nch:
-                x = sweep_chunk(kt, nch, CS, S) + I
-                swept.append(x)
-                ring[rix(x)] = (("S", x + 1), ph)
             if kt == P0 - 1 and I == S - 1 and nch > 0:
                 fill_load((nch - 1) * S, ph + 0.5)   # after the prologue's last barrier
     return errors, swept
@@ -249,6 +252,80 @@ def test_interval_sweep_schedule(S, C, nch):
     errors, swept = replay_sweep(S, C, nch)
     assert not errors, errors[:5]
     assert sorted(swept) == list(range(nch * S))
+
+
+def sweep_cursor_walk(S, C, nch):
+    """The kernel's sweep cursor (interval, chunk position, interval length,
+    chunks left), advanced once per chunk with no division: per sweep step
+    (x, ring slot, ring position, next step, interval that the next step starts)."""
+    CS = C // S
+    J = -(-nch // CS)
+    n_last = nch - (J - 1) * CS
+    s_i, s_pos, s_len, s_left = J - 1, 0, n_last * S, nch
+    out = []
+    while s_left > 0:
+        for I in range(S):
+            x = s_i * C + s_pos + I
+            nx, nck = x + 1, -1
+            last = I + 1 == S and s_pos + S == s_len
+            if last:
+                nck = s_i - 1
+                nx = nck * C if nck >= 0 else -1
+            out.append((x, s_i & 1, s_pos + I, nx, nck))
+            if I + 1 == S:
+                s_left -= 1
+                if last:
+                    s_i, s_pos, s_len = s_i - 1, 0, C
+                else:
+                    s_pos += S
+    return out
+
+
+def fill_cursor_walk(S, C, nch):
+    """The kernel's fill cursor (interval and first step within it of the chunk
+    filled in the period), moved back one chunk per period: per fill load
+    (step, ring slot, ring position), in the kernel's order."""
+    CS = C // S
+    J = -(-nch // CS)
+    n_last = nch - (J - 1) * CS
+    f_i, f_pos = J - 1, (n_last - 1) * S
+    out = [((nch - 1) * S, f_i & 1, f_pos)]
+    for cF in range(nch - 1, -1, -1):
+        for I in range(S):
+            if I + 1 < S:
+                out.append((cF * S + I + 1, f_i & 1, f_pos + I + 1))
+            elif cF >= 1:
+                out.append(((cF - 1) * S, f_i & 1, f_pos - S) if f_pos > 0
+                           else ((cF - 1) * S, (f_i - 1) & 1, C - S))
+        if f_pos > 0:
+            f_pos -= S
+        else:
+            f_i, f_pos = f_i - 1, C - S
+    return out
+
+
+@pytest.mark.parametrize("S,C", [(2, 4), (2, 64), (4, 8), (4, 16), (2, 6), (4, 12), (2, 1024)])
+@pytest.mark.parametrize("nch", [1, 2, 3, 5, 7, 16, 33, 64, 700])
+def test_interval_sweep_cursors_match_the_division_form(S, C, nch):
+    """The counters that replace every division in the kernel's sweep and fill
+    give the same steps, ring slots and positions as the definitions (sweep
+    order from sweep_chunk, slot (t / C) & 1, position t mod C)."""
+    CS = C // S
+    ref = []
+    for kt in range(nch):
+        for I in range(S):
+            x = sweep_chunk(kt, nch, CS, S) + I
+            nx = x + 1 if I + 1 < S else (sweep_chunk(kt + 1, nch, CS, S) if kt + 1 < nch else -1)
+            nck = nx // C if nx >= 0 and nx % C == 0 else -1
+            ref.append((x, (x // C) & 1, x % C, nx, nck))
+    assert sweep_cursor_walk(S, C, nch) == ref
+    fill_ref = [((nch - 1) * S, ((nch - 1) * S // C) & 1, (nch - 1) * S % C)]
+    for cF in range(nch - 1, -1, -1):
+        for I in range(S):
+            if I + 1 < S or cF >= 1:
+                t = cF * S + I + 1 if I + 1 < S else (cF - 1) * S
+                fill_ref.append((t, (t // C) & 1, t % C))
+    assert fill_cursor_walk(S, C, nch) == fill_ref
 
 
 def test_interval_sweep_replay_detects_one_slot():
