@@ -377,6 +377,9 @@ int m2rnn_step(int64_t B, int64_t n_heads, int64_t qk_heads, int64_t K, int64_t 
   a.k = k; a.v = v; a.q = q; a.f = f; a.W = W; a.w_r = w_r; a.H = H; a.y = y;
   a.B = B; a.N = n_heads; a.NQ = qk_heads; a.K = K; a.V = V;
   a.vec = state_dtype == M2RNN_F32 && (V & 3) == 0 && ((uintptr_t)H & 15) == 0;
+  a.full = a.vec && K % 16 == 0 && V == 64 && ((uintptr_t)y & 15) == 0 &&
+           ((uintptr_t)v & 3) == 0 && ((uintptr_t)k & 3) == 0 && ((uintptr_t)q & 3) == 0 &&
+           ((uintptr_t)f & 3) == 0;
   return status_of(launch_step(a, in_dtype, state_dtype, (hipStream_t)stream));
 }
 

@@ -134,6 +134,8 @@ struct StepArgs {
   void* y;           // [B, N, V]
   int64_t B, N, NQ, K, V;
   int vec;           // fp32 state, V % 4 == 0 and H 16-byte aligned: 16-byte state accesses
+  int full;          // fp32 state, K % 16 == 0, V = 64, H and y 16-byte aligned, k, q, v, f
+                     // 4-byte aligned: the full-tile kernel with its LDS ring
   int64_t upw;       // batch rows (units) per wave, set by the launcher
 };
 

@@ -260,6 +260,302 @@ __global__ void __launch_bounds__(256, VT == 4 ? 3 : 1) m2rnn_step_kernel(StepAr
   }
 }
 
+// Full-tile step at V = 64: fp32 state, K a multiple of 16, the state and y
+// 16-byte aligned, k, q, v and f 4-byte aligned (checked on the host).  (At
+// V = 16 the step is bound by HBM alone and the general kernel, with four
+// slabs per load group, reaches 70 % of its peak; this kernel is for the
+// state that is as costly to compute as to move.)  The general kernel's arithmetic in the same order, with every access
+// unguarded and W^T held in registers (VT^2 16-byte A operands per lane).
+//
+// The step reads each state element once, so at V = 64 it needs many bytes in
+// flight per compute unit to keep HBM busy.  Each wave walks its (batch row,
+// slab) sequence with two slabs ahead in flight, loaded straight into an LDS
+// ring of two slots per wave (global_load_lds: no registers held while in
+// flight): the slab's state tiles and, beside them, its rows' k and q, its
+// unit's v and gate.  No load in the loop has a register destination, so the
+// compiler inserts no wait there (it would wait for every ring load in
+// flight); the ring is read with inline ds_read (each asm ends with its own
+// wait), and each slot is awaited by an explicit vmcnt wait that counts only
+// the operations issued after it, in a fixed order per iteration: the ring
+// loads two slabs ahead, the VT state stores, at a unit's end its readout,
+// pinned with scheduling barriers.
+// The LDS offset of a pointer to shared memory.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// One 16-byte (4-byte) load per lane from global memory into LDS at
+// dst + 16 lane (dst + 4 lane).
+__device__ __forceinline__ void global_to_lds16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void global_to_lds4(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+}
+
+template <typename InT, int VT>
+__global__ void __launch_bounds__(256, 3) m2rnn_step_full_kernel(StepArgs a) {
+  using R4 = f32x4;
+  constexpr int VP = 16 * VT;
+  constexpr bool kBf16 = std::is_same_v<InT, uint16_t>;
+  constexpr int D = 2;                          // ring slots (slabs in flight) per wave
+  constexpr int SIDE = VT * 1024;               // bytes: k, q, f, v blocks after the tiles
+  constexpr int SLOT = SIDE + 1024;             // bytes per slot
+  constexpr int RING = 4 * D * SLOT;            // the four waves' rings
+  constexpr int WST = VT * VT * 1024;           // W^T staging (before the rings)
+  __shared__ R4 lds[(RING > WST ? RING : WST) / 16];
+  __shared__ float wrl[VP];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, g = lane >> 4, li = lane & 15;
+  const int64_t B = a.B, N = a.N, K = a.K, NQ = a.NQ;  // V = VP
+  const int64_t n = (int64_t)blockIdx.x % N;
+  const int64_t b0 = ((int64_t)blockIdx.x / N) * 4 * a.upw + w;
+
+  // W^T of the head in MFMA A-operand order ([c][j][lane], as the general
+  // kernel's), staged once, then held in registers
+  const float* __restrict__ Wp = (const float*)a.W + n * VP * VP;
+  for (int e = tid; e < VP * VP; e += 256) {
+    const int l = e / VP, col = e % VP;
+    const int m = l & 15;
+    ((float*)&lds[((col >> 4) * VT + (l >> 4)) * 64 + 16 * acc_g<float>(m) + (col & 15)])
+        [acc_r<float>(m)] = kTanhScale<float> * Wp[l * VP + col];
+  }
+  if (tid < VP) wrl[tid] = ((const float*)a.w_r)[n * VP + tid];
+  __syncthreads();
+  R4 wop[VT][VT];
+#pragma unroll
+  for (int c = 0; c < VT; ++c)
+#pragma unroll
+    for (int j = 0; j < VT; ++j) wop[c][j] = lds[(c * VT + j) * 64 + lane];
+  __syncthreads();  // the staging area becomes the rings
+  if (b0 >= B) return;
+
+  const int64_t nq = n / (N / NQ);
+  const int nslab = (int)(K / 16);
+  const int64_t b_end = ((int64_t)blockIdx.x / N + 1) * 4 * a.upw < B
+                            ? ((int64_t)blockIdx.x / N + 1) * 4 * a.upw
+                            : B;
+  // positions in the wave's sequence: batch row bb (b0, b0 + 4, ...), slab s
+  struct Pos {
+    int64_t bb;
+    int s;
+  };
+  auto advance = [&](Pos p) -> Pos {
+    if (p.s + 1 < nslab) return Pos{p.bb, p.s + 1};
+    return Pos{p.bb + 4, 0};
+  };
+  // past the end, loads go to the last valid position (harmless re-reads)
+  auto valid = [&](Pos p, Pos last) -> Pos { return p.bb < b_end ? p : last; };
+  // this lane's state row (16 s + li, columns 16 j + 4 g .. + 3)
+  auto hrow = [&](Pos p) -> float* {
+    return (float*)a.H + ((p.bb * N + n) * K + p.s * 16 + li) * VP + 4 * g;
+  };
+  char* const ring = (char*)lds + w * D * SLOT;
+  // dwords of a k (or q) slab and of a v row: lane l loads dword l mod their count
+  constexpr int KDW = 16 * (int)sizeof(InT) / 4, VDW = VP * (int)sizeof(InT) / 4;
+  // slab p into ring slot `slot`: VT state tiles, then k, q, the gate and v
+  auto ring_load = [&](Pos p, int slot) {
+    char* base = ring + slot * SLOT;
+    const float* src = hrow(p);
+#pragma unroll
+    for (int j = 0; j < VT; ++j) global_to_lds16(src + 16 * j, base + j * 1024);
+    const int64_t kq = (p.bb * NQ + nq) * K + p.s * 16;
+    global_to_lds4((const uint32_t*)((const InT*)a.k + kq) + (lane % KDW), base + SIDE);
+    global_to_lds4((const uint32_t*)((const InT*)a.q + kq) + (lane % KDW), base + SIDE + 256);
+    global_to_lds4((const float*)a.f + p.bb * N + n, base + SIDE + 512);
+    global_to_lds4((const uint32_t*)((const InT*)a.v + (p.bb * N + n) * VP) + (lane % VDW),
+                     base + SIDE + 768);
+  };
+  // ring slot -> this lane's four state tiles, the k and q of its row and the
+  // gate (raw 32-bit words), and, at a unit's first slab, its v at columns
+  // 16 c + 4 g .. + 3: one asm of LDS reads that ends with their wait.  No
+  // memory clobber: the compiler would take the asm for an LDS read and wait
+  // for every ring load in flight; the order against the ring loads is kept by
+  // the explicit waits and scheduling barriers.
+  static_assert(VT == 4, "the ring kernel reads four tiles per slab");
+  using VRaw = std::conditional_t<kBf16, uint2, R4>;
+  auto ring_read = [&](int slot, R4 (&h)[VT], uint32_t& kr, uint32_t& qr, uint32_t& fr) {
+    const char* base = ring + slot * SLOT;
+    const uint32_t ah = lds_offset(base + 16 * lane);
+    const uint32_t ak = lds_offset(base + SIDE + (kBf16 ? 2 : 4) * li);
+    const uint32_t af = lds_offset(base + SIDE + 512);
+    if constexpr (kBf16) {
+      asm volatile(
+          "ds_read_b128 %0, %7\n ds_read_b128 %1, %7 offset:1024\n"
+          " ds_read_b128 %2, %7 offset:2048\n ds_read_b128 %3, %7 offset:3072\n"
+          " ds_read_u16 %4, %8\n ds_read_u16 %5, %8 offset:256\n ds_read_b32 %6, %9\n"
+          " s_waitcnt lgkmcnt(0)"
+          : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3]), "=&v"(kr), "=&v"(qr), "=&v"(fr)
+          : "v"(ah), "v"(ak), "v"(af));
+    } else {
+      asm volatile(
+          "ds_read_b128 %0, %7\n ds_read_b128 %1, %7 offset:1024\n"
+          " ds_read_b128 %2, %7 offset:2048\n ds_read_b128 %3, %7 offset:3072\n"
+          " ds_read_b32 %4, %8\n ds_read_b32 %5, %8 offset:256\n ds_read_b32 %6, %9\n"
+          " s_waitcnt lgkmcnt(0)"
+          : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3]), "=&v"(kr), "=&v"(qr), "=&v"(fr)
+          : "v"(ah), "v"(ak), "v"(af));
+    }
+  };
+  auto v_read = [&](int slot, VRaw (&x)[VT]) {
+    const uint32_t av = lds_offset(ring + slot * SLOT + SIDE + 768 + (kBf16 ? 8 : 16) * g);
+    if constexpr (kBf16) {
+      asm volatile("ds_read_b64 %0, %4\n ds_read_b64 %1, %4 offset:32\n"
+                   " ds_read_b64 %2, %4 offset:64\n ds_read_b64 %3, %4 offset:96\n"
+                   " s_waitcnt lgkmcnt(0)"
+                   : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]) : "v"(av));
+    } else {
+      asm volatile("ds_read_b128 %0, %4\n ds_read_b128 %1, %4 offset:64\n"
+                   " ds_read_b128 %2, %4 offset:128\n ds_read_b128 %3, %4 offset:192\n"
+                   " s_waitcnt lgkmcnt(0)"
+                   : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]) : "v"(av));
+    }
+  };
+  auto widen4 = [](VRaw x) -> R4 {
+    if constexpr (kBf16) {
+      return R4{__builtin_bit_cast(float, x.x << 16), __builtin_bit_cast(float, x.x & 0xffff0000u),
+                __builtin_bit_cast(float, x.y << 16), __builtin_bit_cast(float, x.y & 0xffff0000u)};
+    } else {
+      return x;
+    }
+  };
+  // w_r of this lane's readout columns, by the same route
+  auto wr_read = [&](R4 (&x)[VT]) {
+    const uint32_t ad = lds_offset(&wrl[4 * g]);
+    asm volatile("ds_read_b128 %0, %4\n ds_read_b128 %1, %4 offset:64\n"
+                 " ds_read_b128 %2, %4 offset:128\n ds_read_b128 %3, %4 offset:192\n"
+                 " s_waitcnt lgkmcnt(0)"
+                 : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]) : "v"(ad));
+  };
+
+  // prologue: slabs 0 and 1 into slots 0 and 1
+  Pos cur{b0, 0};
+  Pos pr = valid(advance(cur), cur);  // the last ring load
+  ring_load(cur, 0);
+  ring_load(pr, 1);
+  __builtin_amdgcn_sched_barrier(0);
+
+  R4 yacc[VT], vv[VT];
+#pragma unroll
+  for (int c = 0; c < VT; ++c) yacc[c] = R4{0, 0, 0, 0};
+  constexpr int kOps = VT + 4;  // memory operations of one ring load
+  int slot = 0;
+  for (int i = 0;; ++i) {
+    // this slab's ring load is done once at most the ring loads and state
+    // stores issued after it remain: one ring load in the first iteration, a
+    // ring load and a slab's stores in the second, then a slab's stores, a
+    // ring load and another slab's stores
+    if (i == 0) {
+      constexpr int m = kOps;
+      __builtin_amdgcn_s_waitcnt((m & 15) | ((m >> 4) << 14) | (7 << 4) | (15 << 8));
+    } else if (i == 1) {
+      constexpr int m = kOps + VT;
+      __builtin_amdgcn_s_waitcnt((m & 15) | ((m >> 4) << 14) | (7 << 4) | (15 << 8));
+    } else {
+      constexpr int m = kOps + 2 * VT;
+      __builtin_amdgcn_s_waitcnt((m & 15) | ((m >> 4) << 14) | (7 << 4) | (15 << 8));
+    }
+    R4 h[VT];
+    uint32_t kr, qr, fr;
+    ring_read(slot, h, kr, qr, fr);
+    if (cur.s == 0) {  // a unit's first slab: its v
+      VRaw vx[VT];
+      v_read(slot, vx);
+#pragma unroll
+      for (int c = 0; c < VT; ++c) vv[c] = widen4(vx[c]);
+    }
+    const float kk = __builtin_bit_cast(float, kBf16 ? kr << 16 : kr);
+    const float qq = __builtin_bit_cast(float, kBf16 ? qr << 16 : qr);
+    const float f = __builtin_bit_cast(float, fr);
+    __builtin_amdgcn_sched_barrier(0);
+    // the slab two ahead into the slot just read
+    const Pos pn = valid(advance(pr), pr);
+    ring_load(pn, slot);
+    __builtin_amdgcn_sched_barrier(0);
+    pr = pn;
+
+    const float omf = 1.0f - f, m2omf = -2.0f * omf;
+    const float ks = kTanhScale<float> * kk;
+    float* dst = hrow(cur);
+#pragma unroll
+    for (int c = 0; c < VT; ++c) {
+      R4 acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = ks * vv[c][r];
+#pragma unroll
+      for (int j = 0; j < VT; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc = mfma_16x16x4(wop[c][j][r], h[j][r], acc);
+      pin_vec(acc);
+      R4 hn;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        hn[r] = fma_r(m2omf, tanh_rc_scaled(acc[r]), fma_r(f, h[c][r], omf));
+      *(R4*)(dst + 16 * c) = hn;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) yacc[c][r] = fma_r(hn[r], qq, yacc[c][r]);
+    }
+    if (cur.s + 1 == nslab) {
+      // y = H^T q + w_r (.) v of the finished unit, from lane 16 g of each row
+      R4 ys[VT];
+#pragma unroll
+      for (int c = 0; c < VT; ++c) ys[c] = row16_sum_x4(yacc[c], 1.0f);
+      if (li == 0) {
+        float* yp = (float*)a.y + (cur.bb * N + n) * VP + 4 * g;
+        R4 wr4[VT];
+        wr_read(wr4);
+#pragma unroll
+        for (int c = 0; c < VT; ++c) {
+          R4 o;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = ys[c][r] + wr4[c][r] * vv[c][r];
+          *(R4*)(yp + 16 * c) = o;
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < VT; ++c) yacc[c] = R4{0, 0, 0, 0};
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    cur = advance(cur);
+    if (cur.bb >= b_end) break;
+    slot ^= 1;
+  }
+  // no ring load may still be writing LDS when the wave ends
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+}
+
+template <typename InT, int VT>
+static hipError_t launch_step_full(StepArgs a, hipStream_t stream) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> resident[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = kMaxDevices;
+  int cap = dev < kMaxDevices ? resident[dev].load(std::memory_order_relaxed) : 0;
+  if (cap <= 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, m2rnn_step_full_kernel<InT, VT>, 256,
+                                                     0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      per_cu = 4;
+      cus = 256;
+    }
+    cap = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+    if (dev < kMaxDevices) resident[dev].store(cap, std::memory_order_relaxed);
+  }
+  const int64_t groups = (a.B + 3) / 4;
+  int64_t upw = (a.N * groups + cap - 1) / cap;
+  if (upw < 1) upw = 1;
+  a.upw = upw;
+  const int64_t wgs = a.N * ((groups + upw - 1) / upw);
+  hipLaunchKernelGGL((m2rnn_step_full_kernel<InT, VT>), dim3((unsigned)wgs), dim3(256), 0, stream,
+                     a);
+  return hipGetLastError();
+}
+
 template <typename InT, typename Real, int VT>
 static hipError_t launch_step_vt(StepArgs a, hipStream_t stream) {
   static_assert(sizeof(typename Vec4<Real>::type) * VT * VT * 64 <= 160 * 1024, "LDS budget");
@@ -297,6 +593,9 @@ static hipError_t launch_step_vt(StepArgs a, hipStream_t stream) {
 
 template <typename InT, typename Real>
 static hipError_t launch_step_t(const StepArgs& a, hipStream_t stream) {
+  if constexpr (std::is_same_v<Real, float>) {
+    if (a.full) return launch_step_full<InT, 4>(a, stream);
+  }
   switch (value_tiles(a.V)) {
     case 1: return launch_step_vt<InT, Real, 1>(a, stream);
     case 2: return launch_step_vt<InT, Real, 2>(a, stream);

@@ -113,6 +113,34 @@ def test_step_unaligned_state_takes_the_scalar_path():
     assert maxerr(np_(Hu), Hn) <= TOL["float32"] and maxerr(np_(y), yo) <= TOL["float32"]
 
 
+@pytest.mark.parametrize("K,V,NQ,B", [(64, 64, 0, 37), (16, 64, 0, 5), (48, 64, 1, 37),
+                                      (256, 64, 0, 9), (64, 64, 1, 4099)])
+@pytest.mark.parametrize("in_bf16", [True, False])
+def test_step_full_tile_kernel_equals_the_general_one(K, V, NQ, B, in_bf16):
+    """K a multiple of 16, V = 64 and aligned buffers take the full-tile kernel
+    (its LDS ring of state slabs); a y buffer one float off alignment sends the
+    same call to the general kernel, whose arithmetic (and order) it shares:
+    equal bit for bit.  Batch sizes with one slab per wave (K = 16, B = 5),
+    several batch rows per wave and a partial last group (B = 4099)."""
+    N = 4 if NQ else 3
+    wl = WORKLOADS["long_t16k_k64"].replace(B=B, N=N, NQ=NQ, K=K, V=V, bf16=in_bf16,
+                                            kq_scale=1 / math.sqrt(K), v_scale=1 / math.sqrt(V),
+                                            w_scale=1 / math.sqrt(V))
+    inp, d, f, H, H0, fo = step_case(wl, "float32")
+    H2 = H.clone()
+    args = (d["k"][:, 0].contiguous(), d["v"][:, 0].contiguous(), d["q"][:, 0].contiguous(), f,
+            d["W"], d["w_r"])
+    y = m2rnn_step(H, *args)
+    buf = torch.empty(y.numel() + 1, dtype=y.dtype, device=y.device)
+    y2 = buf[1:].view(y.shape)
+    assert y.data_ptr() % 16 == 0 and y2.data_ptr() % 16 != 0
+    m2rnn_step(H2, *args, out=y2)
+    torch.cuda.synchronize()
+    assert torch.equal(H, H2) and torch.equal(y, y2)
+    Hn, yo = oracle.decode_step(H0, inp.k[:, 0], inp.v[:, 0], inp.q[:, 0], fo, inp.W, inp.w_r)
+    assert maxerr(np_(H), Hn) <= TOL["float32"] and maxerr(np_(y), yo) <= TOL["float32"]
+
+
 @pytest.mark.parametrize("K,V", [(20, 24), (64, 64)])
 def test_step_large_ragged_batch(K, V):
     # more batch rows than the device holds workgroups for: every wave takes
