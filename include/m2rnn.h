@@ -168,11 +168,12 @@ int m2rnn_fwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K
  *   dH0    [B, n_heads, K, V]   out, or NULL to skip
  *   workspace / workspace_bytes: at least m2rnn_workspace_bytes(1, ...), 16-byte aligned
  *          (else M2RNN_ERR_INVALID_ARG).  The kernels walk time in chunks of 4, 2
- *          or 1 steps (by state type and V).  When the chunk is at least 2 steps
- *          and C is a larger multiple of it, at most 1024, the main kernel sweeps
- *          each checkpoint interval once and keeps two intervals of states (and of
- *          rc when recomputing) per 16-row slab here; otherwise, unless C divides
- *          the chunk length, the chunk-start states are recomputed into it first.
+ *          or 1 steps (by state type and V).  For V > 112, when the chunk is at
+ *          least 2 steps and C is a larger multiple of it, at most 1024, the main
+ *          kernel sweeps each checkpoint interval once and keeps two intervals of
+ *          states (and of rc when recomputing) per 16-row slab here; otherwise,
+ *          unless C divides the chunk length, the chunk-start states are
+ *          recomputed into it first.
  */
 int m2rnn_bwd(int64_t B, int64_t T, int64_t n_heads, int64_t qk_heads, int64_t K, int64_t V,
               int in_dtype, int state_dtype, const void* k, const void* v, const void* q,

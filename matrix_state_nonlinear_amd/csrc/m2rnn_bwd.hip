@@ -156,8 +156,12 @@ BwdWorkspace bwd_workspace_layout(int64_t B, int64_t T, int64_t N, int64_t NQ, i
   const int64_t ns = num_slabs(K);
   L.period = bwd_period(state_dtype, V);
   L.nch = (T + L.period - 1) / L.period;
-  // (one-step chunks, the fp64 state at V > 96 only, keep the chunk-start pass)
-  L.sweep = L.period >= 2 && C > L.period && C % L.period == 0 && C <= kMaxSweepInterval;
+  // The interval sweep pays at V > 112 (eight value tiles), where it replaces a
+  // chunk-start pass that costs a second forward; at V <= 64 its ring traffic and
+  // the forward role's extra work outweigh that pass (measured at V = 16, 64 and
+  // 128).  One-step chunks (the fp64 state at V > 96) keep the pass as well.
+  L.sweep = value_tiles(V) == kMaxValueTiles && L.period >= 2 && C > L.period &&
+            C % L.period == 0 && C <= kMaxSweepInterval;
   L.subck_needed = (L.period % C) != 0 && !L.sweep;
   const int64_t rows = B * T;
   L.row_blocks = (rows + 255) / 256;

@@ -54,20 +54,27 @@ def test_workspace_sizes(L):
     assert ws(0, 1, 10, 1, 1, 300, 16, 1, _lib.M2RNN_F32) == 0
     assert ws(1, 1, 10, 1, 1, 16, 16, 0, _lib.M2RNN_F32) == 0
     # backward: for V = 64 in fp32 the reverse sweep walks 4-step chunks; a
-    # checkpoint interval dividing 4 provides every chunk start; a multiple of 4
-    # (up to 1024) is swept by the main kernel, which keeps two intervals of
-    # states and of rc per 16-row slab ([units, 2, C, 16, 64] each); any other
-    # adds a [B, N, ceil(T / 4), K, V] region of recomputed chunk starts
+    # checkpoint interval dividing 4 provides every chunk start; any other adds
+    # a [B, N, ceil(T / 4), K, V] region of recomputed chunk starts
     base = ws(1, 2, 64, 2, 2, 32, 64, 4, _lib.M2RNN_F32)
     assert base > 0
     for C in (1, 2):
         assert ws(1, 2, 64, 2, 2, 32, 64, C, _lib.M2RNN_F32) == base
-    for C in (3, 6, 2048):
+    for C in (3, 6, 8, 64, 1024, 2048):
         assert ws(1, 2, 64, 2, 2, 32, 64, C, _lib.M2RNN_F32) == base + 2 * 2 * 16 * 32 * 64 * 4
+    # at V = 128 (2-step chunks) a larger multiple of 2, up to 1024, is swept by
+    # the main kernel, which keeps two intervals of states and of rc per 16-row
+    # slab ([units, 2, C, 16, 128] each); odd intervals and longer ones take the
+    # chunk-start region [B, N, ceil(T / 2), K, V]
+    base = ws(1, 2, 64, 2, 2, 32, 128, 2, _lib.M2RNN_F32)
+    assert base > 0
+    assert ws(1, 2, 64, 2, 2, 32, 128, 1, _lib.M2RNN_F32) == base
+    for C in (3, 2048):
+        assert ws(1, 2, 64, 2, 2, 32, 128, C, _lib.M2RNN_F32) == base + 2 * 2 * 32 * 32 * 128 * 4
     units = 2 * 2 * 2
-    for C in (8, 64, 1024):
-        assert ws(1, 2, 64, 2, 2, 32, 64, C, _lib.M2RNN_F32) == \
-            base + 2 * units * 2 * C * 16 * 64 * 4
+    for C in (4, 64, 1024):
+        assert ws(1, 2, 64, 2, 2, 32, 128, C, _lib.M2RNN_F32) == \
+            base + 2 * units * 2 * C * 16 * 128 * 4
 
 
 def fwd(L, **kw):

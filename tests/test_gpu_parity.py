@@ -309,6 +309,36 @@ def test_stored_rc_forward_and_backward(K, V, C, NQ, sd):
             assert torch.equal(g0[name], g1[name]), name
 
 
+@pytest.mark.parametrize("K,V,T,C,NQ", [(32, 128, 45, 4, 0), (20, 120, 61, 6, 1), (48, 128, 130, 8, 0),
+                                        (16, 113, 29, 64, 0), (64, 128, 200, 16, 2)])
+def test_backward_interval_sweep_matches_the_oracle(K, V, T, C, NQ):
+    """V > 112 (eight value tiles) with C a larger multiple of the backward's
+    2-step chunk: the main kernel sweeps each checkpoint interval once (its
+    states, and rc when recomputing, in a two-interval ring of the workspace)
+    instead of a chunk-start pass.  Ragged K, V and T, shared q/k, an interval
+    longer than T, both modes: the gradients match the oracle at the fp32
+    tolerance and the two modes each other bit for bit."""
+    N = 4 if NQ else 2
+    wl = WORKLOADS["fwd_bwd_k32_v128"].replace(B=2, T=T, N=N, NQ=NQ, K=K, V=V,
+                                               kq_scale=1 / math.sqrt(K),
+                                               v_scale=1 / math.sqrt(V), w_scale=1 / math.sqrt(V))
+    inp = make_inputs(wl, with_dy=True, with_h0=True, with_dht=True)
+    d = to_device(inp, "float32")
+    f = m2rnn_gates(d["logit"], wl.gate, d["alpha"], d["beta"])
+    rc = torch.empty((wl.B, wl.N, wl.T, K, V), dtype=f.dtype, device=f.device)
+    _, _, ck = m2rnn_fwd(d["k"], d["v"], d["q"], f, d["W"], d["w_r"], d["H0"], C, rc_out=rc)
+    args = (d["k"], d["v"], d["q"], wl.gate, d["logit"], d["alpha"], d["beta"], f, d["W"],
+            d["w_r"], d["H0"], ck, C, d["dy"], d["dHT"])
+    g0 = m2rnn_bwd(*args)
+    g1 = m2rnn_bwd(*args, rc=rc)
+    torch.cuda.synchronize()
+    for name in g0:
+        if g0[name] is not None:
+            assert torch.equal(g0[name], g1[name]), name
+    check_grads({k_: np_(v_) for k_, v_ in g0.items() if v_ is not None}, oracle_backward(inp),
+                TAU_G["float32"], f"sweep K{K} V{V} T{T} C{C} NQ{NQ}")
+
+
 # ---------------------------------------------------------------- alignment
 
 def _offset_view(shape, dtype, elems=1, dev="cuda:0"):

@@ -102,7 +102,8 @@ def check_against_oracle(wl, inp, sd, C, f, y, HT, ck, rc, g, label):
 
 
 # (K, V, T, NQ, C): ragged slab/tile/chunk edges; C not dividing the backward's
-# chunk length (4 steps for V <= 96, 2 at V = 128) or dividing it; shared q/k
+# chunk length (4 steps for V <= 96, 2 at V = 128) or dividing it; shared q/k;
+# at V > 112 intervals swept by the main kernel (C = 4, 6: its ring workspace)
 CASES = [
     (17, 40, 45, 0, 7),
     (33, 100, 29, 0, 5),
@@ -112,6 +113,8 @@ CASES = [
     (24, 20, 23, 1, 6),
     (64, 16, 41, 1, 2),
     (20, 24, 19, 2, 1),
+    (40, 128, 45, 0, 4),
+    (24, 120, 70, 1, 6),
 ]
 
 
