@@ -235,6 +235,10 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
   // the reverse role's step in phase j, and whether it takes one
   auto rstep = [&](int j) { return nch * S + S - j; };
   auto ractive = [&](int j) { return j >= S + 1 && j <= nch * S + S; };
+  // With one value tile the reverse role reduces dv_t = D_t^T k_t itself, right
+  // after it forms D_t (its phase is the shortest there); otherwise the forward
+  // role does it one phase later.
+  constexpr bool kDvRev = VT == 1 && !SW;
 
   if (role == 0) {
     if constexpr (SW) {
@@ -886,7 +890,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
       // dv_t' = D^T k over this slab's rows (+ w_r (.) u when the slab is the
       // whole head) for the reverse role's step t' = (cF + 2) S - I + 1 of
       // phase j - 1: this wave's D tiles, reduced over the 16 rows with DPP
-      if (ractive(j - 1)) {
+      if (!kDvRev && ractive(j - 1)) {
         const int tp = (cF + 2) * S - I + 1;
         if (tp < T32) {
           constexpr int tq = (1 - I + S) % S;
@@ -989,6 +993,21 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
     }
     // transposed D: element (row li, column c) of a tile at [c][4 (li % 4) + li / 4]
     const int trow = 4 * (li & 3) + (li >> 2);
+    // dv (kDvRev): w_r of this lane's columns, output row of token (b, t = 0, n)
+    Real wrv[TPW][4];
+#pragma unroll
+    for (int p = 0; p < TPW; ++p)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int col = col_of(p, r);
+        wrv[p][r] = (kDvRev && col < V) ? ((const Real*)a.w_r)[(int64_t)n * V + col] : Real(0);
+      }
+#pragma unroll
+    for (int p = 0; p < TPW; ++p) pin_values(wrv[p][0], wrv[p][1], wrv[p][2], wrv[p][3]);
+    const bool dv_vec_r = sizeof(Real) == 4 && (FULL || a.dv_vec);
+    Real* const dv_tok_r = nslab == 1 ? (Real*)a.dv + tok0 * V
+                                      : (Real*)a.ws + L.dv_part + ((int64_t)slab * B * T * N + tok0) * V;
+    const int64_t NV_r = N * V;
 
     __syncthreads();  // prologue staging by the side role
     if constexpr (SW) {  // the forward role's sweep-only periods
@@ -1062,6 +1081,33 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
             if constexpr (Tr::kXdt) {
 #pragma unroll
               for (int r = 0; r < 4; ++r) sm.xdT[jp][wr * TPW + p][acc_m<Real>(g, r)][trow] = D[r];
+            }
+          }
+          if constexpr (kDvRev) {
+            // dv_t = D_t^T k_t over this slab's rows (+ w_r (.) u when the slab
+            // is the whole head)
+            if (t < T32) {
+              const Real kq = stp[li];
+              Real* dvp = dv_tok_r + (int64_t)t * NV_r;
+#pragma unroll
+              for (int p = 0; p < TPW; ++p) {
+                R4 sv = row16_sum_x4(Dp[p], kq);
+                if (li == 0) {
+                  if (nslab == 1) {
+                    const R4 u = cols4(stp + OFF_U + (wr * TPW + p) * 16, g);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sv[r] = fma_r(wrv[p][r], u[r], sv[r]);
+                  }
+                  const int col0 = col_of(p, 0);
+                  if (dv_vec_r) {
+                    if (FULL || col0 < V) *(R4*)(dvp + col0) = sv;
+                  } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                      if (col_of(p, r) < V) dvp[col_of(p, r)] = sv[r];
+                  }
+                }
+              }
             }
           }
           sm.rk[jp][li][wr * 4 + g] = dkp;
@@ -1243,6 +1289,13 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
       constexpr int I = decltype(Ic)::value;
       const int j = k * S + I;
       const int jp = j & 1;
+      // one wave per role: the reverse role's dk and df partials of phase j - 1,
+      // read first so that their latency passes under the dW products
+      R4 rkx = R4{0, 0, 0, 0}, rfx = R4{0, 0, 0, 0};
+      if constexpr (NW == 1) {
+        rkx = *(const R4*)&sm.rk[jp ^ 1][li][0];
+        rfx = *(const R4*)&sm.rf[jp ^ 1][0];
+      }
       // dW += S_t'^T D_t' for the reverse role's step t' of phase j - 1 (zero
       // A operands when it had none); B from the transposed D copy
       {
@@ -1282,6 +1335,13 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
       if (tp >= T32) return;
       // dk_t' and df_t' from the reverse role's partials: lane group q adds
       // entries 4 q .. 4 q + 3, then the four groups are added across lanes
+      if constexpr (NW == 1) {
+        // one wave: the four entries are the four lane groups' partials, so
+        // every lane of group 0 holds its row's complete sum
+        if (g == 0 && (FULL || row_ok)) dk_row[(int64_t)tp * NK] = (rkx[0] + rkx[1]) + (rkx[2] + rkx[3]);
+        if (lane == 0) df_tok[(int64_t)tp * N] = (rfx[0] + rfx[1]) + (rfx[2] + rfx[3]);
+        return;
+      }
       if (wr == 0) {
         Real s4 = 0;
         if (4 * g < 4 * NW) {
