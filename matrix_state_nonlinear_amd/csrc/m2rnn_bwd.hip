@@ -30,7 +30,9 @@
 //  * reverse role: walks the chunk recomputed in the previous period from its
 //    last step to its first, one phase behind, carrying C through the MFMA
 //    product (D W^T)^T = W D^T; it publishes D (plain and transposed) and the
-//    lane partials of dk and df.
+//    lane partials of dk and df.  With one value tile it also reduces dv
+//    itself, right after forming D (the forward role's phase is the longest
+//    there).
 //  * side role: accumulates dW += S_t^T D_t on MFMA one phase behind the
 //    reverse role, finishes dk and df, and stages the next chunk's inputs and
 //    start state from HBM into LDS.
