@@ -73,8 +73,10 @@ struct BwdShape {
   static constexpr int E = (32 + 2 * VP + 1 + 3) / 4 * 4;  // staged values per step
   static constexpr size_t kTileset = (size_t)VT * 64 * 4 * sizeof(Real);
   // the transposed D copy (16-byte dW operand reads) is kept for fp32; the
-  // fp64 instantiations read the operands from the plain copy to fit in LDS
-  static constexpr bool kXdt = sizeof(Real) == 4;
+  // fp64 instantiations read the operands from the plain copy to fit in LDS,
+  // and so does one value tile, where the reverse role (which would write the
+  // copy with scattered 4-byte stores) has the longest phase
+  static constexpr bool kXdt = sizeof(Real) == 4 && VT > 1;
 };
 
 constexpr int bwd_slots(int S) { return S >= 4 ? 3 : (S == 2 ? 4 : 5); }
@@ -880,7 +882,10 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
         if (g == 0) sm.rq[jp][li][wr] = dqp;
       }
       // dq of the previous phase's step: the per-wave sums, added by wave 0
-      if (wr == 0 && g == 0 && (FULL || row_ok) && j >= 1 && j <= nch * S) {
+      // (by the side role when the reverse role reduces dv: with no store here
+      // the role's only global accesses are its rc loads, and a wait for one
+      // of them need not wait for a store issued after it)
+      if (!kDvRev && wr == 0 && g == 0 && (FULL || row_ok) && j >= 1 && j <= nch * S) {
         const int tf = I > 0 ? cF * S + I - 1 : cF * S + 2 * S - 1;
         if (tf < T32) {
           Real sq = 0;
@@ -1085,15 +1090,18 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
               for (int r = 0; r < 4; ++r) sm.xdT[jp][wr * TPW + p][acc_m<Real>(g, r)][trow] = D[r];
             }
           }
+          sm.rk[jp][li][wr * 4 + g] = dkp;
           if constexpr (kDvRev) {
             // dv_t = D_t^T k_t over this slab's rows (+ w_r (.) u when the slab
-            // is the whole head)
+            // is the whole head), reduced together with df's row sum
+            static_assert(TPW == 1, "one tile per wave");
+            const Real kq = stp[li];
+            Real* dvp = dv_tok_r + (int64_t)t * NV_r;
+            R4 sv = row16_sum_x4_e(Dp[0], kq, dfp);
+            if (li == 0) sm.rf[jp][wr * 4 + g] = dfp;
             if (t < T32) {
-              const Real kq = stp[li];
-              Real* dvp = dv_tok_r + (int64_t)t * NV_r;
 #pragma unroll
               for (int p = 0; p < TPW; ++p) {
-                R4 sv = row16_sum_x4(Dp[p], kq);
                 if (li == 0) {
                   if (nslab == 1) {
                     const R4 u = cols4(stp + OFF_U + (wr * TPW + p) * 16, g);
@@ -1111,10 +1119,11 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
                 }
               }
             }
+          } else {
+            sm.rk[jp][li][wr * 4 + g] = dkp;
+            dfp = row16_sum(dfp);
+            if (li == 0) sm.rf[jp][wr * 4 + g] = dfp;
           }
-          sm.rk[jp][li][wr * 4 + g] = dkp;
-          dfp = row16_sum(dfp);
-          if (li == 0) sm.rf[jp][wr * 4 + g] = dfp;
           // rc of step t - 1, for the next phase
           if (t >= 1) {
 #pragma unroll
@@ -1270,6 +1279,7 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
     auto tidx = [&](int kk) { return (16 * acc_g<Real>(li) + 4 * kk + g) * 4 + acc_r<Real>(li); };
     // output pointers at token (b, t = 0, n); step t adds t N rows
     Real* const dk_row = dk_base + tok0 * K + row;
+    Real* const dq_row_s = dq_base + tok0 * K + row;
     Real* const df_tok = ws + L.df_part + (int64_t)slab * B * T * N + tok0;
     const int64_t NK = N * K;
 
@@ -1294,9 +1304,19 @@ __global__ void __launch_bounds__((BwdTraits<Real, VT>::NT))
       // one wave per role: the reverse role's dk and df partials of phase j - 1,
       // read first so that their latency passes under the dW products
       R4 rkx = R4{0, 0, 0, 0}, rfx = R4{0, 0, 0, 0};
+      Real rqx = 0;
       if constexpr (NW == 1) {
         rkx = *(const R4*)&sm.rk[jp ^ 1][li][0];
         rfx = *(const R4*)&sm.rf[jp ^ 1][0];
+        rqx = sm.rq[jp ^ 1][li][0];
+      }
+      // dq of the forward role's step of phase j - 1 (kDvRev: one wave per
+      // role, so its per-wave sum is the slab's)
+      if constexpr (kDvRev) {
+        if (g == 0 && (FULL || row_ok) && j >= 1 && j <= nch * S) {
+          const int tf = I > 0 ? cF * S + I - 1 : cF * S + 2 * S - 1;
+          if (tf < T32) dq_row_s[(int64_t)tf * NK] = rqx;
+        }
       }
       // dW += S_t'^T D_t' for the reverse role's step t' of phase j - 1 (zero
       // A operands when it had none); B from the transposed D copy

@@ -169,6 +169,44 @@ __device__ __forceinline__ f32x4 row16_sum_x4(f32x4 h, float q) {
       : "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "v"(q));
   return f32x4{y0, y1, y2, y3};
 }
+// row16_sum_x4(h, q) together with the row sum of a fifth value e (returned
+// in e), the five chains interleaved level by level.
+__device__ __forceinline__ f32x4 row16_sum_x4_e(f32x4 h, float q, float& e) {
+  float y0, y1, y2, y3;
+  asm volatile(
+      "v_mul_f32 %0, %5, %9\n"
+      "v_mul_f32 %1, %6, %9\n"
+      "v_mul_f32 %2, %7, %9\n"
+      "v_mul_f32 %3, %8, %9\n"
+      "v_add_f32_dpp %4, %4, %4 row_ror:8 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %1, %1, %1 row_ror:8 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %2, %2, %2 row_ror:8 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %3, %3, %3 row_ror:8 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %4, %4, %4 row_ror:4 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %1, %1, %1 row_ror:4 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %2, %2, %2 row_ror:4 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %3, %3, %3 row_ror:4 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %4, %4, %4 row_ror:2 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %0, %0, %0 row_ror:2 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %1, %1, %1 row_ror:2 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %2, %2, %2 row_ror:2 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %3, %3, %3 row_ror:2 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %4, %4, %4 row_ror:1 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %0, %0, %0 row_ror:1 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %1, %1, %1 row_ror:1 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %2, %2, %2 row_ror:1 row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %3, %3, %3 row_ror:1 row_mask:0xf bank_mask:0xf\n"
+      : "=&v"(y0), "=&v"(y1), "=&v"(y2), "=&v"(y3), "+v"(e)
+      : "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "v"(q));
+  return f32x4{y0, y1, y2, y3};
+}
+__device__ __forceinline__ f64x4 row16_sum_x4(f64x4 h, double q);
+__device__ __forceinline__ f64x4 row16_sum_x4_e(f64x4 h, double q, double& e) {
+  e = row16_sum(e);
+  return row16_sum_x4(h, q);
+}
 __device__ __forceinline__ f64x4 row16_sum_x4(f64x4 h, double q) {
   f64x4 y;
 #pragma unroll
