@@ -206,10 +206,13 @@ def test_backward_workload_recipes(name, sd):
 
 
 @pytest.mark.parametrize("K,V,C", [(1, 1, 1), (17, 40, 7), (40, 72, 64), (33, 100, 5),
-                                   (16, 128, 3), (20, 20, 3), (32, 32, 4), (9, 24, 2)])
+                                   (16, 128, 3), (20, 20, 3), (32, 32, 4), (9, 24, 2),
+                                   (9, 10, 3), (70, 12, 4)])
 def test_backward_shapes(K, V, C):
     # V = 20, 24, 32: the column sums of dw_r, dalpha, dbeta read 3 or 2 rows
-    # per load (V in 17..32), V <= 16: 4 rows, V >= 64: one
+    # per load (V in 17..32), V <= 16: 4 rows, V >= 64: one.  V = 10, 12: one
+    # value tile with padding columns (the reverse role's dv with 4-byte stores),
+    # K = 9 one slab with padding rows, K = 70 five slabs (the dv partials summed)
     wl = WORKLOADS["fwd_bwd_k32_v128"].replace(B=2, T=29, N=2, K=K, V=V,
                                                kq_scale=1 / math.sqrt(K),
                                                v_scale=1 / math.sqrt(V), w_scale=1 / math.sqrt(V))

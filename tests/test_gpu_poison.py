@@ -113,6 +113,7 @@ CASES = [
     (24, 20, 23, 1, 6),
     (64, 16, 41, 1, 2),
     (20, 24, 19, 2, 1),
+    (9, 10, 27, 0, 3),
     (40, 128, 45, 0, 4),
     (24, 120, 70, 1, 6),
 ]
