@@ -34,7 +34,12 @@ def main(names):
         t0 = time.time()
         inp = make_inputs(wl, with_dy=False)
         f = oracle.gates(wl.gate, inp.logit, inp.alpha, inp.beta)
-        G = oracle.tangent_growth(inp.k, inp.v, inp.q, f, inp.W)
+        # shared q/k (the review's section 2.4 layout): value head n reads q/k
+        # head n // (N / NQ); the tangent pass takes one q/k row per value head
+        rep = wl.N // wl.qk_heads
+        k = np.repeat(inp.k, rep, axis=2)
+        q = np.repeat(inp.q, rep, axis=2)
+        G = oracle.tangent_growth(k, inp.v, q, f, inp.W)
         data[name] = {"B": wl.B, "N": wl.N, "T": wl.T, "seed": wl.seed,
                       "growth": [[float(x) for x in row] for row in G]}
         print(f"{name}: growth quantiles {np.quantile(G, [0, 0.25, 0.5, 0.75, 1])} "
@@ -43,4 +48,4 @@ def main(names):
 
 
 if __name__ == "__main__":
-    main(sys.argv[1:] or WORKLOAD_ORDER)
+    main(sys.argv[1:] or WORKLOAD_ORDER + ["multi_value_k64_v16"])

@@ -455,11 +455,41 @@ def test_backward_fp32_full_size_best_head(name, Cs):
                                f"(max growth {G[:, n].max():.3g}):")
 
 
+def test_backward_fp32_full_size_best_head_shared_qk():
+    """Multi-value workload (one q/k head shared by all 64 value heads, [R]
+    section 2.4), full size, fp32 product path in the benchmark's mode: the
+    per-value-head gradients (dv, dlogit, dW, dw_r, dalpha, dbeta) of the
+    best-conditioned head, with all its batch rows, against the oracle run on
+    that head with the shared q and k, at tau max(1, |g|), tau = 2e-2.  dk and
+    dq sum over all value heads; the restarted windows check them."""
+    name = "multi_value_k64_v16"
+    wl = WORKLOADS[name]
+    inp = make_inputs(wl, with_dy=True)
+    G = growth(name)
+    n = int(np.argmin(G.max(axis=0)))
+    _, _, _, g = _stored_rc_backward(inp, wl.C)
+    sl = lambda a: a[:, :, n:n + 1]  # noqa: E731
+    a_n = None if inp.alpha is None else inp.alpha[n:n + 1]
+    b_n = None if inp.beta is None else inp.beta[n:n + 1]
+    f = oracle.gates(wl.gate, sl(inp.logit), a_n, b_n)
+    ref = oracle.backward(inp.k, sl(inp.v), inp.q, f, inp.W[n:n + 1], inp.w_r[n:n + 1],
+                          sl(inp.dy), gate_kind=wl.gate, logit=sl(inp.logit), alpha=a_n,
+                          beta=b_n, b_group=4)
+    mine = {"dv": np_(g["dv"][:, :, n:n + 1]), "dlogit": np_(g["dlogit"][:, :, n:n + 1]),
+            "dW": np_(g["dW"][n:n + 1]), "dw_r": np_(g["dw_r"][n:n + 1])}
+    if g["dalpha"] is not None:
+        mine["dalpha"] = np_(g["dalpha"][n:n + 1])
+        mine["dbeta"] = np_(g["dbeta"][n:n + 1])
+    ref = {k_: v_ for k_, v_ in ref.items() if k_ in mine}
+    _check(mine, ref, tol(wl), f"{name} fp32 backward (stored rc, C={wl.C}), head {n} "
+                               f"(max growth {G[:, n].max():.3g}):")
+
+
 WINDOW_BWD = 64   # steps of each restarted backward window
 BWD_WINDOW_ENDS = 4
 
 
-@pytest.mark.parametrize("name,Cs", BWD_CASES)
+@pytest.mark.parametrize("name,Cs", BWD_CASES + [("multi_value_k64_v16", 4)])
 def test_backward_fp32_restarted_windows(name, Cs):
     """Every head: windows [t1 - 64, t1) of the full-size fp32 backward (the
     benchmark's mode), t1 spread over the sequence.  The state gradient that
