@@ -271,10 +271,16 @@ def tangent_growth(k, v, q, f, W, H0=None, seed=0):
 
         dH_t = f_t dH_{t-1} + (1 - f_t) (1 - Z_t^2) (.) (dH_{t-1} W),
 
-    i.e. J_t applied to vec(dH) without forming J_t.  Returns, per (b, n), the
-    largest finite-time amplification max_{s <= t} |dH_t| / |dH_s| (max-abs
-    norms).  Values near or below 1 mean rounding errors do not grow; large
-    values mean the trajectory is not reproducible in finite precision.
+    i.e. J_t applied to vec(dH) without forming J_t.  Each row of the state is
+    a recurrence of its own (W right-multiplies, so it mixes the value columns
+    of one row; the rank-1 write and the gate act row by row), and J_t is block
+    diagonal over the K rows: a perturbation of one row is amplified by that
+    row's blocks alone.  So the amplification is measured per row (max-abs
+    norm over the row's V entries; one norm over the whole state would hide a
+    row whose tangent stays smaller than another's), and the result per
+    (b, n) is the largest over the rows of max_{s <= t} |dH_t[i]| / |dH_s[i]|.
+    Values near or below 1 mean rounding errors do not grow; large values
+    mean the trajectory is not reproducible in finite precision.
     """
     k, v, q, f, W = map(_a, (k, v, q, f, W))
     B, T, N, K = k.shape
@@ -282,19 +288,19 @@ def tangent_growth(k, v, q, f, W, H0=None, seed=0):
     rng = np.random.Generator(np.random.PCG64(seed))
     H = np.zeros((B, N, K, V), _f64) if H0 is None else _a(H0).copy()
     dH = rng.standard_normal((B, N, K, V))
-    dH /= np.abs(dH).max(axis=(-2, -1))[..., None, None]
-    logn = np.zeros((B, N))          # log of the tangent's true max-abs norm
-    run_min = np.zeros((B, N))
-    best = np.ones((B, N)) * 0.0
+    dH /= np.abs(dH).max(axis=-1)[..., None]
+    logn = np.zeros((B, N, K))       # log of each row's true max-abs norm
+    run_min = np.zeros((B, N, K))
+    best = np.zeros((B, N, K))
     for t in range(T):
         A = np.matmul(H, W[None]) + k[:, t, :, :, None] * v[:, t, :, None, :]
         Z = np.tanh(A)
         ft = f[:, t, :, None, None]
         dH = ft * dH + (1.0 - ft) * (1.0 - Z * Z) * np.matmul(dH, W[None])
         H = ft * H + (1.0 - ft) * Z
-        m = np.abs(dH).max(axis=(-2, -1))
-        dH = dH / m[..., None, None]     # renormalise; the log keeps the scale
+        m = np.abs(dH).max(axis=-1)
+        dH = dH / m[..., None]           # renormalise each row; the log keeps the scale
         logn = logn + np.log(m)
         best = np.maximum(best, logn - run_min)
         run_min = np.minimum(run_min, logn)
-    return np.exp(best)
+    return np.exp(best.max(axis=-1))

@@ -159,8 +159,10 @@ def _oracle_heads(inp, units, T=None, C=C):
     out = {}
     for n in sorted({n for _, n in units}):
         bs = [b for b, nn in units if nn == n]
+        hq = n // (wl.N // wl.qk_heads)   # the q/k head that value head n reads
         sl = lambda a: a[bs][:, :T, n:n + 1]  # noqa: E731
-        o = oracle.forward(sl(inp.k), sl(inp.v), sl(inp.q), fo[bs][:, :T, n:n + 1],
+        sq = lambda a: a[bs][:, :T, hq:hq + 1]  # noqa: E731
+        o = oracle.forward(sq(inp.k), sl(inp.v), sq(inp.q), fo[bs][:, :T, n:n + 1],
                            inp.W[n:n + 1], inp.w_r[n:n + 1], C=C)
         for i, b in enumerate(bs):
             out[(b, n)] = {k_: v_[i:i + 1] for k_, v_ in o.items()}
@@ -186,7 +188,7 @@ def _conditioned_groups(report=False):
     in groups of at most 32 heads so that each test's oracle work stays within
     about a minute."""
     groups = []
-    for name in ["long_t16k_k64", "big_state_k128", "fwd_bwd_k32_v128"]:
+    for name in ["long_t16k_k64", "big_state_k128", "fwd_bwd_k32_v128", "multi_value_k64_v16"]:
         wl = WORKLOADS[name]
         G = growth(name)
         sel = (G > g_max(wl)) & (G <= F32_MAX_GROWTH) if report else G <= g_max(wl)
