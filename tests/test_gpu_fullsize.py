@@ -86,9 +86,12 @@ def f64_units(name, count=2):
 
 
 def unit_inputs(inp, b, n):
-    """The arrays of one (b, n) head, as a B = N = 1 problem."""
+    """The arrays of one (b, n) head, as a B = N = 1 problem (with the q/k head
+    that value head n reads when q/k are shared)."""
+    hq = n // (inp.wl.N // inp.wl.qk_heads)
     sl = lambda a: None if a is None else a[b:b + 1, :, n:n + 1]  # noqa: E731
-    return dict(k=sl(inp.k), v=sl(inp.v), q=sl(inp.q), logit=sl(inp.logit),
+    sq = lambda a: a[b:b + 1, :, hq:hq + 1]  # noqa: E731
+    return dict(k=sq(inp.k), v=sl(inp.v), q=sq(inp.q), logit=sl(inp.logit),
                 alpha=None if inp.alpha is None else inp.alpha[n:n + 1],
                 beta=None if inp.beta is None else inp.beta[n:n + 1],
                 W=inp.W[n:n + 1], w_r=inp.w_r[n:n + 1], dy=sl(inp.dy))
@@ -114,7 +117,8 @@ def maxerr(a, b):
     return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
 
 
-NAMES = ["tiny_fp32", "fp32_k64", "long_t16k_k64", "big_state_k128", "fwd_bwd_k32_v128"]
+NAMES = ["tiny_fp32", "fp32_k64", "long_t16k_k64", "big_state_k128", "fwd_bwd_k32_v128",
+         "multi_value_k64_v16"]
 
 
 @pytest.mark.parametrize("name", NAMES)
@@ -269,7 +273,7 @@ def test_forward_fp32_full_horizon_report():
 RESTART_TOL = 2e-5
 # checkpoint intervals checked per workload (None: every interval)
 RESTART_EVERY = {"tiny_fp32": None, "fp32_k64": None, "long_t16k_k64": 8, "big_state_k128": 16,
-                 "fwd_bwd_k32_v128": 4}
+                 "fwd_bwd_k32_v128": 4, "multi_value_k64_v16": 8}
 
 
 @pytest.mark.parametrize("name", NAMES)
@@ -346,25 +350,31 @@ def _check(g, ref, tau, label):
     assert not bad, bad
 
 
-@pytest.mark.parametrize("name", ["fwd_bwd_k32_v128", "long_t16k_k64"])
+@pytest.mark.parametrize("name", ["fwd_bwd_k32_v128", "long_t16k_k64", "multi_value_k64_v16"])
 def test_backward_fp64_full_horizon(name):
     """Every gradient of one head (all batch rows of it, so dW, dw_r, dalpha
-    and dbeta of that head are complete sums), full horizon, fp64 kernels."""
+    and dbeta of that head are complete sums), full horizon, fp64 kernels.
+    With q/k shared by several value heads, dk and dq sum over all of them and
+    are left out (the oracle runs the one value head with its q/k head)."""
     wl = WORKLOADS[name]
     inp = make_inputs(wl, with_dy=True)
     G = growth(name)
     n = int(np.argmin(G.max(axis=0)))   # the head whose batch rows amplify least
     g = _backward(inp, "float64")
+    hq = n // (wl.N // wl.qk_heads)
     sl = lambda a: None if a is None else a[:, :, n:n + 1]  # noqa: E731
+    sq = lambda a: a[:, :, hq:hq + 1]  # noqa: E731
     f = oracle.gates(wl.gate, sl(inp.logit), None if inp.alpha is None else inp.alpha[n:n + 1],
                      None if inp.beta is None else inp.beta[n:n + 1])
-    ref = oracle.backward(sl(inp.k), sl(inp.v), sl(inp.q), f, inp.W[n:n + 1], inp.w_r[n:n + 1],
+    ref = oracle.backward(sq(inp.k), sl(inp.v), sq(inp.q), f, inp.W[n:n + 1], inp.w_r[n:n + 1],
                           sl(inp.dy), gate_kind=wl.gate, logit=sl(inp.logit),
                           alpha=None if inp.alpha is None else inp.alpha[n:n + 1],
                           beta=None if inp.beta is None else inp.beta[n:n + 1], b_group=4)
-    mine = {"dk": np_(g["dk"][:, :, n:n + 1]), "dv": np_(g["dv"][:, :, n:n + 1]),
-            "dq": np_(g["dq"][:, :, n:n + 1]), "dlogit": np_(g["dlogit"][:, :, n:n + 1]),
+    mine = {"dv": np_(g["dv"][:, :, n:n + 1]), "dlogit": np_(g["dlogit"][:, :, n:n + 1]),
             "dW": np_(g["dW"][n:n + 1]), "dw_r": np_(g["dw_r"][n:n + 1])}
+    if wl.qk_heads == wl.N:
+        mine["dk"] = np_(g["dk"][:, :, n:n + 1])
+        mine["dq"] = np_(g["dq"][:, :, n:n + 1])
     if g["dalpha"] is not None:
         mine["dalpha"] = np_(g["dalpha"][n:n + 1])
         mine["dbeta"] = np_(g["dbeta"][n:n + 1])
