@@ -1762,11 +1762,34 @@ __global__ void __launch_bounds__(256)
 // Sum over groups of G consecutive heads (shared q and k: the gradient of a
 // shared head is the sum of its value heads' gradients): out[r][i] =
 // sum_{g < G} part[(r G + g) K + i] for the rows r of [B, T, NQ], in head order.
+// `vec` (fp32, K % 4 == 0, both arrays 16-byte aligned): four columns per
+// thread with 16-byte accesses, the group's loads issued four at a time and
+// added in head order (the same sums, bit for bit).
 template <typename Real>
 __global__ void __launch_bounds__(256)
     m2rnn_group_sum_kernel(int64_t total, int64_t K, int G, const Real* __restrict__ part,
-                           Real* __restrict__ out) {
+                           Real* __restrict__ out, bool vec) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  if (sizeof(Real) == 4 && vec) {
+    const int64_t total4 = total >> 2, K4 = K >> 2;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total4; e += stride) {
+      const int64_t r = e / K4, i = e - r * K4;
+      const f32x4* p = (const f32x4*)part + r * G * K4 + i;
+      f32x4 s = p[0];
+      int g = 1;
+      for (; g + 3 < G; g += 4) {
+        const f32x4 a0 = p[g * K4], a1 = p[(g + 1) * K4], a2 = p[(g + 2) * K4],
+                    a3 = p[(g + 3) * K4];
+        s += a0;
+        s += a1;
+        s += a2;
+        s += a3;
+      }
+      for (; g < G; ++g) s += p[g * K4];
+      ((f32x4*)out)[e] = s;
+    }
+    return;
+  }
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
     const int64_t r = e / K, i = e - r * K;
     const Real* p = part + r * G * K + i;
@@ -1981,11 +2004,13 @@ static hipError_t launch_bwd_vt(const BwdArgs& a0, hipStream_t stream) {
   if (a.NQ < a.N) {
     // shared q and k: dk and dq of a shared head are the sums over its group
     const int64_t out = a.B * a.T * a.NQ * a.K;
-    hipLaunchKernelGGL((m2rnn_group_sum_kernel<Real>), dim3(grid_for(out)), dim3(256), 0, stream,
-                       out, a.K, (int)(a.N / a.NQ), ws + L.dk_part, (Real*)a.dk);
+    const bool gv = sizeof(Real) == 4 && a.K % 4 == 0;  // the workspace partials are aligned
+    const bool vk = gv && aligned16(a.dk), vq = gv && aligned16(a.dq);
+    hipLaunchKernelGGL((m2rnn_group_sum_kernel<Real>), dim3(grid_for(vk ? out / 4 : out)), dim3(256),
+                       0, stream, out, a.K, (int)(a.N / a.NQ), ws + L.dk_part, (Real*)a.dk, vk);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((m2rnn_group_sum_kernel<Real>), dim3(grid_for(out)), dim3(256), 0, stream,
-                       out, a.K, (int)(a.N / a.NQ), ws + L.dq_part, (Real*)a.dq);
+    hipLaunchKernelGGL((m2rnn_group_sum_kernel<Real>), dim3(grid_for(vq ? out / 4 : out)), dim3(256),
+                       0, stream, out, a.K, (int)(a.N / a.NQ), ws + L.dq_part, (Real*)a.dq, vq);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   const int64_t per = a.N * a.V * a.V;
