@@ -1815,8 +1815,12 @@ __global__ void __launch_bounds__(256)
   constexpr int kMaxCols = 16 * kMaxValueTiles + 2;
   __shared__ Real red[16][kMaxCols];  // [wave x rows per load][column] partials
   __shared__ Real red2[2][256];       // the two per-head columns, one row per thread
-  const int64_t rb = blockIdx.x;
-  const int64_t n = blockIdx.y;
+  // one block per (row block, head), heads fastest, each XCD taking a
+  // contiguous range: neighbouring heads of a row block share an L2, and with
+  // V < 32 they share the 128-byte lines of dy and v
+  const int64_t unit = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t rb = unit / N;
+  const int64_t n = unit - rb * N;
   const int ncol = (int)V + 2;
   const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
   const int64_t r0 = rb * 256;
@@ -2018,7 +2022,7 @@ static hipError_t launch_bwd_vt(const BwdArgs& a0, hipStream_t stream) {
                      a.B * a.nslab, ws + L.dW_part, (Real*)a.dW);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL((m2rnn_bwd_colsum_kernel<InT, Real>),
-                     dim3((unsigned)L.row_blocks, (unsigned)a.N), dim3(256), 0, stream,
+                     dim3((unsigned)(L.row_blocks * a.N)), dim3(256), 0, stream,
                      a.B * a.T, a.N, a.V, a.gate_kind, (const Real*)a.dy, (const InT*)a.v,
                      ws + L.df_part, (const Real*)a.f, (const Real*)a.logit,
                      (const Real*)a.alpha, (const Real*)a.beta, (const Real*)a.dlogit,
